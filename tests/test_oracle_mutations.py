@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that
+the pin tests catch every one of them."""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE = os.path.join(ROOT, "oracle", "qsa_oracle.py")
+
+MUTATIONS = {
+    "pool_drops_last_row": ("rows = kidx[BLOCK * b: BLOCK * b + BLOCK]",
+                            "rows = kidx[BLOCK * b: BLOCK * b + BLOCK - 1]"),
+    "pool_sum_not_mean": ("rows.sum(axis=0) / BLOCK", "rows.sum(axis=0)"),
+    "relu_sign": ("np.maximum(dots, 0.0)", "np.maximum(-dots, 0.0)"),
+    "no_relu": ("np.maximum(dots, 0.0)", "dots"),
+    "weight_index": ("s += w[h] *", "s += w[0] *"),
+    "tie_to_higher_id": ("order = np.lexsort((ids, -scores))",
+                         "order = np.lexsort((-ids, -scores))"),
+    "select_lowest": ("order = np.lexsort((ids, -scores))",
+                      "order = np.lexsort((ids, scores))"),
+    "own_block_cut": ("toks += list(range(BLOCK * own_block(t), t + 1))",
+                      "toks += list(range(BLOCK * own_block(t), t))"),
+    "own_block_competes": ("return own_block(t)\n", "return own_block(t) + 1\n"),
+    "gqa_interleaved": ("return hq // (n_q_heads // n_kv_heads)",
+                        "return hq % n_kv_heads"),
+    "softmax_no_scale": ("z = scale * (kk @ q[hq])", "z = (kk @ q[hq])"),
+    "bf16_spacing": ("spacing = np.ldexp(1.0, e - 8)", "spacing = np.ldexp(1.0, e - 9)"),
+    "bf16_truncates": ("return np.rint(x / spacing) * spacing",
+                       "return np.trunc(x / spacing) * spacing"),
+    "mask_wrong_head": ("z = scale * (q[:, hq, :] @ k[:, hk, :].T)",
+                        "z = scale * (q[:, hq, :] @ k[:, hq % k.shape[1], :].T)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTATIONS[name]
+    src = open(ORACLE).read()
+    assert src.count(before) >= 1, "mutation target vanished from the oracle"
+    dst = tmp_path / "repo"
+    os.makedirs(dst / "block_sparse_attention_32_amd")
+    shutil.copytree(os.path.join(ROOT, "oracle"), dst / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), dst / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    for f in ("__init__.py", "workloads.py"):
+        shutil.copy(os.path.join(ROOT, "block_sparse_attention_32_amd", f),
+                    dst / "block_sparse_attention_32_amd" / f)
+    (dst / "oracle" / "qsa_oracle.py").write_text(src.replace(before, after))
+    r = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+         "tests/test_oracle_pins.py", "tests/test_workloads.py"],
+        cwd=dst, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"planted mistake {name!r} passed every pin"
