@@ -1,0 +1,348 @@
+// C ABI of libqsa: host-side validation, workspace planning and launches.
+// Every call validates its arguments before enqueuing anything and never
+// synchronises, allocates or copies device data to the host.
+#include <string.h>
+
+#include "attention.hpp"
+#include "index.hpp"
+
+using namespace qsa;
+
+namespace {
+
+constexpr int kRowBatch = 4096;              // top-k rows per launch pair
+constexpr size_t kMaterializeBytes = 1u << 30;  // long rows keep scores below this
+constexpr int kTargetSplitWgs = 1024;        // decode: workgroups over all rows
+constexpr int kMinEntriesPerSplit = 4;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+qsa_status check_cache(const qsa_cache* c) {
+  if (c == nullptr) return QSA_ERR_INVALID_ARG;
+  if (c->dtype != QSA_F32 && c->dtype != QSA_BF16) return QSA_ERR_INVALID_ARG;
+  if (!is_pow2(c->page_size) || c->page_size < QSA_BLOCK) return QSA_ERR_INVALID_ARG;
+  if (c->n_kv_heads < 1 || c->n_seqs < 1 || c->max_pages_per_seq < 1) return QSA_ERR_INVALID_ARG;
+  if (c->max_seq_len < 1 || c->n_pages < 1) return QSA_ERR_INVALID_ARG;
+  if ((int64_t)c->max_seq_len > (int64_t)c->max_pages_per_seq * c->page_size)
+    return QSA_ERR_INVALID_ARG;
+  if (c->block_table == nullptr || c->seq_len == nullptr) return QSA_ERR_INVALID_ARG;
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+  if (c->idx_dim != 16 && c->idx_dim != 32 && c->idx_dim != 64 && c->idx_dim != 128)
+    return QSA_ERR_UNSUPPORTED;
+  return QSA_OK;
+}
+
+qsa_status check_queries(const qsa_cache* c, const qsa_queries* qm) {
+  if (qm == nullptr) return QSA_ERR_INVALID_ARG;
+  if (qm->n_rows < 0 || qm->max_pos < 0) return QSA_ERR_INVALID_ARG;
+  if (qm->n_rows > 0 && (qm->seq_id == nullptr || qm->pos == nullptr)) return QSA_ERR_INVALID_ARG;
+  if (qm->max_pos >= c->max_seq_len) return QSA_ERR_INVALID_ARG;
+  if (qm->max_pos / QSA_BLOCK > QSA_MAX_BLOCKS) return QSA_ERR_UNSUPPORTED;
+  if (qm->n_rows > 65535) return QSA_ERR_UNSUPPORTED;  // grid y
+  return QSA_OK;
+}
+
+PageMap page_map(const qsa_cache* c) {
+  PageMap pm;
+  pm.table = c->block_table;
+  pm.max_pages = c->max_pages_per_seq;
+  pm.page_shift = log2i(c->page_size);
+  return pm;
+}
+
+qsa_status launched() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+// ------------------------------------------------------------- top-k plan
+
+struct TopkPlan {
+  int rows, w_max, materialize;
+  int64_t ws_ld;
+  size_t off_ctr, off_cc, off_tops, off_slots, off_scores, total;
+};
+
+TopkPlan topk_plan(const qsa_queries* qm) {
+  TopkPlan p;
+  const int max_n = qm->max_pos / QSA_BLOCK;
+  p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
+  if (p.rows < 1) p.rows = 1;
+  p.w_max = (max_n + kChunk - 1) / kChunk;
+  if (p.w_max < 1) p.w_max = 1;
+  const int64_t full = (int64_t)p.w_max * kChunk;
+  p.materialize = (size_t)p.rows * (size_t)full * 4 <= kMaterializeBytes;
+  p.ws_ld = p.materialize ? full : (full < kDirectCap ? full : kDirectCap);
+  size_t o = 0;
+  p.off_ctr = o;    o = align256(o + (size_t)4 * p.rows * 4);
+  p.off_cc = o;     o = align256(o + (size_t)p.rows * p.w_max * 4);
+  p.off_tops = o;   o = align256(o + (size_t)p.rows * kUnionCap * 4);
+  p.off_slots = o;  o = align256(o + (size_t)p.rows * kSlotCap * 8);
+  p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
+  p.total = o;
+  return p;
+}
+
+// ------------------------------------------------------------- attention plan
+
+struct AttnPlan {
+  int splits, eps, tile;
+  size_t off_cnt, off_ml, off_acc, total;
+};
+
+AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, int top_k) {
+  AttnPlan p;
+  const bool dense = (op == QSA_OP_DENSE_DECODE || op == QSA_OP_DENSE_PREFILL);
+  const bool split = (op == QSA_OP_ATTN_DECODE || op == QSA_OP_DENSE_DECODE);
+  const int entries = (dense ? qm->max_pos / QSA_BLOCK : top_k) + 1;
+  p.tile = attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
+  const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
+  if (split) {
+    int s = (kTargetSplitWgs + rows - 1) / rows;
+    int s_max = (entries + kMinEntriesPerSplit - 1) / kMinEntriesPerSplit;
+    if (s > s_max) s = s_max;
+    if (s < 1) s = 1;
+    p.eps = (entries + s - 1) / s;
+    p.splits = (entries + p.eps - 1) / p.eps;
+  } else {
+    p.splits = 1;
+    p.eps = entries;
+  }
+  size_t o = 0;
+  p.off_cnt = o;
+  p.off_ml = p.off_acc = 0;
+  if (p.splits > 1) {
+    o = align256(o + (size_t)rows * 4);
+    p.off_ml = o;  o = align256(o + (size_t)rows * p.splits * hq * 2 * 4);
+    p.off_acc = o; o = align256(o + (size_t)rows * p.splits * hq * c->head_dim * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, const void* q,
+                            int32_t hq, const int32_t* sel, const int32_t* n_sel,
+                            int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  qsa_status st = check_cache(c);
+  if (st != QSA_OK) return st;
+  if ((st = check_queries(c, qm)) != QSA_OK) return st;
+  const bool dense = (op == QSA_OP_DENSE_DECODE || op == QSA_OP_DENSE_PREFILL);
+  if (hq < 1 || hq % c->n_kv_heads != 0) return QSA_ERR_INVALID_ARG;
+  if (hq * c->head_dim > kMaxOutPerThread * kAttnThreads) return QSA_ERR_UNSUPPORTED;
+  if (!dense && (top_k < 1 || top_k > QSA_MAX_TOPK)) return QSA_ERR_INVALID_ARG;
+  if (!dense && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || scale != scale) return QSA_ERR_INVALID_ARG;
+  if (qm->n_rows > 0 && (q == nullptr || out == nullptr)) return QSA_ERR_INVALID_ARG;
+  if (c->k == nullptr || c->v == nullptr) return QSA_ERR_INVALID_ARG;
+  const AttnPlan p = attn_plan(op, c, qm, hq, top_k);
+  if (p.tile < QSA_BLOCK) return QSA_ERR_UNSUPPORTED;
+  if (p.total > 0 && (ws == nullptr || ws_bytes < p.total)) return QSA_ERR_WORKSPACE;
+  if (qm->n_rows == 0) return QSA_OK;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pm = page_map(c);
+  a.k = c->k;
+  a.v = c->v;
+  a.hkv = c->n_kv_heads;
+  a.hq = hq;
+  a.q = q;
+  a.out = out;
+  a.seq_id = qm->seq_id;
+  a.pos = qm->pos;
+  a.n_seqs = c->n_seqs;
+  a.max_pos = qm->max_pos;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.top_k = top_k;
+  a.scale = scale;
+  a.n_splits = p.splits;
+  a.eps = p.eps;
+  a.tile_tokens = p.tile;
+  if (p.splits > 1) {
+    char* base = static_cast<char*>(ws);
+    a.cnt = reinterpret_cast<uint32_t*>(base + p.off_cnt);
+    a.part_ml = reinterpret_cast<float*>(base + p.off_ml);
+    a.part_acc = reinterpret_cast<float*>(base + p.off_acc);
+  }
+  run_attention(a, c->dtype, c->head_dim, dense, qm->n_rows, as_stream(stream));
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_pool_blocks(const qsa_cache* c, const int32_t* blk_begin, int32_t max_new_blocks,
+                           void* stream) {
+  qsa_status st = check_cache(c);
+  if (st != QSA_OK) return st;
+  if (max_new_blocks < 0) return QSA_ERR_INVALID_ARG;
+  if (max_new_blocks == 0) return QSA_OK;
+  if (blk_begin == nullptr || c->kidx == nullptr || c->kbar == nullptr) return QSA_ERR_INVALID_ARG;
+  if (c->n_seqs > 65535) return QSA_ERR_UNSUPPORTED;
+  PoolArgs a;
+  a.pm = page_map(c);
+  a.kidx = c->kidx;
+  a.kbar = c->kbar;
+  a.seq_len = c->seq_len;
+  a.blk_begin = blk_begin;
+  a.max_new = max_new_blocks;
+  a.max_seq_len = c->max_seq_len;
+  run_pool(a, c->dtype, c->idx_dim, c->n_seqs, as_stream(stream));
+  return launched();
+}
+
+qsa_status qsa_index_scores(const qsa_cache* c, const qsa_queries* qm, const void* q_idx,
+                            const float* w, int32_t n_idx_heads, float* scores, int64_t ld,
+                            void* stream) {
+  qsa_status st = check_cache(c);
+  if (st != QSA_OK) return st;
+  if ((st = check_queries(c, qm)) != QSA_OK) return st;
+  if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
+  const int max_n = qm->max_pos / QSA_BLOCK;
+  if (ld < (int64_t)max_n) return QSA_ERR_INVALID_ARG;
+  if (qm->n_rows == 0 || max_n == 0) return QSA_OK;
+  if (q_idx == nullptr || w == nullptr || scores == nullptr || c->kbar == nullptr)
+    return QSA_ERR_INVALID_ARG;
+  IdxArgs a;
+  a.pm = page_map(c);
+  a.kbar = c->kbar;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.hi = n_idx_heads;
+  a.seq_id = qm->seq_id;
+  a.pos = qm->pos;
+  a.n_seqs = c->n_seqs;
+  a.max_pos = qm->max_pos;
+  run_scores(a, c->dtype, c->idx_dim, qm->n_rows, max_n, scores, ld, as_stream(stream));
+  return launched();
+}
+
+qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const float* scores,
+                           int64_t ld, const void* q_idx, const float* w, int32_t n_idx_heads,
+                           int32_t top_k, int32_t* sel, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, void* stream) {
+  qsa_status st = check_cache(c);
+  if (st != QSA_OK) return st;
+  if ((st = check_queries(c, qm)) != QSA_OK) return st;
+  if (top_k < 1 || top_k > QSA_MAX_TOPK) return QSA_ERR_INVALID_ARG;
+  const int max_n = qm->max_pos / QSA_BLOCK;
+  if (scores != nullptr) {
+    if (ld < (int64_t)max_n) return QSA_ERR_INVALID_ARG;
+  } else {
+    if (q_idx == nullptr || w == nullptr || c->kbar == nullptr) return QSA_ERR_INVALID_ARG;
+    if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
+  }
+  if (qm->n_rows > 0 && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
+  const TopkPlan p = topk_plan(qm);
+  if (ws == nullptr || ws_bytes < p.total) return QSA_ERR_WORKSPACE;
+  if (qm->n_rows == 0) return QSA_OK;
+  char* base = static_cast<char*>(ws);
+  TopkArgs t;
+  memset(&t, 0, sizeof(t));
+  t.idx.pm = page_map(c);
+  t.idx.kbar = c->kbar;
+  t.idx.q_idx = q_idx;
+  t.idx.w = w;
+  t.idx.hi = n_idx_heads;
+  t.idx.seq_id = qm->seq_id;
+  t.idx.pos = qm->pos;
+  t.idx.n_seqs = c->n_seqs;
+  t.idx.max_pos = qm->max_pos;
+  t.scores = scores;
+  t.ld = ld;
+  t.top_k = top_k;
+  t.sel = sel;
+  t.n_sel = n_sel;
+  t.w_max = p.w_max;
+  t.materialize = p.materialize;
+  t.ws_scores = reinterpret_cast<float*>(base + p.off_scores);
+  t.ws_ld = p.ws_ld;
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(base + p.off_ctr);
+  t.cnt_a = ctr;
+  t.cnt_b = ctr + p.rows;
+  t.flags = ctr + 2 * p.rows;
+  t.tau = ctr + 3 * p.rows;
+  t.chunk_cnt = reinterpret_cast<uint32_t*>(base + p.off_cc);
+  t.tops = reinterpret_cast<uint32_t*>(base + p.off_tops);
+  t.slots = reinterpret_cast<uint2*>(base + p.off_slots);
+  for (int r0 = 0; r0 < qm->n_rows; r0 += p.rows) {
+    const int rows = (qm->n_rows - r0) < p.rows ? (qm->n_rows - r0) : p.rows;
+    t.row0 = r0;
+    run_topk(t, c->dtype, c->idx_dim, rows, as_stream(stream));
+    if ((st = launched()) != QSA_OK) return st;
+  }
+  return QSA_OK;
+}
+
+qsa_status qsa_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                           int32_t n_q_heads, const int32_t* sel, const int32_t* n_sel,
+                           int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return attention_common(QSA_OP_ATTN_DECODE, c, qm, q, n_q_heads, sel, n_sel, top_k, scale,
+                          out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_attn_prefill(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                            int32_t n_q_heads, const int32_t* sel, const int32_t* n_sel,
+                            int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return attention_common(QSA_OP_ATTN_PREFILL, c, qm, q, n_q_heads, sel, n_sel, top_k, scale,
+                          out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_dense_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                                 int32_t n_q_heads, float scale, void* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return attention_common(QSA_OP_DENSE_DECODE, c, qm, q, n_q_heads, nullptr, nullptr, 0, scale,
+                          out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_dense_attn_prefill(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                                  int32_t n_q_heads, float scale, void* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return attention_common(QSA_OP_DENSE_PREFILL, c, qm, q, n_q_heads, nullptr, nullptr, 0, scale,
+                          out, ws, ws_bytes, stream);
+}
+
+size_t qsa_workspace_size(int32_t op, const qsa_cache* c, const qsa_queries* qm,
+                          int32_t n_q_heads, int32_t top_k) {
+  if (c == nullptr || qm == nullptr) return 0;
+  if (check_cache(c) != QSA_OK || check_queries(c, qm) != QSA_OK) return 0;
+  switch (op) {
+    case QSA_OP_TOPK:
+      return topk_plan(qm).total;
+    case QSA_OP_ATTN_DECODE:
+    case QSA_OP_ATTN_PREFILL:
+    case QSA_OP_DENSE_DECODE:
+    case QSA_OP_DENSE_PREFILL:
+      if (n_q_heads < 1) return 0;
+      return attn_plan(op, c, qm, n_q_heads, top_k < 1 ? 1 : top_k).total;
+    default:
+      return 0;
+  }
+}
+
+const char* qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case QSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t qsa_version(void) { return (0 << 16) | 1; }
+
+}  // extern "C"

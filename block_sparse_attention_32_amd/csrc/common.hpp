@@ -1,0 +1,167 @@
+// Device helpers shared by the libqsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+using bf16_t = uint16_t;  // bfloat16 storage (upper half of a binary32)
+
+constexpr int kWave = 64;
+constexpr int kBlock = QSA_BLOCK;
+
+// ---------------------------------------------------------------- dtypes
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// binary32 -> bfloat16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Vec;
+// 16-byte vector of T, widened to float.
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float (&f)[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&f)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&f)[8]) {
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __device__ __forceinline__ static void load(const bf16_t* p, float (&f)[8]) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    unpack(v, f);
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, const float (&f)[8]) {
+    uint4 v;
+    v.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
+    v.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
+    v.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
+    v.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// -0.0 -> +0.0 so that equal scores get equal keys.
+__device__ __forceinline__ float canon_zero(float s) {
+  return __float_as_uint(s) == 0x80000000u ? 0.0f : s;
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).  Key 0
+// lies below every real score and marks "no element".
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(canon_zero(s));
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- paging
+
+struct PageMap {
+  const int32_t* table;   // [n_seqs][max_pages]
+  int32_t max_pages;
+  int32_t page_shift;     // log2(page_size)
+  __device__ __forceinline__ int64_t token_slot(int seq, int tok) const {
+    // global token-row index: page * page_size + slot
+    int32_t page = table[(int64_t)seq * max_pages + (tok >> page_shift)];
+    return ((int64_t)page << page_shift) + (tok & ((1 << page_shift) - 1));
+  }
+  // row index of block b of sequence seq in the pooled-key array
+  __device__ __forceinline__ int64_t block_slot(int seq, int b) const {
+    int tok = b * kBlock;
+    int32_t page = table[(int64_t)seq * max_pages + (tok >> page_shift)];
+    int sh = page_shift - 2;
+    return ((int64_t)page << sh) + (b & ((1 << sh) - 1));
+  }
+};
+
+// ---------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// number of set bits of m below this lane
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u);
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), lo);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t o = (uint32_t)__shfl_up((int)v, off);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- grid sync
+
+// "Last workgroup" hand-off: every workgroup of a group calls this after
+// writing its results; exactly one (the last to arrive) gets true and may
+// read what the others wrote.  The counter is reset for the next call.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected,
+                                            uint32_t* smem_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = atomicAdd(counter, 1u);
+    bool last = (prev == expected - 1);
+    if (last) atomicExch(counter, 0u);
+    *smem_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  bool last = *smem_flag != 0u;
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace qsa

@@ -1,0 +1,77 @@
+"""One pass of the QSA hot path over a batch of query rows.
+
+Orchestration only: allocates the output and workspace buffers with torch
+and calls the libqsa entry points in order (pool the newly completed
+blocks, select the top-k blocks per row, attend).  All arithmetic happens
+in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class QsaStep:
+    """Buffers and calls of one step.
+
+    cache: binding.CacheView; rows: binding.QueriesView; q [T, Hq, D];
+    q_idx [T, Hi, Di]; w [T, Hi] float32.  mode "decode" uses the split
+    attention kernel, "prefill" one workgroup per row.
+    """
+
+    def __init__(self, cache: B.CacheView, rows: B.QueriesView, q, q_idx, w, top_k: int,
+                 scale: float, mode: str = "decode"):
+        self.cache, self.rows = cache, rows
+        self.q, self.q_idx, self.w = q, q_idx, w
+        self.top_k, self.scale, self.mode = int(top_k), float(scale), mode
+        dev = cache.device
+        t = rows.n_rows
+        self.sel = torch.empty((t, self.top_k), dtype=torch.int32, device=dev)
+        self.n_sel = torch.empty((t,), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q)
+        self.ws_topk = B.workspace(B.QSA_OP_TOPK, cache, rows, 0, self.top_k)
+        op = B.QSA_OP_ATTN_DECODE if mode == "decode" else B.QSA_OP_ATTN_PREFILL
+        self.ws_attn = B.workspace(op, cache, rows, q.shape[1], self.top_k)
+
+    def pool(self, blk_begin: torch.Tensor, max_new_blocks: int):
+        B.qsa_pool_blocks(self.cache, blk_begin, max_new_blocks)
+
+    def select(self, scores=None):
+        B.qsa_topk_blocks(self.cache, self.rows, self.top_k, self.sel, self.n_sel, self.ws_topk,
+                          scores=scores, q_idx=self.q_idx, w=self.w)
+
+    def attend(self):
+        fn = B.qsa_attn_decode if self.mode == "decode" else B.qsa_attn_prefill
+        fn(self.cache, self.rows, self.q, self.sel, self.n_sel, self.top_k, self.scale,
+           self.out, self.ws_attn)
+
+    def run(self, blk_begin=None, max_new_blocks: int = 0):
+        if blk_begin is not None and max_new_blocks > 0:
+            self.pool(blk_begin, max_new_blocks)
+        self.select()
+        self.attend()
+        return self.sel, self.n_sel, self.out
+
+
+class DenseStep:
+    """Dense causal GQA attention of the same rows (comparison baseline)."""
+
+    def __init__(self, cache: B.CacheView, rows: B.QueriesView, q, scale: float,
+                 mode: str = "decode"):
+        self.cache, self.rows, self.q, self.scale, self.mode = cache, rows, q, float(scale), mode
+        self.out = torch.empty_like(q)
+        op = B.QSA_OP_DENSE_DECODE if mode == "decode" else B.QSA_OP_DENSE_PREFILL
+        self.ws = B.workspace(op, cache, rows, q.shape[1], 0)
+
+    def run(self):
+        fn = B.qsa_dense_attn_decode if self.mode == "decode" else B.qsa_dense_attn_prefill
+        fn(self.cache, self.rows, self.q, self.scale, self.out, self.ws)
+        return self.out
+
+
+def pool_all(cache: B.CacheView, n_seqs: int, n_blocks: int, device) -> None:
+    """Pool blocks 0 .. n_blocks-1 of every sequence (cache set-up)."""
+    begin = torch.zeros(n_seqs, dtype=torch.int32, device=device)
+    B.qsa_pool_blocks(cache, begin, n_blocks)

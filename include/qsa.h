@@ -1,0 +1,209 @@
+/*
+ * qsa.h -- C ABI of libqsa, the MI355X (gfx950) hot path of Qwen Sparse
+ * Attention (QSA).
+ *
+ * What the calls compute (sources are the web pages describing the method):
+ *
+ *   - keieiax.jp glossary "Qwen Sparse Attention", section
+ *     4トークンずつまとめて、必要な場所を探す: the context is compressed into
+ *     4-token micro-blocks; a lightweight learned indexer estimates the
+ *     importance of each block; at most 512 blocks (2,048 tokens) are
+ *     selected per query.
+ *   - blog.cecily.jp/6295 (digest of llama.cpp PR #30965), paragraph on
+ *     Raschka's explanation: the indexer averages the keys of each block and
+ *     scores it, and blocks are taken best first; paragraph on the trade-offs:
+ *     whole blocks are read, and the budget is 2,048 tokens plus the current
+ *     fractional block.
+ *   - ai-manual.ru, "Экономия VRAM в llama.cpp: что даёт QSA-выбор без
+ *     kq_mask", section "QSA-выбор и kq_mask": the selection is consumed
+ *     without materialising a [queries x keys] mask.
+ *   - ai-manual.ru, "llama.cpp получил разреженный Flash Attention для Qwen4
+ *     на CUDA", section "Разреженный Flash Attention и обычный": attention is
+ *     computed tile by tile without writing intermediates to global memory,
+ *     and the sparse variant drops token pairs.
+ *   - keieiax.jp glossary, section 長文AIのコストと応答時間にどう影響する？: the
+ *     reference point is dense grouped-query attention (GQA); the dense calls
+ *     below provide it on the same cache.
+ *
+ * The indexer score is not printed on the pages; this library fixes it as
+ *     s[b] = sum_h w[h] * max(0, q_idx[h] . kbar[b])
+ * with one indexer key head (dimension Di) shared by all indexer query heads.
+ *
+ * Conventions shared by every call:
+ *   - Ownership: every pointer inside the structs and every array argument
+ *     is DEVICE memory owned by the caller, unless marked "host".  The
+ *     library never allocates or frees memory and keeps no pointer after a
+ *     call returns.
+ *   - Execution: every call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream) and returns; it
+ *     never synchronises and never copies device data to the host.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; on failure nothing is written and a negative qsa_status is
+ *     returned.  QSA_ERR_HIP reports a failed launch (hipGetLastError).
+ *     Device-side data (page ids, positions, seq_len, sel) must be in range;
+ *     out-of-range device data is undefined behaviour.
+ *   - Positions: query row i belongs to sequence seq_id[i] and sits at
+ *     absolute position pos[i] (0-based); its own K/V/indexer key is already
+ *     in the cache, and it may see tokens 0..pos[i] only.  Its own block is
+ *     b_own = pos[i] / 4; blocks 0..b_own-1 are its candidates; the own
+ *     block's tokens 4*b_own..pos[i] are always attended.
+ *   - Workspaces: size them with qsa_workspace_size().  A workspace must be
+ *     zero-filled once before its first use; every call leaves its counters
+ *     at zero again when its kernels finish, so a workspace can be reused by
+ *     later calls on the same stream without clearing.  Calls that share one
+ *     workspace must not run concurrently.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_BLOCK 4        /* tokens per micro-block */
+#define QSA_MAX_TOPK 512   /* largest supported top_k (the pages' budget) */
+#define QSA_MAX_BLOCKS (1 << 21) /* candidate blocks per query (8M tokens) */
+
+typedef enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
+  QSA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype this build lacks   */
+  QSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  QSA_ERR_HIP = -4          /* the HIP runtime reported an error           */
+} qsa_status;
+
+typedef enum qsa_dtype { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+typedef enum qsa_op {
+  QSA_OP_TOPK = 0,
+  QSA_OP_ATTN_DECODE = 1,
+  QSA_OP_ATTN_PREFILL = 2,
+  QSA_OP_DENSE_DECODE = 3,
+  QSA_OP_DENSE_PREFILL = 4
+} qsa_op;
+
+/* Paged cache shared by K, V, the indexer keys and the pooled block keys.
+ * Logical token j of sequence s lives in physical page
+ * block_table[s * max_pages_per_seq + j / page_size], slot j % page_size. */
+typedef struct qsa_cache {
+  int32_t dtype;             /* qsa_dtype of k, v, kidx, kbar, q, q_idx, out */
+  int32_t page_size;         /* tokens per page: a power of two, >= 4        */
+  int32_t n_kv_heads;        /* Hkv                                          */
+  int32_t head_dim;          /* D: 32, 64 or 128                             */
+  int32_t idx_dim;           /* Di: 16, 32, 64 or 128                        */
+  int32_t n_seqs;            /* rows of block_table / entries of seq_len     */
+  int32_t max_pages_per_seq; /* row stride of block_table                    */
+  int32_t max_seq_len;       /* host: upper bound of every seq_len[s]        */
+  int64_t n_pages;           /* host: pages in the pool (k, v, kidx, kbar)   */
+  const int32_t *block_table;/* [n_seqs][max_pages_per_seq] physical pages   */
+  const int32_t *seq_len;    /* [n_seqs] tokens present in the cache         */
+  const void *k;             /* [n_pages][page_size][Hkv][D]                 */
+  const void *v;             /* [n_pages][page_size][Hkv][D]                 */
+  const void *kidx;          /* [n_pages][page_size][Di]   indexer keys      */
+  void *kbar;                /* [n_pages][page_size/4][Di] pooled keys       */
+} qsa_cache;
+
+/* Query rows of one call. */
+typedef struct qsa_queries {
+  int32_t n_rows;            /* host: T                                       */
+  int32_t max_pos;           /* host: upper bound of every pos[i]             */
+  const int32_t *seq_id;     /* [T] sequence of each row                      */
+  const int32_t *pos;        /* [T] absolute position of each row             */
+} qsa_queries;
+
+/* Step 1 -- pooling (glossary: 4-token micro-blocks; PR #30965 digest:
+ * the indexer averages the keys of each block).
+ * For every sequence s, for the complete blocks b with
+ *   blk_begin[s] <= b < min(seq_len[s] / 4, blk_begin[s] + max_new_blocks),
+ * writes kbar[b] = (((kidx[4b] + kidx[4b+1]) + kidx[4b+2]) + kidx[4b+3]) / 4,
+ * summed in float32 and rounded to nearest-even in the cache dtype.
+ * blk_begin: [n_seqs] device.  max_new_blocks (host) bounds the launch; 0 is
+ * a no-op. */
+qsa_status qsa_pool_blocks(const qsa_cache *c, const int32_t *blk_begin,
+                           int32_t max_new_blocks, void *stream);
+
+/* Step 2 -- indexer scores (glossary: the indexer rates every block).
+ * For every row i and candidate block b < pos[i] / 4:
+ *   scores[i * ld + b] = sum_h w[i*Hi + h] * max(0, q_idx[i][h] . kbar[b])
+ * accumulated in float32 (a -0 result is stored as +0).  Columns >= pos[i]/4
+ * are not written.  q_idx: [T][Hi][Di] in the cache dtype; w: [T][Hi]
+ * float32; 1 <= n_idx_heads <= 8; ld >= max_pos / 4 (host). */
+qsa_status qsa_index_scores(const qsa_cache *c, const qsa_queries *qm,
+                            const void *q_idx, const float *w,
+                            int32_t n_idx_heads, float *scores, int64_t ld,
+                            void *stream);
+
+/* Step 3 -- top-k block selection (glossary: at most 512 blocks per query,
+ * best first).  For every row i with n = pos[i] / 4 candidates:
+ *   n_sel[i] = min(top_k, n);
+ *   sel[i * top_k + j], j < n_sel[i]: the ids of the n_sel[i] highest scores,
+ *       ties broken toward the lower block id, written in ascending order;
+ *   sel[i * top_k + j], j >= n_sel[i]: -1.
+ * Score source: if scores != NULL they are read from scores[i * ld + b]
+ * (as written by qsa_index_scores); if scores == NULL (fused mode) they are
+ * computed from q_idx, w and kbar as in qsa_index_scores, and q_idx, w,
+ * n_idx_heads must be given.  1 <= top_k <= QSA_MAX_TOPK.
+ * ws: workspace of qsa_workspace_size(QSA_OP_TOPK, ...) bytes. */
+qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
+                           const float *scores, int64_t ld,
+                           const void *q_idx, const float *w,
+                           int32_t n_idx_heads, int32_t top_k, int32_t *sel,
+                           int32_t *n_sel, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Steps 4/5 -- block-sparse attention without a mask (PR #30965 digest:
+ * whole selected blocks plus the current fractional block; sparse FA
+ * explainer: tiled softmax attention).  For every row i and query head hq
+ * (KV head hk = hq / (n_q_heads / Hkv)), over the token set
+ *   S_i = {4b .. 4b+3 : b in sel[i][0 .. n_sel[i]-1]} U {4*(pos[i]/4) .. pos[i]}
+ *   out[i][hq] = sum_{j in S_i} softmax_j(scale * q[i][hq] . K[j][hk]) V[j][hk]
+ * accumulated in float32 and rounded to nearest-even in the cache dtype.
+ * q, out: [T][n_q_heads][D] in the cache dtype; sel/n_sel as written by
+ * qsa_topk_blocks (row stride top_k).
+ * qsa_attn_decode splits each row's token set across workgroups (for few
+ * rows); qsa_attn_prefill gives each row its own workgroup (for many rows).
+ * Both compute the same result. */
+qsa_status qsa_attn_decode(const qsa_cache *c, const qsa_queries *qm,
+                           const void *q, int32_t n_q_heads,
+                           const int32_t *sel, const int32_t *n_sel,
+                           int32_t top_k, float scale, void *out, void *ws,
+                           size_t ws_bytes, void *stream);
+qsa_status qsa_attn_prefill(const qsa_cache *c, const qsa_queries *qm,
+                            const void *q, int32_t n_q_heads,
+                            const int32_t *sel, const int32_t *n_sel,
+                            int32_t top_k, float scale, void *out, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Comparison baseline (glossary: dense GQA attention kernels): causal
+ * attention of every row over all tokens 0..pos[i] of its sequence, same
+ * layouts and rounding as the sparse calls. */
+qsa_status qsa_dense_attn_decode(const qsa_cache *c, const qsa_queries *qm,
+                                 const void *q, int32_t n_q_heads,
+                                 float scale, void *out, void *ws,
+                                 size_t ws_bytes, void *stream);
+qsa_status qsa_dense_attn_prefill(const qsa_cache *c, const qsa_queries *qm,
+                                  const void *q, int32_t n_q_heads,
+                                  float scale, void *out, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by `op` (a qsa_op) for these shapes; host-only,
+ * reads only host fields of c and qm.  top_k is ignored by the dense ops,
+ * n_q_heads by QSA_OP_TOPK.  Returns 0 for a null argument or unknown op. */
+size_t qsa_workspace_size(int32_t op, const qsa_cache *c,
+                          const qsa_queries *qm, int32_t n_q_heads,
+                          int32_t top_k);
+
+/* Static description of a status code. */
+const char *qsa_status_string(qsa_status s);
+
+/* Library version, (major << 16) | minor. */
+int32_t qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,104 @@
+"""Test-side helpers for the GPU parity tests: draw a workload on the GPU,
+run the HIP path through the C ABI, and hand the same inputs to the CPU
+oracle (paged device tensors -> contiguous float64 numpy)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from block_sparse_attention_32_amd import binding as B
+from block_sparse_attention_32_amd import pipeline as P
+from block_sparse_attention_32_amd import workloads as W
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}   # max-abs output tolerance
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+class Problem:
+    """A workload drawn on the GPU with its views for the C ABI."""
+
+    def __init__(self, wl: W.Workload, device, seq_id=None, pos=None, chunk_index=0):
+        self.wl = wl
+        self.device = device
+        self.cache = W.make_cache(wl, device=device)
+        if pos is None:
+            seq_id, pos = W.step_rows(wl, chunk_index)
+        self.seq_id_list = [int(s) for s in seq_id]
+        self.pos_list = [int(p) for p in pos]
+        self.qs = W.make_queries(wl, self.cache, seq_id, pos, device=device)
+        self.cv = B.CacheView.from_cache(self.cache)
+        self.rows = B.QueriesView(self.qs.seq_id, self.qs.pos, max(self.pos_list))
+        self._kbar_oracle = {}
+
+    # ---- HIP path
+    def pool_all(self):
+        P.pool_all(self.cv, self.wl.n_seqs, self.wl.total_len // 4, self.device)
+
+    def step(self, mode=None):
+        mode = mode or self.wl.mode
+        st = P.QsaStep(self.cv, self.rows, self.qs.q, self.qs.q_idx, self.qs.w, self.wl.top_k,
+                       self.wl.scale, mode)
+        st.run()
+        return st
+
+    def gpu_kbar(self, s: int) -> np.ndarray:
+        """Pooled keys of sequence s as written by the GPU, in block order."""
+        wl = self.wl
+        nb = wl.total_len // 4
+        n_p = -(-wl.total_len // wl.page_size)
+        pages = self.cache.block_table[s, :n_p].long()
+        kb = self.cache.kbar[pages].reshape(-1, wl.di)[:nb]
+        return f64(kb)
+
+    # ---- oracle side
+    def kbar_oracle(self, s: int) -> np.ndarray:
+        if s not in self._kbar_oracle:
+            _, _, kidx = W.seq_view(self.cache, s)
+            self._kbar_oracle[s] = O.pool_blocks(f64(kidx), self.wl.dtype)
+        return self._kbar_oracle[s]
+
+    def oracle_select(self, i: int) -> np.ndarray:
+        s, t = self.seq_id_list[i], self.pos_list[i]
+        return O.qsa_select_row(self.kbar_oracle(s), f64(self.qs.q_idx[i]),
+                                f64(self.qs.w[i]), t, self.wl.top_k)
+
+    def oracle_scores(self, i: int) -> np.ndarray:
+        s, t = self.seq_id_list[i], self.pos_list[i]
+        n = O.n_candidates(t)
+        return O.block_scores(self.kbar_oracle(s)[:n], f64(self.qs.q_idx[i]), f64(self.qs.w[i]))
+
+    def token_kv(self, s: int, tokens: np.ndarray):
+        """float64 K, V rows [len(tokens), Hkv, D] of the given tokens of seq s."""
+        wl = self.wl
+        tok = torch.as_tensor(tokens, dtype=torch.long, device=self.device)
+        pages = self.cache.block_table[s].long()[tok // wl.page_size]
+        slots = tok % wl.page_size
+        return f64(self.cache.k[pages, slots]), f64(self.cache.v[pages, slots])
+
+    def oracle_attend(self, i: int, sel: np.ndarray) -> np.ndarray:
+        s, t = self.seq_id_list[i], self.pos_list[i]
+        toks = O.token_set(sel, t)
+        k, v = self.token_kv(s, toks)
+        return O.attend(f64(self.qs.q[i]), k, v, np.arange(len(toks)), self.wl.scale)
+
+    def oracle_dense(self, i: int) -> np.ndarray:
+        s, t = self.seq_id_list[i], self.pos_list[i]
+        k, v = self.token_kv(s, np.arange(t + 1))
+        return O.dense_causal(f64(self.qs.q[i])[None], k, v, np.array([t]), self.wl.scale)[0]
+
+
+def sel_rows(sel: torch.Tensor, n_sel: torch.Tensor):
+    sel = sel.cpu().numpy()
+    n = n_sel.cpu().numpy()
+    return [sel[i, : n[i]] for i in range(len(n))], sel, n
+
+
+def assert_sel_row(got_sel_row: np.ndarray, got_n: int, want: np.ndarray, top_k: int):
+    assert got_n == len(want), (got_n, len(want))
+    assert np.array_equal(got_sel_row[:got_n], want), "selected block ids differ"
+    assert np.all(got_sel_row[got_n:top_k] == -1), "padding must be -1"

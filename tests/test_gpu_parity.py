@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Selected block ids and pooled keys/scores are compared bit for bit (the
+indexer inputs lie on a grid where float32 arithmetic is exact); attention
+outputs within max-abs 2e-2 (bfloat16) / 1e-4 (float32).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_attention_32_amd import binding as B
+from block_sparse_attention_32_amd import pipeline as P
+from block_sparse_attention_32_amd import workloads as W
+
+from gpu_helpers import TOL, Problem, assert_sel_row, f64, sel_rows
+
+pytestmark = pytest.mark.gpu
+
+WL = W.WORKLOADS
+SMALL_BF16 = WL["decode_8x32k"].replace(n_ctx=3000, n_seqs=3)
+
+# rows of one long sequence covering: no candidate, n <= k, the one-pass
+# path (n <= 8192 candidates) and the two-pass path, every t mod 4
+MIXED = WL["prefill_8k_at_128k"].replace(name="mixed", n_ctx=60000, n_new=1, n_needles=6,
+                                          permute_pages=True, seed=77)
+MIXED_POS = [0, 1, 3, 4, 7, 100, 2047, 2048, 2050, 2051, 2052, 2055, 4000, 32767, 32768,
+             32771, 32774, 40000, 59999, 60000]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ pooling
+
+@pytest.mark.parametrize("wl", [WL["tiny_decode"], SMALL_BF16], ids=lambda w: w.name)
+def test_pool_bit_exact(gpu, wl):
+    _say(f"pool {wl.name}")
+    pb = Problem(wl, gpu)
+    pb.pool_all()
+    torch.cuda.synchronize()
+    for s in range(wl.n_seqs):
+        assert np.array_equal(pb.gpu_kbar(s), pb.kbar_oracle(s))
+
+
+def test_pool_ranges_and_nongrid(gpu):
+    _say("pool ranges")
+    wl = SMALL_BF16
+    pb = Problem(wl, gpu)
+    # off-grid keys: float32 sum then one rounding vs float64 mean then one
+    # rounding may differ by one bfloat16 step; on the grid they agree exactly
+    pb.cache.kidx.copy_(torch.randn(pb.cache.kidx.shape, device=gpu).to(torch.bfloat16))
+    begin = torch.tensor([5, 0, 700], dtype=torch.int32, device=gpu)
+    B.qsa_pool_blocks(pb.cv, begin, 40)
+    torch.cuda.synchronize()
+    for s in range(wl.n_seqs):
+        got = pb.gpu_kbar(s)
+        b0 = int(begin[s])
+        want = pb.kbar_oracle(s)
+        assert np.all(got[:b0] == 0) and np.all(got[b0 + 40:] == 0)
+        blk = got[b0:b0 + 40]
+        ref = want[b0:b0 + 40]
+        step = np.ldexp(1.0, np.frexp(np.abs(ref) + 1e-30)[1] - 8)
+        assert np.all(np.abs(blk - ref) <= step)
+
+
+# ------------------------------------------------------------------ scores
+
+@pytest.mark.parametrize("wl,pos", [(WL["tiny_decode"], None), (MIXED, MIXED_POS)],
+                         ids=["tiny", "mixed"])
+def test_scores_bit_exact(gpu, wl, pos):
+    _say(f"scores {wl.name}")
+    seq = None if pos is None else [0] * len(pos)
+    pb = Problem(wl, gpu, seq, pos)
+    pb.pool_all()
+    max_n = max(pb.pos_list) // 4
+    scores = torch.full((len(pb.pos_list), max(max_n, 1)), float("nan"), device=gpu)
+    B.qsa_index_scores(pb.cv, pb.rows, pb.qs.q_idx, pb.qs.w, scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    for i, t in enumerate(pb.pos_list):
+        n = t // 4
+        want = pb.oracle_scores(i)
+        assert np.array_equal(got[i, :n].astype(np.float64), want), f"row {i} t={t}"
+        assert np.all(np.signbit(got[i, :n]) == False)  # noqa: E712  (-0 stored as +0)
+        assert np.all(np.isnan(got[i, n:]))             # untouched past the candidates
+
+
+# ------------------------------------------------------------------ top-k
+
+def _check_topk(pb, st):
+    got_rows, sel, n = sel_rows(st.sel, st.n_sel)
+    for i in range(len(pb.pos_list)):
+        assert_sel_row(sel[i], int(n[i]), pb.oracle_select(i), pb.wl.top_k)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
+@pytest.mark.parametrize("case", ["tiny", "decode_8x32k", "mixed"])
+def test_topk_bit_exact(gpu, case, fused):
+    _say(f"topk {case} fused={fused}")
+    if case == "tiny":
+        pb = Problem(WL["tiny_decode"], gpu)
+    elif case == "decode_8x32k":
+        pb = Problem(WL["decode_8x32k"], gpu)
+    else:
+        pb = Problem(MIXED, gpu, [0] * len(MIXED_POS), MIXED_POS)
+    pb.pool_all()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, pb.wl.top_k, pb.wl.scale)
+    st.sel.fill_(-7)
+    if fused:
+        st.select()
+    else:
+        max_n = max(max(pb.pos_list) // 4, 1)
+        scores = torch.empty((len(pb.pos_list), max_n), device=gpu)
+        B.qsa_index_scores(pb.cv, pb.rows, pb.qs.q_idx, pb.qs.w, scores)
+        st.select(scores=scores)
+    torch.cuda.synchronize()
+    _check_topk(pb, st)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
+@pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190)])
+def test_topk_ties_lower_id_wins(gpu, n_tied, first, fused):
+    """Many blocks with identical top scores: the lowest ids win.  1024 tied
+    blocks in one chunk overflow its survivor slots (exact fallback)."""
+    _say(f"ties {n_tied} {first} fused={fused}")
+    wl = MIXED.replace(n_ctx=80004)
+    pos = [20000 * 4 + 1, 9000 * 4 + 3, 8000 * 4, 600 * 4 + 2]
+    pb = Problem(wl, gpu, [0] * len(pos), pos)
+    pat = (3.0 * pb.cache.direction[0]).to(torch.bfloat16)
+    for b in range(first, first + n_tied):
+        for i in range(4):
+            tok = 4 * b + i
+            page = int(pb.cache.block_table[0, tok // wl.page_size])
+            pb.cache.kidx[page, tok % wl.page_size] = pat
+    pb.pool_all()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, wl.top_k, wl.scale)
+    if fused:
+        st.select()
+    else:
+        scores = torch.empty((len(pos), max(pos) // 4), device=gpu)
+        B.qsa_index_scores(pb.cv, pb.rows, pb.qs.q_idx, pb.qs.w, scores)
+        st.select(scores=scores)
+    torch.cuda.synchronize()
+    _check_topk(pb, st)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
+def test_topk_all_scores_equal(gpu, fused):
+    """q_idx = 0 gives every block score 0: ids 0..k-1 are selected."""
+    _say(f"all-equal fused={fused}")
+    pos = [3, 2100, 30000, 80003]
+    pb = Problem(MIXED.replace(n_ctx=80004), gpu, [0] * len(pos), pos)
+    pb.qs.q_idx.zero_()
+    pb.pool_all()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, 512, pb.wl.scale)
+    if fused:
+        st.select()
+    else:
+        scores = torch.empty((len(pos), max(pos) // 4), device=gpu)
+        B.qsa_index_scores(pb.cv, pb.rows, pb.qs.q_idx, pb.qs.w, scores)
+        st.select(scores=scores)
+    torch.cuda.synchronize()
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    for i, t in enumerate(pos):
+        m = min(512, t // 4)
+        assert n[i] == m and np.array_equal(sel[i, :m], np.arange(m))
+        assert np.all(sel[i, m:] == -1)
+
+
+# ------------------------------------------------------------------ attention
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("case", ["tiny", "mixed"])
+def test_attention_given_selection(gpu, case, mode):
+    """Attention alone, fed the oracle's selection."""
+    _say(f"attention {case} {mode}")
+    if case == "tiny":
+        pb = Problem(WL["tiny_decode"], gpu)
+    else:
+        pb = Problem(MIXED, gpu, [0] * len(MIXED_POS), MIXED_POS)
+    wl = pb.wl
+    T = len(pb.pos_list)
+    sel = torch.full((T, wl.top_k), -1, dtype=torch.int32)
+    n_sel = torch.zeros(T, dtype=torch.int32)
+    sels = []
+    for i in range(T):
+        s = pb.oracle_select(i)
+        sels.append(s)
+        sel[i, : len(s)] = torch.from_numpy(s.astype(np.int32))
+        n_sel[i] = len(s)
+    sel, n_sel = sel.to(gpu), n_sel.to(gpu)
+    out = torch.full_like(pb.qs.q, float("nan"))
+    op = B.QSA_OP_ATTN_DECODE if mode == "decode" else B.QSA_OP_ATTN_PREFILL
+    ws = B.workspace(op, pb.cv, pb.rows, wl.hq, wl.top_k)
+    fn = B.qsa_attn_decode if mode == "decode" else B.qsa_attn_prefill
+    fn(pb.cv, pb.rows, pb.qs.q, sel, n_sel, wl.top_k, wl.scale, out, ws)
+    torch.cuda.synchronize()
+    got = f64(out)
+    for i in range(T):
+        want = pb.oracle_attend(i, sels[i])
+        err = np.abs(got[i] - want).max()
+        assert err <= TOL[wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_dense_attention(gpu, mode):
+    _say(f"dense {mode}")
+    pos = [0, 5, 2051, 4000, 9001]
+    pb = Problem(MIXED.replace(n_ctx=9002), gpu, [0] * len(pos), pos)
+    out = torch.full_like(pb.qs.q, float("nan"))
+    st = P.DenseStep(pb.cv, pb.rows, pb.qs.q, pb.wl.scale, mode)
+    st.out = out
+    st.run()
+    torch.cuda.synchronize()
+    got = f64(out)
+    for i in range(len(pos)):
+        err = np.abs(got[i] - pb.oracle_dense(i)).max()
+        assert err <= TOL["bf16"], f"row {i} err={err}"
+
+
+# ------------------------------------------------------------------ end to end
+
+def _e2e(pb, rows_to_check=None, mode=None):
+    st = pb.step(mode)
+    torch.cuda.synchronize()
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    got = f64(st.out)
+    idx = range(len(pb.pos_list)) if rows_to_check is None else rows_to_check
+    worst = 0.0
+    for i in idx:
+        want_sel = pb.oracle_select(i)
+        assert_sel_row(sel[i], int(n[i]), want_sel, pb.wl.top_k)
+        err = np.abs(got[i] - pb.oracle_attend(i, want_sel)).max()
+        worst = max(worst, err)
+        assert err <= TOL[pb.wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
+    assert not np.isnan(got).any()
+    return st, worst
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_8x32k", "decode_1m"])
+def test_e2e_decode_configs(gpu, name):
+    _say(f"e2e {name}")
+    pb = Problem(WL[name], gpu)
+    pb.pool_all()
+    st, worst = _e2e(pb)
+    _say(f"  max err {worst:.3g}")
+    # planted needles are selected
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    for i, s in enumerate(pb.seq_id_list):
+        assert set(pb.cache.needles[s]) <= set(sel[i, : n[i]].tolist())
+
+
+def test_e2e_prefill_8k_at_128k(gpu):
+    _say("e2e prefill_8k_at_128k")
+    wl = WL["prefill_8k_at_128k"]
+    pb = Problem(wl, gpu)
+    pb.pool_all()
+    T = len(pb.pos_list)
+    check = sorted(set([0, 1, 2, 3, T - 1, T - 2] + list(range(5, T, 181))))
+    _e2e(pb, check)
+
+
+@pytest.mark.parametrize("chunk", [0, 31])
+def test_e2e_prefill_1m_chunk(gpu, chunk):
+    _say(f"e2e prefill_1m chunk {chunk}")
+    wl = WL["prefill_1m"]
+    pb = Problem(wl, gpu, chunk_index=chunk)
+    pb.pool_all()
+    T = len(pb.pos_list)
+    check = sorted(set([0, 1, 2, 3, 2047, 2048, 2051, T - 1] + list(range(11, T, 1531))))
+    _e2e(pb, check)
+
+
+def test_decode_with_boundary_margin(gpu):
+    """Decode with a score gap of at least 2^-4 at the k-th boundary: blocks
+    just below the boundary get their indexer keys halved (which halves
+    their scores and keeps the inputs on the grid)."""
+    _say("margin")
+    wl = WL["decode_8x32k"]
+    pb = Problem(wl, gpu)
+    margin = 2.0 ** -4
+    for _ in range(4):
+        changed = False
+        for i, s in enumerate(pb.seq_id_list):
+            pb._kbar_oracle.pop(s, None)
+            sc = pb.oracle_scores(i)
+            order = np.lexsort((np.arange(len(sc)), -sc))
+            kth = sc[order[wl.top_k - 1]]
+            band = [int(b) for b in order[wl.top_k:] if sc[b] >= kth - margin]
+            for b in band:
+                for j in range(4):
+                    tok = 4 * b + j
+                    page = int(pb.cache.block_table[s, tok // wl.page_size])
+                    pb.cache.kidx[page, tok % wl.page_size] *= 0.5
+            changed |= bool(band)
+        if not changed:
+            break
+    assert not changed
+    pb.pool_all()
+    _e2e(pb)
+
+
+def test_determinism_and_poison(gpu):
+    _say("determinism")
+    pb = Problem(WL["decode_8x32k"].replace(n_seqs=3), gpu)
+    pb.pool_all()
+    a = pb.step()
+    a.out.fill_(float("nan"))
+    a.sel.fill_(-5)
+    a.run()
+    torch.cuda.synchronize()
+    sel1, out1 = a.sel.clone(), a.out.clone()
+    assert not torch.isnan(out1).any()
+    a.run()
+    torch.cuda.synchronize()
+    assert torch.equal(sel1, a.sel) and torch.equal(out1, a.out)
