@@ -197,6 +197,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_1m", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the QSA path "
@@ -208,6 +210,13 @@ def main():
     B.lib()  # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if wl.mode != "decode":
         raise SystemExit("prefill benchmarking is not wired yet")
     wall, kern, work, kernels, files, dense_ms, ctx = run_decode(wl, args.steps, args.warmup, dev)

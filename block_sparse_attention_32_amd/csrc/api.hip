@@ -1,6 +1,7 @@
 // C ABI of libqsa: host-side validation, workspace planning and launches.
 // Every call validates its arguments before enqueuing anything and never
 // synchronises, allocates or copies device data to the host.
+#include <stdint.h>
 #include <string.h>
 
 #include "attention.hpp"
@@ -12,8 +13,9 @@ namespace {
 
 constexpr int kRowBatch = 4096;              // top-k rows per launch pair
 constexpr size_t kMaterializeBytes = 1u << 30;  // long rows keep scores below this
-constexpr int kTargetSplitWgs = 1024;        // decode: workgroups over all rows
-constexpr int kMinEntriesPerSplit = 4;
+constexpr int kTargetSplitWgs = 256;         // decode (generic kernel): workgroups over all rows
+constexpr int kMinEntriesPerSplit = 8;
+constexpr int64_t kMaxSplitWgs = 1024;       // decode (MFMA kernel): workgroup cap
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -35,6 +37,7 @@ qsa_status check_cache(const qsa_cache* c) {
     return QSA_ERR_INVALID_ARG;
   if (c->block_table == nullptr || c->seq_len == nullptr) return QSA_ERR_INVALID_ARG;
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)c->n_pages * c->page_size > INT32_MAX) return QSA_ERR_UNSUPPORTED;  // token rows fit int32
   if (c->idx_dim != 16 && c->idx_dim != 32 && c->idx_dim != 64 && c->idx_dim != 128)
     return QSA_ERR_UNSUPPORTED;
   return QSA_OK;
@@ -68,7 +71,7 @@ qsa_status launched() {
 struct TopkPlan {
   int rows, w_max, materialize;
   int64_t ws_ld;
-  size_t off_ctr, off_cc, off_tops, off_slots, off_scores, total;
+  size_t off_ctr, off_tops, off_scores, total;
 };
 
 TopkPlan topk_plan(const qsa_queries* qm) {
@@ -82,10 +85,8 @@ TopkPlan topk_plan(const qsa_queries* qm) {
   p.materialize = (size_t)p.rows * (size_t)full * 4 <= kMaterializeBytes;
   p.ws_ld = p.materialize ? full : (full < kDirectCap ? full : kDirectCap);
   size_t o = 0;
-  p.off_ctr = o;    o = align256(o + (size_t)4 * p.rows * 4);
-  p.off_cc = o;     o = align256(o + (size_t)p.rows * p.w_max * 4);
-  p.off_tops = o;   o = align256(o + (size_t)p.rows * kUnionCap * 4);
-  p.off_slots = o;  o = align256(o + (size_t)p.rows * kSlotCap * 8);
+  p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
+  p.off_tops = o;   o = align256(o + (size_t)p.rows * kUnionCap * 8);
   p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
   p.total = o;
   return p;
@@ -94,7 +95,7 @@ TopkPlan topk_plan(const qsa_queries* qm) {
 // ------------------------------------------------------------- attention plan
 
 struct AttnPlan {
-  int splits, eps, tile;
+  int splits, eps, tile, mfma;
   size_t off_cnt, off_ml, off_acc, total;
 };
 
@@ -103,9 +104,18 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
   const bool dense = (op == QSA_OP_DENSE_DECODE || op == QSA_OP_DENSE_PREFILL);
   const bool split = (op == QSA_OP_ATTN_DECODE || op == QSA_OP_DENSE_DECODE);
   const int entries = (dense ? qm->max_pos / QSA_BLOCK : top_k) + 1;
-  p.tile = attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
+  p.mfma = attn_mfma_supported(c->dtype, hq, c->n_kv_heads, c->head_dim) ? 1 : 0;
+  p.tile = p.mfma ? kMfmaTileTok : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
   const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
-  if (split) {
+  if (split && p.mfma) {
+    // one 8-block tile per wave: 4 waves share a split across the KV heads;
+    // grow the split when rows x splits would exceed kMaxSplitWgs
+    const int wph = 4 / c->n_kv_heads;
+    int eps = kMfmaTileEnt * wph;
+    while ((int64_t)rows * ((entries + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
+    p.eps = eps;
+    p.splits = (entries + eps - 1) / eps;
+  } else if (split) {
     int s = (kTargetSplitWgs + rows - 1) / rows;
     int s_max = (entries + kMinEntriesPerSplit - 1) / kMinEntriesPerSplit;
     if (s > s_max) s = s_max;
@@ -173,7 +183,10 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
     a.part_ml = reinterpret_cast<float*>(base + p.off_ml);
     a.part_acc = reinterpret_cast<float*>(base + p.off_acc);
   }
-  run_attention(a, c->dtype, c->head_dim, dense, qm->n_rows, as_stream(stream));
+  if (p.mfma)
+    run_attention_mfma(a, c->head_dim, dense, qm->n_rows, as_stream(stream));
+  else
+    run_attention(a, c->dtype, c->head_dim, dense, qm->n_rows, as_stream(stream));
   return launched();
 }
 
@@ -267,14 +280,8 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   t.materialize = p.materialize;
   t.ws_scores = reinterpret_cast<float*>(base + p.off_scores);
   t.ws_ld = p.ws_ld;
-  uint32_t* ctr = reinterpret_cast<uint32_t*>(base + p.off_ctr);
-  t.cnt_a = ctr;
-  t.cnt_b = ctr + p.rows;
-  t.flags = ctr + 2 * p.rows;
-  t.tau = ctr + 3 * p.rows;
-  t.chunk_cnt = reinterpret_cast<uint32_t*>(base + p.off_cc);
-  t.tops = reinterpret_cast<uint32_t*>(base + p.off_tops);
-  t.slots = reinterpret_cast<uint2*>(base + p.off_slots);
+  t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);
+  t.tops = reinterpret_cast<uint64_t*>(base + p.off_tops);
   for (int r0 = 0; r0 < qm->n_rows; r0 += p.rows) {
     const int rows = (qm->n_rows - r0) < p.rows ? (qm->n_rows - r0) : p.rows;
     t.row0 = r0;

@@ -158,11 +158,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int jo = 0; jo < kMaxOutPerThread; ++jo) {
     const int o = tid + jo * kAttnThreads;
-    if (jo < n_out && o < hq * D) a.part_acc[pbase * D + o] = acc[jo];
+    if (jo < n_out && o < hq * D) st_agent(a.part_acc + pbase * D + o, acc[jo]);
   }
   for (int h = tid; h < hq; h += kAttnThreads) {
-    a.part_ml[(pbase + h) * 2 + 0] = m_s[h];
-    a.part_ml[(pbase + h) * 2 + 1] = l_s[h];
+    st_agent(a.part_ml + (pbase + h) * 2 + 0, m_s[h]);
+    st_agent(a.part_ml + (pbase + h) * 2 + 1, l_s[h]);
   }
   if (!arrive_last(a.cnt + row, (uint32_t)a.n_splits, &flag)) return;
   // merge: out = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M)
@@ -173,17 +173,17 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
     float M = -INFINITY;
     for (int s = 0; s < a.n_splits; ++s) {
       const int64_t pb = ((int64_t)row * a.n_splits + s) * hq + h;
-      M = fmaxf(M, __builtin_nontemporal_load(a.part_ml + pb * 2));
+      M = fmaxf(M, a.part_ml[pb * 2]);
     }
     float L = 0.0f, O = 0.0f;
     for (int s = 0; s < a.n_splits; ++s) {
       const int64_t pb = ((int64_t)row * a.n_splits + s) * hq + h;
-      const float ms = __builtin_nontemporal_load(a.part_ml + pb * 2);
-      const float ls = __builtin_nontemporal_load(a.part_ml + pb * 2 + 1);
+      const float ms = a.part_ml[pb * 2];
+      const float ls = a.part_ml[pb * 2 + 1];
       if (ls > 0.0f) {
         const float f = __expf(ms - M);
         L = fmaf(ls, f, L);
-        O = fmaf(__builtin_nontemporal_load(a.part_acc + pb * D + (o % D)), f, O);
+        O = fmaf(a.part_acc[pb * D + (o % D)], f, O);
       }
     }
     orow[o] = from_f32<T>(O / L);

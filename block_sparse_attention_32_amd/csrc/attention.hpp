@@ -55,3 +55,17 @@ int attn_tile_tokens(int dtype, int hq, int hkv, int d);
 void run_attention(const AttnArgs& a, int dtype, int d, bool dense, int n_rows, hipStream_t st);
 
 }  // namespace qsa
+
+namespace qsa {
+
+// MFMA path (bfloat16, head_dim 64 or 128, up to 16 query heads per KV
+// head, 1, 2 or 4 KV heads): tile geometry.
+constexpr int kMfmaTileTok = 32;    // tokens per wave tile
+constexpr int kMfmaTileEnt = 8;     // token-list entries (blocks) per tile
+constexpr int kMfmaEntChunk = 512;  // entries staged in LDS per pass
+constexpr int kVPitch = 272;        // LDS bytes per staged V row (256 + 16)
+
+bool attn_mfma_supported(int dtype, int hq, int hkv, int d);
+void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st);
+
+}  // namespace qsa

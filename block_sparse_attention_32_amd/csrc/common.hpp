@@ -111,13 +111,23 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), lo);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum over the wave, returned in every lane: DPP inside each 16-lane
+// row, then the four row results read as scalars.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off);
-    v = v > o ? v : o;
-  }
-  return v;
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -143,24 +153,60 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// ---------------------------------------------------------------- grid sync
+// ---------------------------------------------------------------- DPP sums
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 1, 2, 4, 8, 16 or 32); every lane
+// of a group gets the group's sum.  DPP quad permutes and row mirrors keep
+// the data in VGPRs (no LDS crossbar).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);  // row_mirror
+  if constexpr (G >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// ---------------------------------------------------------------- hand-off
+
+// Data handed from one workgroup of a kernel to another is written with
+// agent-scope atomic stores (write-through past the XCD-private L2) and read
+// with agent-scope atomic loads, so no L2 write-back fence is needed.
+template <typename U>
+__device__ __forceinline__ void st_agent(U* p, U v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename U>
+__device__ __forceinline__ U ld_agent(const U* p) {
+  return __hip_atomic_load(const_cast<U*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // "Last workgroup" hand-off: every workgroup of a group calls this after
-// writing its results; exactly one (the last to arrive) gets true and may
-// read what the others wrote.  The counter is reset for the next call.
+// publishing its results with st_agent; exactly one (the last to arrive)
+// gets true.  Each wave first waits for its own stores to complete; the
+// counter is reset for the next call.  The last workgroup then invalidates
+// its caches once (agent-scope acquire), after which ordinary loads see the
+// published data and can be issued back to back.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected,
                                             uint32_t* smem_flag) {
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(counter, 1u);
+    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     bool last = (prev == expected - 1);
-    if (last) atomicExch(counter, 0u);
+    if (last) st_agent(counter, 0u);
     *smem_flag = last ? 1u : 0u;
   }
   __syncthreads();
-  bool last = *smem_flag != 0u;
-  if (last) __threadfence();
+  const bool last = *smem_flag != 0u;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
 

@@ -14,8 +14,12 @@
 //                 reported in ascending order.
 //
 // Streaming layout: a pooled key row is Di elements (128 B for 64 bf16);
-// G = 16 B / lane-vector lanes cooperate on one row so each load
-// instruction reads whole rows, fully coalesced.
+// G = Di / (16 B of elements) lanes cooperate on one row so each load
+// instruction reads whole rows, fully coalesced, and the per-row dot
+// products are summed across the G lanes with DPP.  A workgroup owns a chunk
+// of kChunk consecutive blocks of one query row: it first stages the
+// chunk's page ids in LDS, then issues every pooled-key load of the chunk
+// before using any, so one round trip to memory covers the whole chunk.
 #include "index.hpp"
 #include "select.hpp"
 
@@ -51,18 +55,18 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
 
 // ================================================================ scores
 
-// Per-thread slice of one query row's indexer: this lane's V dims of every
-// head, and the head weights.
-template <typename T, int DI>
+// Per-thread slice of one query row's indexer: this lane's V dims of each of
+// the HI heads (heads beyond the real count have zero weight), and weights.
+template <typename T, int DI, int HI>
 struct IdxQuery {
   static constexpr int V = Vec<T>::N;
   static constexpr int G = DI / V;
-  float q[kMaxIdxHeads][V];
-  float w[kMaxIdxHeads];
-  __device__ __forceinline__ void load(const T* q_idx_row, const float* w_row,
-                                       int hi, int part) {
+  float q[HI][V];
+  float w[HI];
+  __device__ __forceinline__ void load(const T* q_idx_row, const float* w_row, int hi,
+                                       int part) {
 #pragma unroll
-    for (int h = 0; h < kMaxIdxHeads; ++h) {
+    for (int h = 0; h < HI; ++h) {
       if (h < hi) {
         Vec<T>::load(q_idx_row + h * DI + part * V, q[h]);
         w[h] = w_row[h];
@@ -73,154 +77,166 @@ struct IdxQuery {
       }
     }
   }
-  // score of the row whose V-slice this lane loaded into x; all G lanes of
-  // the group return the same value
+  // score of the row whose V-slice this lane holds in x; all G lanes of the
+  // group return the same value
   __device__ __forceinline__ float score(const float (&x)[V]) const {
-    float d[kMaxIdxHeads];
+    float s = 0.0f;
 #pragma unroll
-    for (int h = 0; h < kMaxIdxHeads; ++h) {
+    for (int h = 0; h < HI; ++h) {
       float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) acc = fmaf(q[h][i], x[i], acc);
-      d[h] = acc;
+      acc = group_sum<G>(acc);
+      s = fmaf(w[h], fmaxf(acc, 0.0f), s);
     }
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) {
-#pragma unroll
-      for (int h = 0; h < kMaxIdxHeads; ++h) d[h] += __shfl_xor(d[h], off);
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kMaxIdxHeads; ++h) s = fmaf(w[h], fmaxf(d[h], 0.0f), s);
     return canon_zero(s);
   }
 };
 
-// Scores of blocks [c0, c0 + kChunk) of one row (blocks >= n get key 0 and
-// score 0), computed by the whole workgroup.  keys[i] receives the ordered
-// key of block c0 + i; if sc_out is given, sc_out[i] receives the score
-// (for i < n - c0).
-template <typename T, int DI>
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Page ids of the blocks [c0, c0 + kChunk) of sequence seq, staged in LDS.
+__device__ __forceinline__ void stage_pages(const PageMap& pm, int seq, int c0, int n,
+                                            int32_t* pages) {
+  const int first = (c0 * kBlock) >> pm.page_shift;
+  const int last_b = min(c0 + kChunk, n) - 1;
+  const int cnt = ((last_b * kBlock) >> pm.page_shift) - first + 1;
+  const int32_t* row = pm.table + (int64_t)seq * pm.max_pages + first;
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) pages[i] = row[i];
+  __syncthreads();
+}
+
+// Scores of blocks [c0, c0 + kChunk) of one row, computed by the whole
+// workgroup into keys[] (ordered keys; blocks >= n get key 0).
+template <typename T, int DI, int HI>
 __device__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
-                             const IdxQuery<T, DI>& iq, uint32_t* keys,
-                             float* sc_out) {
+                             const IdxQuery<T, DI, HI>& iq, int32_t* pages, uint32_t* keys) {
   constexpr int V = Vec<T>::N;
   constexpr int G = DI / V;
-  constexpr int RPI = 256 / G;           // rows per workgroup iteration
-  constexpr int NIT = kChunk / RPI;      // iterations per chunk
-  constexpr int U = NIT < 8 ? NIT : 8;   // loads in flight per thread
+  constexpr int RPI = 256 / G;            // rows per workgroup iteration
+  constexpr int NIT = kChunk / RPI;       // iterations per chunk
+  constexpr int U = NIT < 32 ? NIT : 32;  // loads in flight per thread
+  stage_pages(a.pm, seq, c0, n, pages);
   const T* kbar = static_cast<const T*>(a.kbar);
   const int gi = threadIdx.x / G, part = threadIdx.x % G;
+  const int first = (c0 * kBlock) >> a.pm.page_shift;
+  const int bsh = a.pm.page_shift - 2;  // log2(blocks per page)
 #pragma unroll 1
   for (int it0 = 0; it0 < NIT; it0 += U) {
-    float x[U][V];
-    bool ok[U];
+    uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = c0 + (it0 + u) * RPI + gi;
-      ok[u] = b < n;
-      if (ok[u]) {
-        Vec<T>::load(kbar + a.pm.block_slot(seq, b) * DI + part * V, x[u]);
+      if (b < n) {
+        const int64_t slot =
+            ((int64_t)pages[((b * kBlock) >> a.pm.page_shift) - first] << bsh) +
+            (b & ((1 << bsh) - 1));
+        raw[u] = *reinterpret_cast<const uint4*>(kbar + slot * DI + part * V);
       } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) x[u][i] = 0.0f;
+        raw[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      float x[V];
+      if constexpr (V == 8) {
+        float t8[8];
+        Vec<bf16_t>::unpack(raw[u], t8);
+#pragma unroll
+        for (int i = 0; i < V; ++i) x[i] = t8[i];
+      } else {
+        x[0] = __uint_as_float(raw[u].x);
+        x[1] = __uint_as_float(raw[u].y);
+        x[2] = __uint_as_float(raw[u].z);
+        x[3] = __uint_as_float(raw[u].w);
+      }
       const int i = (it0 + u) * RPI + gi;
-      float s = iq.score(x[u]);
-      if (part == 0) keys[i] = ok[u] ? score_key(s) : 0u;
+      const float s = iq.score(x);
+      if (part == 0) keys[i] = (c0 + i < n) ? score_key(s) : 0u;
     }
   }
   __syncthreads();
-  if (sc_out != nullptr) {
-    for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
-      if (c0 + i < n) {
-        uint32_t k = keys[i];
-        uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-        sc_out[i] = __uint_as_float(u);
-      }
-    }
-  }
 }
 
-template <typename T, int DI>
-__global__ void __launch_bounds__(256) scores_kernel(IdxArgs a, float* scores,
-                                                     int64_t ld) {
+template <typename T, int DI, int HI>
+__global__ void __launch_bounds__(256) scores_kernel(IdxArgs a, float* scores, int64_t ld) {
   __shared__ uint32_t keys[kChunk];
+  __shared__ int32_t pages[kChunk];
   const int row = blockIdx.y;
   const int seq = a.seq_of(row);
   const int n = a.pos_of(row) / kBlock;
   const int c0 = blockIdx.x * kChunk;
   if (c0 >= n) return;
-  IdxQuery<T, DI> iq;
-  iq.load(static_cast<const T*>(a.q_idx) + (int64_t)row * a.hi * DI,
-          a.w + (int64_t)row * a.hi, a.hi, threadIdx.x % IdxQuery<T, DI>::G);
-  chunk_scores<T, DI>(a, seq, n, c0, iq, keys, scores + (int64_t)row * ld + c0);
+  IdxQuery<T, DI, HI> iq;
+  iq.load(static_cast<const T*>(a.q_idx) + (int64_t)row * a.hi * DI, a.w + (int64_t)row * a.hi,
+          a.hi, threadIdx.x % IdxQuery<T, DI, HI>::G);
+  chunk_scores<T, DI, HI>(a, seq, n, c0, iq, pages, keys);
+  float* out = scores + (int64_t)row * ld + c0;
+  for (int i = threadIdx.x; i < kChunk && c0 + i < n; i += blockDim.x)
+    out[i] = key_to_score(keys[i]);
 }
 
 // ================================================================ top-k
 
-// Per-row plan shared by both passes.
+// Per-row plan.
 struct RowPlan {
-  int seq, n, W, jw, sc;
+  int seq, n, W, jw;
   __device__ __forceinline__ RowPlan(const TopkArgs& t, int row) {
     seq = t.idx.seq_of(row);
     n = t.idx.pos_of(row) / kBlock;
     W = (n + kChunk - 1) / kChunk;
     jw = row_jw(n, t.top_k);
-    sc = W > 0 ? kSlotCap / W : 0;
-  }
-};
-
-// key of candidate e of a row, from whichever score source is available
-template <typename T, int DI>
-struct ScoreKey {
-  const TopkArgs* t;
-  int row_local, row, seq;
-  IdxQuery<T, DI>* iq;  // fused recompute (lane-local full dot product)
-  const float* src;     // stored scores of this row, or null
-  __device__ __forceinline__ uint32_t operator()(int e) const {
-    if (src != nullptr) return score_key(src[e]);
-    // recompute: this lane alone reads the whole pooled row
-    const T* kbar = static_cast<const T*>(t->idx.kbar);
-    const T* p = kbar + t->idx.pm.block_slot(seq, e) * DI;
-    float d[kMaxIdxHeads];
-#pragma unroll
-    for (int h = 0; h < kMaxIdxHeads; ++h) d[h] = 0.0f;
-    for (int c = 0; c < DI; c += Vec<T>::N) {
-      float x[Vec<T>::N];
-      Vec<T>::load(p + c, x);
-      const T* qrow = static_cast<const T*>(t->idx.q_idx) + (int64_t)row * t->idx.hi * DI;
-      for (int h = 0; h < t->idx.hi; ++h) {
-#pragma unroll
-        for (int i = 0; i < Vec<T>::N; ++i)
-          d[h] = fmaf(to_f32(qrow[h * DI + c + i]), x[i], d[h]);
-      }
-    }
-    float s = 0.0f;
-    for (int h = 0; h < t->idx.hi; ++h)
-      s = fmaf(t->idx.w[(int64_t)row * t->idx.hi + h], fmaxf(d[h], 0.0f), s);
-    return score_key(s);
   }
 };
 
 struct SelfId {
   __device__ __forceinline__ int32_t operator()(int e) const { return e; }
 };
+struct KeyArray {  // keys in LDS or global memory
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
+};
+struct IdArray {
+  const int32_t* id;
+  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
+};
 
-__device__ __forceinline__ void write_all(int32_t* sel_row, int32_t* n_sel, int row,
-                                          int n, int top_k) {
+// Key of candidate e of a row from whichever source the row has: caller
+// scores, keys stored in the workspace, or (rare exact fallback of rows
+// whose keys are not stored) recomputed by this lane alone.
+template <typename T, int DI>
+struct RowKeys {
+  const float* given;
+  const uint32_t* stored;
+  const TopkArgs* t;
+  int row, seq;
+  __device__ __forceinline__ uint32_t operator()(int e) const {
+    if (given != nullptr) return score_key(given[e]);
+    if (stored != nullptr) return stored[e];
+    const T* p = static_cast<const T*>(t->idx.kbar) + t->idx.pm.block_slot(seq, e) * DI;
+    const T* qrow = static_cast<const T*>(t->idx.q_idx) + (int64_t)row * t->idx.hi * DI;
+    float s = 0.0f;
+    for (int h = 0; h < t->idx.hi; ++h) {
+      float d = 0.0f;
+      for (int c = 0; c < DI; ++c) d = fmaf(to_f32(qrow[h * DI + c]), to_f32(p[c]), d);
+      s = fmaf(t->idx.w[(int64_t)row * t->idx.hi + h], fmaxf(d, 0.0f), s);
+    }
+    return score_key(s);
+  }
+};
+
+__device__ __forceinline__ void write_all(int32_t* sel_row, int32_t* n_sel, int row, int n,
+                                          int top_k) {
   for (int j = threadIdx.x; j < top_k; j += blockDim.x) sel_row[j] = j < n ? j : -1;
   if (threadIdx.x == 0) n_sel[row] = n;
 }
 
-// Exact selection over every candidate of a row straight from a score
-// source (used for short rows and as the fallback of long rows).
+// Exact selection over every candidate of a row straight from a key source.
 template <class Get>
-__device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row,
-                            int32_t* n_sel, int row, SelShared& sh) {
+__device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row, int32_t* n_sel,
+                            int row, SelShared& sh) {
   uint32_t thr;
   int r;
   radix_kth(get, n, top_k, sh, thr, r);
@@ -228,25 +244,45 @@ __device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row,
   if (threadIdx.x == 0) n_sel[row] = top_k;
 }
 
-struct LdsKeys {
-  const uint32_t* k;
-  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
-};
-struct LdsIds {
-  const int32_t* id;
-  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
-};
+// One workgroup per (row, chunk of kChunk candidates).
+//
+// Rows with at most kDirectCap candidates: the chunks store their keys; the
+// last chunk of the row to finish selects over all of them in LDS.
+//
+// Longer rows: each of the chunk's four waves publishes its jw largest
+// (key, id) pairs.  The last chunk takes tau = the k-th largest key of all
+// published pairs: tau is a key of the row, and at least k keys are >= tau,
+// so tau never exceeds the row's k-th largest key and every selected block
+// has key >= tau.  A wave whose jw-th published key is below tau has all of
+// its keys >= tau among its published pairs; only a wave whose jw-th key
+// reaches tau ("saturated", rare) is rescanned.  The survivors are gathered
+// wave by wave, ascending ids inside each wave, so they come out in
+// ascending id order, and the exact radix select + ordered emission of
+// select.hpp picks the k best with ties to the lower id.
+constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
 
-// Pass A: scores of one chunk of one row; per-wave top-jw keys as the
-// chunk's contribution to a lower bound of the row's k-th score.  The last
-// chunk of a row either selects directly (short rows, all scores stored)
-// or turns the collected keys into the bound tau.
-template <typename T, int DI>
-__global__ void __launch_bounds__(256) topk_pass_a(TopkArgs t) {
+// Exact top-k of n <= kDirectCap keys read from keys[0..n) (global memory
+// or LDS), every key held in registers.
+__device__ void select_direct(const uint32_t* keys, int n, int top_k, int32_t* sel_row,
+                              int32_t* n_sel, int row, SelShared& sh) {
+  uint32_t thr;
+  int r;
+  radix_kth(KeyArray{keys}, n, top_k, sh, thr, r);
+  emit_topk(KeyArray{keys}, SelfId{}, n, thr, r, sel_row, top_k, sh);
+  if (threadIdx.x == 0) n_sel[row] = top_k;
+}
+
+template <typename T, int DI, int HI>
+__global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   __shared__ uint32_t keys[kChunk];
-  __shared__ uint32_t uni[kUnionCap];
+  __shared__ int32_t pages[kChunk];
+  __shared__ uint32_t dkeys[kDirectCap];
+  __shared__ uint32_t skey[kSelCap];
+  __shared__ int32_t sid[kSelCap];
+  __shared__ int32_t sat_w[kMaxSat];
+  __shared__ uint32_t sat_cnt[kMaxSat], sat_off[kMaxSat];
   __shared__ SelShared sh;
-  __shared__ uint32_t flag;
+  __shared__ uint32_t flag, n_sat;
   const int rl = blockIdx.y, row = t.row0 + rl, c = blockIdx.x;
   const RowPlan p(t, row);
   int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
@@ -256,175 +292,186 @@ __global__ void __launch_bounds__(256) topk_pass_a(TopkArgs t) {
   }
   const bool direct = p.n <= kDirectCap;
   const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
-  if (direct && given) {  // all scores are stored already: one workgroup
+  if (direct && given) {  // every score is stored already: one workgroup
     if (c != 0) return;
-    for (int e = threadIdx.x; e < p.n; e += blockDim.x) uni[e] = score_key(given[e]);
+    for (int e = threadIdx.x; e < p.n; e += blockDim.x) dkeys[e] = score_key(given[e]);
     __syncthreads();
-    select_full(LdsKeys{uni}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(dkeys, p.n, t.top_k, sel_row, t.n_sel, row, sh);
     return;
   }
   if (c >= p.W) return;
   const int c0 = c * kChunk;
-  float* ws_row = t.ws_scores ? t.ws_scores + (int64_t)rl * t.ws_ld : nullptr;
-  const bool store = ws_row != nullptr && (direct || t.materialize);
+  uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
+  const bool keep = !given && (direct || t.materialize);
   if (given) {
     for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
       keys[i] = (c0 + i < p.n) ? score_key(given[c0 + i]) : 0u;
     __syncthreads();
   } else {
-    IdxQuery<T, DI> iq;
+    IdxQuery<T, DI, HI> iq;
     iq.load(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI,
-            t.idx.w + (int64_t)row * t.idx.hi, t.idx.hi,
-            threadIdx.x % IdxQuery<T, DI>::G);
-    chunk_scores<T, DI>(t.idx, p.seq, p.n, c0, iq, keys, store ? ws_row + c0 : nullptr);
+            t.idx.w + (int64_t)row * t.idx.hi, t.idx.hi, threadIdx.x % IdxQuery<T, DI, HI>::G);
+    chunk_scores<T, DI, HI>(t.idx, p.seq, p.n, c0, iq, pages, keys);
+    if (keep) {
+      for (int i = threadIdx.x; i < kChunk && c0 + i < p.n; i += blockDim.x)
+        st_agent(ws_row + c0 + i, keys[i]);
+    }
   }
+  uint64_t* tops = t.tops + (int64_t)rl * kUnionCap;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
   if (!direct) {
-    // per-wave top-jw keys of this chunk (key 0 = none left)
-    const int wave = threadIdx.x / kWave, lane = lane_id();
+    // per-wave top-jw (key, id) pairs of this chunk, best first (key 0 =
+    // nothing left)
     uint32_t v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = keys[wave * 256 + lane + 64 * i];
-    uint32_t* dst = t.tops + (int64_t)rl * kUnionCap + (c * kSelWaves + wave) * p.jw;
+    uint64_t* dst = tops + (c * kSelWaves + wave) * p.jw;
     for (int j = 0; j < p.jw; ++j) {
-      uint32_t lm = max(max(v[0], v[1]), max(v[2], v[3]));
-      uint32_t wm = wave_max_u32(lm);
-      uint64_t b = ballot(lm == wm);
+      const uint32_t lm = max(max(v[0], v[1]), max(v[2], v[3]));
+      const uint32_t wm = wave_max_u32(lm);
+      const uint64_t b = ballot(lm == wm);
       if (lane == (int)(__ffsll((unsigned long long)b) - 1)) {
-        bool done = false;
+        int hit = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+          if (v[i] == wm) hit = i;
+        const uint32_t id = (uint32_t)(c0 + wave * 256 + lane + 64 * hit);
+        st_agent(dst + j, ((uint64_t)id << 32) | wm);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!done && v[i] == wm) { v[i] = 0u; done = true; }
+          if (i == hit) v[i] = 0u;
       }
-      if (lane == 0) dst[j] = wm;
     }
   }
-  if (!arrive_last(t.cnt_a + rl, (uint32_t)p.W, &flag)) return;
+  if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
   if (direct) {
-    for (int e = threadIdx.x; e < p.n; e += blockDim.x)
-      uni[e] = score_key(__builtin_nontemporal_load(ws_row + e));
+    for (int e = threadIdx.x; e < p.n; e += blockDim.x) dkeys[e] = ws_row[e];
     __syncthreads();
-    select_full(LdsKeys{uni}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(dkeys, p.n, t.top_k, sel_row, t.n_sel, row, sh);
     return;
   }
-  const int un = p.W * kSelWaves * p.jw;
-  const uint32_t* src = t.tops + (int64_t)rl * kUnionCap;
-  for (int e = threadIdx.x; e < un; e += blockDim.x) uni[e] = __builtin_nontemporal_load(src + e);
+
+  // ---- last chunk of a long row.  This code runs once per row on one CU,
+  // so it is kept compact (rolled loops over LDS data): its instructions
+  // are fetched cold.
+  const RowKeys<T, DI> src{given, keep ? ws_row : nullptr, &t, row, p.seq};
+  const int jw = p.jw, nw = p.W * kSelWaves, un = nw * jw;
+  uint32_t* ukey = dkeys;                                   // [kUnionCap]
+  int32_t* uid = reinterpret_cast<int32_t*>(dkeys + kUnionCap);  // [kUnionCap]
+  for (int e = threadIdx.x; e < un; e += blockDim.x) {
+    const uint64_t v = tops[e];
+    ukey[e] = (uint32_t)v;
+    uid[e] = (int32_t)(v >> 32);
+  }
+  if (threadIdx.x == 0) n_sat = 0u;
   __syncthreads();
-  uint32_t tau = 0u;
-  if (un >= t.top_k) {
+  // tau: the k-th largest published key, low bits past two digits cleared
+  uint32_t tau;
+  {
     int r;
-    radix_kth(LdsKeys{uni}, un, t.top_k, sh, tau, r);
+    radix_kth(KeyArray{ukey}, un, t.top_k, sh, tau, r, 2);
   }
-  if (threadIdx.x == 0) t.tau[rl] = tau;
-}
-
-// Pass B: the survivors (key >= tau) of one chunk, in index order, into the
-// chunk's slots; the last chunk of a row gathers all survivors in order and
-// selects the k best exactly.
-template <typename T, int DI>
-__global__ void __launch_bounds__(256) topk_pass_b(TopkArgs t) {
-  __shared__ uint32_t keys[kChunk];
-  __shared__ uint32_t ckey[kSelCap];
-  __shared__ int32_t cid[kSelCap];
-  __shared__ SelShared sh;
-  __shared__ uint32_t flag;
-  const int rl = blockIdx.y, row = t.row0 + rl, c = blockIdx.x;
-  const RowPlan p(t, row);
-  if (p.n <= kDirectCap || c >= p.W) return;
-  int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
-  const int c0 = c * kChunk;
-  const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
-  const float* stored = given ? given
-                              : (t.materialize ? t.ws_scores + (int64_t)rl * t.ws_ld : nullptr);
-  if (stored) {
-    for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
-      keys[i] = (c0 + i < p.n) ? score_key(stored[c0 + i]) : 0u;
-    __syncthreads();
-  } else {
-    IdxQuery<T, DI> iq;
-    iq.load(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI,
-            t.idx.w + (int64_t)row * t.idx.hi, t.idx.hi,
-            threadIdx.x % IdxQuery<T, DI>::G);
-    chunk_scores<T, DI>(t.idx, p.seq, p.n, c0, iq, keys, nullptr);
+  // runs (waves) owned by this thread: [w0, w1)
+  const int q = (nw + kSelThreads - 1) / kSelThreads;
+  const int w0 = min(nw, (int)threadIdx.x * q), w1 = min(nw, w0 + q);
+  // a run whose last published key still reaches tau is saturated
+#pragma unroll 1
+  for (int gw = w0; gw < w1; ++gw) {
+    const uint32_t last = ukey[gw * jw + jw - 1];
+    if (last >= tau && last != 0u) {
+      const uint32_t sidx = atomicAdd(&n_sat, 1u);
+      if (sidx < (uint32_t)kMaxSat) sat_w[sidx] = gw;
+    }
   }
-  const uint32_t tau = t.tau[rl];
-  // keys 0 are padding past n; a real key is always > 0
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t k = keys[wave * 256 + i * 64 + lane];
-    cnt += __popcll(ballot(k != 0u && k >= tau));
-  }
-  if (lane == 0) sh.wcnt[0][wave] = cnt;
   __syncthreads();
-  uint32_t base = 0, total = 0;
-  for (int w = 0; w < kSelWaves; ++w) {
-    base += (w < wave) ? sh.wcnt[0][w] : 0u;
-    total += sh.wcnt[0][w];
+  const int ns = (int)n_sat;
+  bool fits = ns <= kMaxSat;
+  // survivor counts of saturated runs (whole workgroup, one run at a time)
+#pragma unroll 1
+  for (int i = 0; fits && i < ns; ++i) {
+    const int e = sat_w[i] * 256 + (int)threadIdx.x;
+    const bool hit = e < p.n && src(e) >= tau;
+    const uint32_t cw = (uint32_t)__popcll(ballot(hit));
+    if (lane == 0) sh.wcnt[1][wave] = cw;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
+    __syncthreads();
   }
-  uint2* slot = t.slots + (int64_t)rl * kSlotCap + (int64_t)c * p.sc;
-  if (total <= (uint32_t)p.sc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int li = wave * 256 + i * 64 + lane;
-      uint32_t k = keys[li];
-      bool take = k != 0u && k >= tau;
-      uint64_t m = ballot(take);
-      if (take) slot[base + lanes_below(m)] = make_uint2(k, (uint32_t)(c0 + li));
-      base += __popcll(m);
-    }
-  } else if (threadIdx.x == 0) {
-    atomicOr(t.flags + rl, 1u);
-  }
-  if (threadIdx.x == 0) t.chunk_cnt[(int64_t)rl * t.w_max + c] = total;
-  if (!arrive_last(t.cnt_b + rl, (uint32_t)p.W, &flag)) return;
-
-  // ---- last chunk of the row: gather survivors in index order
-  bool overflow = __builtin_nontemporal_load(t.flags + rl) != 0u;
-  uint32_t m_total = 0;
-  if (!overflow) {
-    // thread th owns chunks [th*q, th*q+q)
-    const int q = (p.W + kSelThreads - 1) / kSelThreads;
-    uint32_t mine = 0;
-    const uint32_t* cc = t.chunk_cnt + (int64_t)rl * t.w_max;
-    for (int j = 0; j < q; ++j) {
-      int ch = threadIdx.x * q + j;
-      if (ch < p.W) mine += __builtin_nontemporal_load(cc + ch);
-    }
-    uint32_t off = block_excl_scan(mine, sh, m_total);
-    if (m_total <= (uint32_t)kSelCap) {
-      for (int j = 0; j < q; ++j) {
-        int ch = threadIdx.x * q + j;
-        if (ch >= p.W) break;
-        uint32_t nc = __builtin_nontemporal_load(cc + ch);
-        const uint2* sl = t.slots + (int64_t)rl * kSlotCap + (int64_t)ch * p.sc;
-        for (uint32_t i = 0; i < nc; ++i) {
-          const uint2 v = sl[i];
-          ckey[off + i] = v.x;
-          cid[off + i] = (int32_t)v.y;
-        }
-        off += nc;
-      }
+  // survivors of an unsaturated run are its leading entries with key >= tau
+  uint32_t mine = 0;
+#pragma unroll 1
+  for (int gw = w0; gw < w1; ++gw) {
+    const uint32_t* rk = ukey + gw * jw;
+    if (rk[jw - 1] >= tau && rk[jw - 1] != 0u) {
+#pragma unroll 1
+      for (int i = 0; i < ns; ++i)
+        if (sat_w[i] == gw) mine += sat_cnt[i];
     } else {
-      overflow = true;
+      int c2 = 0;
+      while (c2 < jw && rk[c2] >= tau && rk[c2] != 0u) ++c2;
+      mine += (uint32_t)c2;
+    }
+  }
+  uint32_t m_total;
+  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
+  fits = fits && m_total <= (uint32_t)kSelCap;
+  if (fits) {
+#pragma unroll 1
+    for (int gw = w0; gw < w1; ++gw) {
+      const uint32_t* rk = ukey + gw * jw;
+      const int32_t* ri = uid + gw * jw;
+      if (rk[jw - 1] >= tau && rk[jw - 1] != 0u) {
+#pragma unroll 1
+        for (int i = 0; i < ns; ++i)
+          if (sat_w[i] == gw) {
+            sat_off[i] = off;
+            off += sat_cnt[i];
+          }
+        continue;
+      }
+      int c2 = 0;
+      while (c2 < jw && rk[c2] >= tau && rk[c2] != 0u) ++c2;
+      // the run lists its survivors best first: place them by ascending id
+#pragma unroll 1
+      for (int i = 0; i < c2; ++i) {
+        uint32_t rank = 0;
+#pragma unroll 1
+        for (int j = 0; j < c2; ++j) rank += ri[j] < ri[i] ? 1u : 0u;
+        skey[off + rank] = rk[i];
+        sid[off + rank] = ri[i];
+      }
+      off += (uint32_t)c2;
+    }
+  }
+  __syncthreads();
+  // survivors of saturated runs, in id order (whole workgroup per run)
+#pragma unroll 1
+  for (int i = 0; fits && i < ns; ++i) {
+    const int e = sat_w[i] * 256 + (int)threadIdx.x;
+    const uint32_t k = e < p.n ? src(e) : 0u;
+    const bool hit = e < p.n && k >= tau;
+    const uint64_t m = ballot(hit);
+    if (lane == 0) sh.wcnt[1][wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t base = sat_off[i];
+    for (int w2 = 0; w2 < wave; ++w2) base += sh.wcnt[1][w2];
+    if (hit) {
+      skey[base + lanes_below(m)] = k;
+      sid[base + lanes_below(m)] = e;
     }
     __syncthreads();
   }
-  if (!overflow) {
+  if (fits) {
     uint32_t thr;
     int r;
-    radix_kth(LdsKeys{ckey}, (int)m_total, t.top_k, sh, thr, r);
-    emit_topk(LdsKeys{ckey}, LdsIds{cid}, (int)m_total, thr, r, sel_row, t.top_k, sh);
+    radix_kth(KeyArray{skey}, (int)m_total, t.top_k, sh, thr, r);
+    emit_topk(KeyArray{skey}, IdArray{sid}, (int)m_total, thr, r, sel_row, t.top_k, sh);
     if (threadIdx.x == 0) t.n_sel[row] = t.top_k;
   } else {
-    // rare: more survivors than the slots hold (heavy ties); exact select
-    // over every candidate, recomputing scores if none are stored
-    IdxQuery<T, DI> dummy;
-    ScoreKey<T, DI> get{&t, rl, row, p.seq, &dummy, stored};
-    select_full(get, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    // rare: too many survivors (heavy ties): exact select over every key
+    select_full(src, p.n, t.top_k, sel_row, t.n_sel, row, sh);
   }
-  if (threadIdx.x == 0) t.flags[rl] = 0u;
 }
 
 // ================================================================ launch
@@ -432,51 +479,74 @@ __global__ void __launch_bounds__(256) topk_pass_b(TopkArgs t) {
 template <typename T, int DI>
 static void launch_pool(const PoolArgs& a, int n_seqs, hipStream_t st) {
   constexpr int G = DI / Vec<T>::N;
-  int64_t threads = (int64_t)a.max_new * G;
+  const int64_t threads = (int64_t)a.max_new * G;
   dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_seqs);
   hipLaunchKernelGGL((pool_kernel<T, DI>), grid, dim3(256), 0, st, a);
 }
 
-template <typename T, int DI>
-static void launch_scores(const IdxArgs& a, int n_rows, int max_n, float* scores,
-                          int64_t ld, hipStream_t st) {
+template <typename T, int DI, int HI>
+static void launch_scores(const IdxArgs& a, int n_rows, int max_n, float* scores, int64_t ld,
+                          hipStream_t st) {
   dim3 grid((unsigned)((max_n + kChunk - 1) / kChunk), (unsigned)n_rows);
-  hipLaunchKernelGGL((scores_kernel<T, DI>), grid, dim3(256), 0, st, a, scores, ld);
+  hipLaunchKernelGGL((scores_kernel<T, DI, HI>), grid, dim3(256), 0, st, a, scores, ld);
 }
 
-template <typename T, int DI>
+template <typename T, int DI, int HI>
 static void launch_topk(const TopkArgs& t, int rows, hipStream_t st) {
   dim3 grid((unsigned)t.w_max, (unsigned)rows);
-  hipLaunchKernelGGL((topk_pass_a<T, DI>), grid, dim3(256), 0, st, t);
-  hipLaunchKernelGGL((topk_pass_b<T, DI>), grid, dim3(256), 0, st, t);
+  hipLaunchKernelGGL((topk_kernel<T, DI, HI>), grid, dim3(256), 0, st, t);
 }
 
-#define QSA_DISPATCH_DI(T, DI, CALL)                  \
-  switch (DI) {                                       \
-    case 16: { constexpr int kDi = 16; CALL; } break; \
-    case 32: { constexpr int kDi = 32; CALL; } break; \
-    case 64: { constexpr int kDi = 64; CALL; } break; \
-    case 128: { constexpr int kDi = 128; CALL; } break; \
-    default: break;                                   \
-  }
+// compile-time indexer head count: the real count rounded up to 2, 4 or 8
+// (padding heads carry zero weight and zero query)
+template <typename T, int DI, class F>
+static void with_hi(int hi, F&& f) {
+  if (hi <= 2) f(std::integral_constant<int, 2>{});
+  else if (hi <= 4) f(std::integral_constant<int, 4>{});
+  else f(std::integral_constant<int, 8>{});
+}
+
+template <class F>
+static void with_types(int dtype, int di, F&& f) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    switch (di) {
+      case 16: f(T{}, std::integral_constant<int, 16>{}); break;
+      case 32: f(T{}, std::integral_constant<int, 32>{}); break;
+      case 64: f(T{}, std::integral_constant<int, 64>{}); break;
+      case 128: f(T{}, std::integral_constant<int, 128>{}); break;
+      default: break;
+    }
+  };
+  if (dtype == QSA_F32) go(float{});
+  else go(bf16_t{});
+}
 
 void run_pool(const PoolArgs& a, int dtype, int di, int n_seqs, hipStream_t st) {
-  if (dtype == QSA_F32) { QSA_DISPATCH_DI(float, di, (launch_pool<float, kDi>(a, n_seqs, st))); }
-  else { QSA_DISPATCH_DI(bf16_t, di, (launch_pool<bf16_t, kDi>(a, n_seqs, st))); }
+  with_types(dtype, di, [&](auto tag, auto dic) {
+    launch_pool<decltype(tag), decltype(dic)::value>(a, n_seqs, st);
+  });
 }
 
 void run_scores(const IdxArgs& a, int dtype, int di, int n_rows, int max_n, float* scores,
                 int64_t ld, hipStream_t st) {
-  if (dtype == QSA_F32) {
-    QSA_DISPATCH_DI(float, di, (launch_scores<float, kDi>(a, n_rows, max_n, scores, ld, st)));
-  } else {
-    QSA_DISPATCH_DI(bf16_t, di, (launch_scores<bf16_t, kDi>(a, n_rows, max_n, scores, ld, st)));
-  }
+  with_types(dtype, di, [&](auto tag, auto dic) {
+    using T = decltype(tag);
+    constexpr int DI = decltype(dic)::value;
+    with_hi<T, DI>(a.hi, [&](auto hic) {
+      launch_scores<T, DI, decltype(hic)::value>(a, n_rows, max_n, scores, ld, st);
+    });
+  });
 }
 
 void run_topk(const TopkArgs& t, int dtype, int di, int rows, hipStream_t st) {
-  if (dtype == QSA_F32) { QSA_DISPATCH_DI(float, di, (launch_topk<float, kDi>(t, rows, st))); }
-  else { QSA_DISPATCH_DI(bf16_t, di, (launch_topk<bf16_t, kDi>(t, rows, st))); }
+  with_types(dtype, di, [&](auto tag, auto dic) {
+    using T = decltype(tag);
+    constexpr int DI = decltype(dic)::value;
+    with_hi<T, DI>(t.idx.hi, [&](auto hic) {
+      launch_topk<T, DI, decltype(hic)::value>(t, rows, st);
+    });
+  });
 }
 
 }  // namespace qsa

@@ -1,25 +1,33 @@
 // Argument blocks and host entry points of the indexer kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace qsa {
 
 constexpr int kChunk = 1024;        // candidate blocks per workgroup (4 per thread)
 constexpr int kDirectCap = 8192;    // rows with <= this many candidates select in one pass
-constexpr int kUnionCap = 8192;     // keys of the per-chunk tops of one row
-constexpr int kSelCap = 8192;       // survivors gathered into LDS for the final select
-constexpr int kSlotCap = 16384;     // survivor slots per row, split evenly over its chunks
+constexpr int kUnionCap = 4096;     // (key, id) pairs of the per-wave tops of one row
+constexpr int kSelCap = 2048;       // survivors gathered into LDS for the final select
 constexpr int kMaxIdxHeads = 8;
+constexpr int kMaxJw = 16;
 
-// per-wave top count of the chunk tops: the union over a row's chunks holds
-// about 2k keys, and never more than kUnionCap
+// Per-wave top count: each wave of each chunk publishes its jw best
+// (key, id) pairs: the largest power of two that fits kUnionCap, at most
+// kMaxJw.  Rows that take
+// this path have at least 9 chunks (more than kDirectCap candidates); the
+// union then holds at least 4 * W * jw >= 1024 > QSA_MAX_TOPK pairs.  A larger
+// jw makes a wave whose jw-th key still reaches the bound (a "saturated"
+// wave, rescanned in full) rarer.
 __host__ __device__ inline int row_jw(int n, int top_k) {
+  (void)top_k;
   int W = (n + kChunk - 1) / kChunk;
   if (W <= 0) return 1;
-  int jw = (2 * top_k + 4 * W - 1) / (4 * W);
-  jw = jw < 1 ? 1 : (jw > 16 ? 16 : jw);
-  while (jw > 1 && 4 * W * jw > kUnionCap) --jw;
+  int cap = kUnionCap / (4 * W);
+  int jw = 1;
+  while (jw * 2 <= cap && jw * 2 <= kMaxJw) jw *= 2;  // a power of two
   return jw;
 }
 
@@ -65,13 +73,8 @@ struct TopkArgs {
   int materialize;       // long rows keep their scores in ws_scores
   float* ws_scores;      // [R][ws_ld]
   int64_t ws_ld;
-  uint32_t* cnt_a;       // [R]
-  uint32_t* cnt_b;       // [R]
-  uint32_t* flags;       // [R]
-  uint32_t* tau;         // [R]
-  uint32_t* chunk_cnt;   // [R][w_max]
-  uint32_t* tops;        // [R][kUnionCap]
-  uint2* slots;          // [R][kSlotCap]
+  uint32_t* cnt;         // [R] arrival counters
+  uint64_t* tops;        // [R][kUnionCap] (block id << 32 | key)
 };
 
 void run_pool(const PoolArgs& a, int dtype, int di, int n_seqs, hipStream_t st);

@@ -36,54 +36,109 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh,
   return base + incl - v;
 }
 
+// ---------------------------------------------------------------- register-resident selection
+
+// Inclusive prefix sum over the wave with DPP: row shifts inside each
+// 16-lane row, then row broadcasts carry the row totals upward.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
+}
+
+// Inclusive prefix sum of one value per thread over the workgroup (one
+// barrier pair).  total receives the workgroup sum.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, SelShared& sh, uint32_t& total) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const uint32_t incl = wave_incl_scan_dpp(v);
+  if (lane == kWave - 1) sh.wcnt[0][wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t c = sh.wcnt[0][w];
+    base += (w < wave) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, SelShared& sh) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  v = wave_max_u32(v);
+  if (lane == 0) sh.wcnt[1][wave] = v;
+  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) m = max(m, sh.wcnt[1][w]);
+  __syncthreads();
+  return m;
+}
+
 // Finds T, the k-th largest key among get(0..n-1) (1 <= k <= n), and r, the
 // number of elements equal to T that belong to the k largest (ties are
-// later resolved by index order).  Four passes of 8-bit digits, most
-// significant first; each pass histograms the elements still matching the
-// digits fixed so far.
+// later resolved by index order).  The digits are 8 bits wide, starting
+// below the bits common to all keys; each pass histograms (LDS atomics)
+// the elements still matching the digits fixed so far.  With max_passes
+// too small to reach bit 0, T is the k-th largest key with its unresolved
+// low bits cleared, a lower bound of it.
 template <class Get>
 __device__ void radix_kth(const Get& get, int n, int k, SelShared& sh,
-                          uint32_t& T, int& r) {
+                          uint32_t& T, int& r, int max_passes = 4) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  // bits above the highest bit where the largest and smallest keys differ
+  // are common to all keys: the digits start below them
+  uint32_t mx = 0u, nmn = 0u;
+#pragma unroll 4
+  for (int e = tid; e < n; e += kSelThreads) {
+    const uint32_t key = get(e);
+    mx = max(mx, key);
+    nmn = max(nmn, ~key);
+  }
+  mx = block_max_u32(mx, sh);
+  const uint32_t mn = ~block_max_u32(nmn, sh);
+  if (mx == mn) {
+    T = mx;
+    r = k;
+    return;
+  }
+  int hi = 31 - __clz(mx ^ mn);
+  uint32_t prefix = (hi == 31) ? 0u : (mx & ~((2u << hi) - 1u));
+  uint32_t mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
   uint32_t kk = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int pass = 0; pass < max_passes; ++pass) {
+    const int shift = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (1u << (hi - shift + 1)) - 1u;
     sh.hist[tid] = 0u;
     __syncthreads();
+#pragma unroll 4
     for (int e = tid; e < n; e += kSelThreads) {
-      uint32_t key = get(e);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      const uint32_t key = get(e);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < kWave) {
-      const int l = tid;
-      uint32_t h[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = sh.hist[4 * l + j];
-      uint32_t s = h[0] + h[1] + h[2] + h[3];
-      // suffix sums from the top digit down: lanes above l
-      uint32_t incl = s;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        uint32_t o = (uint32_t)__shfl_down((int)incl, off);
-        if (l + off < kWave) incl += o;
-      }
-      uint32_t above = incl - s;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < kk && kk <= above + h[j]) {
-          sh.bc[0] = (uint32_t)(4 * l + j);
-          sh.bc[1] = kk - above;
-        }
-        above += h[j];
-      }
+    // thread t looks at digit 255 - t: counts from the top down
+    const uint32_t d = 255u - (uint32_t)tid;
+    const uint32_t h = sh.hist[d];
+    uint32_t tot;
+    const uint32_t incl = block_incl_scan(h, sh, tot);
+    if (incl - h < kk && kk <= incl) {
+      sh.bc[0] = d;
+      sh.bc[1] = kk - (incl - h);
     }
     __syncthreads();
-    uint32_t d = sh.bc[0];
+    prefix |= sh.bc[0] << shift;
+    mask |= dmask << shift;
     kk = sh.bc[1];
-    prefix |= d << shift;
-    mask |= 0xffu << shift;
     __syncthreads();
+    if (shift == 0) break;
+    hi = shift - 1;
   }
   T = prefix;
   r = (int)kk;
@@ -134,6 +189,108 @@ __device__ void emit_topk(const Get& get, const Id& id, int n, uint32_t T,
     if (take && at < (uint32_t)out_cap) out[at] = id(e);
     tie_base += __popcll(eqm);
     sel_base += __popcll(tm);
+  }
+}
+
+// k-th largest key (1 <= k <= n) of the keys held in registers: thread t
+// holds key[i] for element t * EPT + i, valid when that index is below n.
+// The bits above the highest bit in which the largest and smallest keys
+// differ are common to all keys; the radix digits start below them, 8 bits
+// per pass, for at most max_passes passes.  On return T is the k-th largest
+// key with any unresolved low bits cleared (a lower bound of it) and r the
+// number of keys equal to T among the k largest (meaningful only when
+// resolved is set).
+template <int EPT>
+__device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShared& sh,
+                               uint32_t& T, int& r, bool& resolved, int max_passes = 4) {
+  const int base_e = threadIdx.x * EPT;
+  uint32_t mx = 0u, nmn = 0u;  // max and (~min)
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (base_e + i < n) {
+      mx = max(mx, key[i]);
+      nmn = max(nmn, ~key[i]);
+    }
+  }
+  mx = block_max_u32(mx, sh);
+  const uint32_t mn = ~block_max_u32(nmn, sh);
+  if (mx == mn) {
+    T = mx;
+    r = k;
+    resolved = true;
+    return;
+  }
+  int hi = 31 - __clz(mx ^ mn);  // highest differing bit
+  uint32_t prefix = (hi == 31) ? 0u : (mx & ~((2u << hi) - 1u));
+  uint32_t mask = (hi == 31) ? 0u : ~((2u << hi) - 1u);
+  uint32_t kk = (uint32_t)k;
+  resolved = false;
+  for (int pass = 0; pass < max_passes; ++pass) {
+    const int shift = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (1u << (hi - shift + 1)) - 1u;
+    sh.hist[threadIdx.x] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (base_e + i < n && (key[i] & mask) == prefix)
+        atomicAdd(&sh.hist[(key[i] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread t looks at digit 255 - t: counts from the top down
+    const uint32_t d = 255u - threadIdx.x;
+    const uint32_t h = sh.hist[d];
+    uint32_t tot;
+    const uint32_t incl = block_incl_scan(h, sh, tot);
+    if (incl - h < kk && kk <= incl) {
+      sh.bc[0] = d;
+      sh.bc[1] = kk - (incl - h);
+    }
+    __syncthreads();
+    prefix |= sh.bc[0] << shift;
+    mask |= dmask << shift;
+    kk = sh.bc[1];
+    __syncthreads();
+    if (shift == 0) {
+      resolved = true;
+      break;
+    }
+    hi = shift - 1;
+  }
+  T = prefix;
+  r = (int)kk;
+}
+
+// Ordered emission for register-held keys and ids (thread t holds elements
+// t * EPT + i, in increasing index order): element e is selected when its
+// key > T, or key == T and fewer than r earlier elements equal T; the
+// selected ids are written to out[0..) in index order (writes past out_cap
+// are dropped).
+template <int EPT>
+__device__ void emit_regs(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int n,
+                          uint32_t T, int r, int32_t* out, int out_cap, SelShared& sh) {
+  const int base_e = threadIdx.x * EPT;
+  uint32_t ties = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) ties += (base_e + i < n && key[i] == T) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t tie_before = block_incl_scan(ties, sh, tot) - ties;
+  uint32_t take_n = 0;
+  bool take[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const bool valid = base_e + i < n;
+    const bool eq = valid && key[i] == T;
+    take[i] = valid && (key[i] > T || (eq && tie_before < (uint32_t)r));
+    tie_before += eq ? 1u : 0u;
+    take_n += take[i] ? 1u : 0u;
+  }
+  uint32_t at = block_incl_scan(take_n, sh, tot) - take_n;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (take[i]) {
+      if (at < (uint32_t)out_cap) out[at] = id[i];
+      ++at;
+    }
   }
 }
 

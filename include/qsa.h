@@ -65,7 +65,7 @@ extern "C" {
 
 #define QSA_BLOCK 4        /* tokens per micro-block */
 #define QSA_MAX_TOPK 512   /* largest supported top_k (the pages' budget) */
-#define QSA_MAX_BLOCKS (1 << 21) /* candidate blocks per query (8M tokens) */
+#define QSA_MAX_BLOCKS (1 << 20) /* candidate blocks per query (4M tokens) */
 
 typedef enum qsa_status {
   QSA_OK = 0,
