@@ -152,6 +152,66 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev):
     return wall, kern, work, kernels, files, dense_ms, ctx
 
 
+# ------------------------------------------------------------------ prefill
+
+def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense_too: bool = True):
+    """One step = the whole prefill of wl: every chunk of query rows in
+    order (pool the chunk's new blocks -> fused scores + top-k -> per-row
+    sparse attention).  The existing context (if any) is pooled at set-up."""
+    from block_sparse_attention_32_amd import pipeline as P
+    log(f"[bench] drawing {wl.name} cache on {dev}")
+    cache = W.make_cache(wl, device=dev)
+    cv = B.CacheView.from_cache(cache)
+    n_chunks = max(1, -(-wl.n_new // (wl.chunk or wl.n_new)))
+    chunks = []
+    for ci in range(n_chunks):
+        seq_id, pos = W.prefill_rows(wl, ci)
+        qs = W.make_queries(wl, cache, seq_id, pos, device=dev, seed=wl.seed + 7919 + ci)
+        rows = B.QueriesView(qs.seq_id, qs.pos, max(pos))
+        st = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "prefill")
+        b0 = pos[0] // 4
+        begin = torch.full((1,), b0, dtype=torch.int32, device=dev)
+        chunks.append((st, begin, (pos[-1] + 1) // 4 - b0, pos))
+    if wl.n_ctx:
+        P.pool_all(cv, 1, wl.n_ctx // 4, dev)               # set-up, untimed
+
+    def one(timer=None):
+        call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
+        for st, begin, nb, _ in chunks:
+            call("pool", B.qsa_pool_blocks, cv, begin, nb)
+            call("topk", st.select)
+            call("attn", st.attend)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer = Timer()
+    one(timer)
+    torch.cuda.synchronize()
+    kern = {k: v * len(chunks) for k, v in timer.avg_us().items()}   # per step
+    rows_total = sum(len(c[3]) for c in chunks)
+    n_tok = 0
+    cand = 0
+    for st, _, _, pos in chunks:
+        ns = st.n_sel.cpu().numpy().astype(np.int64)
+        p_ = np.asarray(pos, dtype=np.int64)
+        n_tok += int((4 * ns + p_ % 4 + 1).sum())
+        cand += int((p_ // 4).sum())
+    esz = 2 if wl.dtype == "bf16" else 4
+    work = {
+        "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "flops": 4 * wl.hq * wl.d * n_tok,
+                 "bound": "hbm"},
+        "topk": {"flops": 2 * wl.hi * wl.di * cand, "bound": "alu"},
+        "pool": {"bytes": (wl.n_new // 4) * 5 * wl.di * esz, "bound": "hbm"},
+    }
+    return wall, kern, work, rows_total, chunks, cache
+
+
 # ------------------------------------------------------------------ CPU oracle
 
 def cpu_baseline_decode(wl, ctx, budget_s=12.0):
@@ -218,7 +278,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if wl.mode != "decode":
-        raise SystemExit("prefill benchmarking is not wired yet")
+        wall, kern, work, rows_total, chunks, cache = run_prefill(wl, args.steps, args.warmup, dev)
+        ms = 1e3 * wall / args.steps
+        out = {
+            "metric": METRIC, "value": round(rows_total / (wall / args.steps), 1),
+            "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+            "config": {"workload": wl.name, "context": wl.n_ctx, "new_tokens": wl.n_new,
+                       "chunk": wl.chunk or wl.n_new, "hq": wl.hq, "hkv": wl.hkv,
+                       "head_dim": wl.d, "idx_heads": wl.hi, "idx_dim": wl.di,
+                       "top_k": wl.top_k, "page_size": wl.page_size,
+                       "parallelism": "single-gpu"},
+            "kernels_us": {k: round(v, 1) for k, v in kern.items()},
+            "work": work,
+        }
+        print(json.dumps(out), flush=True)
+        return
     wall, kern, work, kernels, files, dense_ms, ctx = run_decode(wl, args.steps, args.warmup, dev)
     ms = 1e3 * wall / args.steps
     value = ctx["rows"] / (wall / args.steps)

@@ -74,6 +74,30 @@ struct TopkPlan {
   size_t off_ctr, off_tops, off_scores, total;
 };
 
+// MFMA prefill indexer plan (fused mode, many rows)
+struct PidxPlan {
+  int rows, splits;
+  size_t off_uni, off_tau, off_tstride, off_rstride, off_surv, off_scnt, total;
+};
+
+PidxPlan pidx_plan(const qsa_queries* qm) {
+  PidxPlan p;
+  p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
+  if (p.rows < 1) p.rows = 1;
+  const int tiles = (p.rows + kPQT - 1) / kPQT;
+  int sp = 256 / tiles;
+  p.splits = sp < 1 ? 1 : (sp > kPMaxSplits ? kPMaxSplits : sp);
+  size_t o = 0;
+  p.off_uni = o;     o = align256(o + (size_t)p.rows * kPUnion * 4);
+  p.off_tau = o;     o = align256(o + (size_t)p.rows * 4);
+  p.off_tstride = o; o = align256(o + (size_t)(tiles + 1) * 4);
+  p.off_rstride = o; o = align256(o + (size_t)p.rows * 4);
+  p.off_surv = o;    o = align256(o + (size_t)p.rows * kPSurvCap * 8);
+  p.off_scnt = o;    o = align256(o + (size_t)p.rows * p.splits * 4);
+  p.total = o;
+  return p;
+}
+
 TopkPlan topk_plan(const qsa_queries* qm) {
   TopkPlan p;
   const int max_n = qm->max_pos / QSA_BLOCK;
@@ -257,9 +281,43 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   }
   if (qm->n_rows > 0 && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
   const TopkPlan p = topk_plan(qm);
-  if (ws == nullptr || ws_bytes < p.total) return QSA_ERR_WORKSPACE;
+  const PidxPlan pp = pidx_plan(qm);
+  const bool mfma = scores == nullptr && qm->n_rows >= kPMinRows &&
+                    pidx_supported(c->dtype, c->idx_dim, n_idx_heads);
+  if (ws == nullptr || ws_bytes < (mfma ? pp.total : p.total)) return QSA_ERR_WORKSPACE;
   if (qm->n_rows == 0) return QSA_OK;
   char* base = static_cast<char*>(ws);
+  if (mfma) {
+    PIdxArgs a;
+    memset(&a, 0, sizeof(a));
+    a.idx.pm = page_map(c);
+    a.idx.kbar = c->kbar;
+    a.idx.q_idx = q_idx;
+    a.idx.w = w;
+    a.idx.hi = n_idx_heads;
+    a.idx.seq_id = qm->seq_id;
+    a.idx.pos = qm->pos;
+    a.idx.n_seqs = c->n_seqs;
+    a.idx.max_pos = qm->max_pos;
+    a.top_k = top_k;
+    a.splits = pp.splits;
+    a.uni = reinterpret_cast<uint32_t*>(base + pp.off_uni);
+    a.tau = reinterpret_cast<uint32_t*>(base + pp.off_tau);
+    a.tile_stride = reinterpret_cast<int32_t*>(base + pp.off_tstride);
+    a.row_stride = reinterpret_cast<int32_t*>(base + pp.off_rstride);
+    a.surv = reinterpret_cast<uint64_t*>(base + pp.off_surv);
+    a.surv_cnt = reinterpret_cast<uint32_t*>(base + pp.off_scnt);
+    a.sel = sel;
+    a.n_sel = n_sel;
+    for (int r0 = 0; r0 < qm->n_rows; r0 += pp.rows) {
+      a.row0 = r0;
+      a.rows = (qm->n_rows - r0) < pp.rows ? (qm->n_rows - r0) : pp.rows;
+      a.idx.seq_id = qm->seq_id;
+      run_pidx(a, c->idx_dim, as_stream(stream));
+      if ((st = launched()) != QSA_OK) return st;
+    }
+    return QSA_OK;
+  }
   TopkArgs t;
   memset(&t, 0, sizeof(t));
   t.idx.pm = page_map(c);
@@ -326,8 +384,10 @@ size_t qsa_workspace_size(int32_t op, const qsa_cache* c, const qsa_queries* qm,
   if (c == nullptr || qm == nullptr) return 0;
   if (check_cache(c) != QSA_OK || check_queries(c, qm) != QSA_OK) return 0;
   switch (op) {
-    case QSA_OP_TOPK:
-      return topk_plan(qm).total;
+    case QSA_OP_TOPK: {
+      const size_t a = topk_plan(qm).total, b = pidx_plan(qm).total;
+      return a > b ? a : b;
+    }
     case QSA_OP_ATTN_DECODE:
     case QSA_OP_ATTN_PREFILL:
     case QSA_OP_DENSE_DECODE:

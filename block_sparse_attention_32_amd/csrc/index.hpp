@@ -77,6 +77,32 @@ struct TopkArgs {
   uint64_t* tops;        // [R][kUnionCap] (block id << 32 | key)
 };
 
+// ---- MFMA prefill indexer (index_mfma.hip)
+constexpr int kPQT = 128;         // query rows per workgroup tile (4 waves x 32)
+constexpr int kPGrp = 256;        // pooled keys staged per group
+constexpr int kPUnion = 4096;     // union entries (group maxima) per row
+constexpr int kPSurvCap = 8192;   // survivor slots per row, over all splits
+constexpr int kPMaxStride = 8;    // largest group sampling stride of P1
+constexpr int kPMaxSplits = 8;    // block splits per tile
+constexpr int kPMinRows = 64;     // fused top-k of at least this many rows uses it
+
+struct PIdxArgs {
+  IdxArgs idx;
+  int row0, rows, top_k;
+  int splits;                // block splits per query tile
+  uint32_t* uni;             // [rows][kPUnion] group maxima (P1)
+  uint32_t* tau;             // [rows] lower bound of the k-th key (P2)
+  int32_t* tile_stride;      // [tiles] sampling stride of P1
+  int32_t* row_stride;       // [rows] stride used for each row's union
+  uint64_t* surv;            // [rows][splits][kPSurvCap / splits] (block << 32 | key)
+  uint32_t* surv_cnt;        // [rows][splits]
+  int32_t* sel;
+  int32_t* n_sel;
+};
+
+bool pidx_supported(int dtype, int di, int hi);
+void run_pidx(const PIdxArgs& a, int di, hipStream_t st);
+
 void run_pool(const PoolArgs& a, int dtype, int di, int n_seqs, hipStream_t st);
 void run_scores(const IdxArgs& a, int dtype, int di, int n_rows, int max_n, float* scores,
                 int64_t ld, hipStream_t st);

@@ -1,0 +1,400 @@
+// Prefill-side indexer and exact top-k on gfx950 matrix cores (bfloat16
+// pooled keys, Di 64 or 128, up to 4 indexer heads).
+//
+// What is computed is exactly what index.hip computes -- the pooled-key
+// scores s[b] = sum_h w[h] * max(0, q_idx[h] . kbar[b]) of every candidate
+// block of every query row, and per row the top_k blocks (ties to the lower
+// id, ascending ids) -- following keieiax.jp glossary "Qwen Sparse
+// Attention", section 4トークンずつまとめて (a lightweight learned indexer
+// rates each 4-token block; at most 512 blocks are kept per query).
+//
+// Many query rows share one sequence's pooled keys, so scoring is a dense
+// contraction [rows x heads] x [Di x blocks]:
+//   v_mfma_f32_16x16x32_bf16 with A = q_idx rows ordered (query, head) --
+//   4 queries x 4 heads = 16 rows -- and B = 16 pooled-key rows.  Lane l of
+//   the 16x16 result holds the four head dot products of query l/16 with
+//   block l%16, so the ReLU and the weighted head sum are in-lane.
+// A workgroup (4 waves x 32 queries) stages 256 pooled keys (one "group")
+// at a time in LDS and runs them against its 128 queries.
+//
+// Exact top-k in four launches per batch of rows:
+//   P1  sampled groups only (every s-th): for each (query, lane) the largest
+//       key of the group -> the row's "union" of group maxima;
+//   P2  per row: tau = k-th largest union key.  Every union key is a key of
+//       the row and at least k keys are >= tau, so tau is at most the row's
+//       k-th largest key (a lower bound; keys 0 pad missing entries);
+//   P3  all groups: keys >= tau (the survivors) appended per (row, split) in
+//       block order;
+//   P4  per row: survivors gathered in block order -> exact radix select and
+//       ordered emission (select.hpp); a row whose survivors overflowed its
+//       slots falls back to an exact select over recomputed keys.
+#include "index.hpp"
+#include "select.hpp"
+
+namespace qsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int DI>
+struct PGeom {
+  static constexpr int KS = DI / 32;              // MFMA k steps
+  static constexpr int ROWB = DI * 2;             // bytes per pooled key
+  static constexpr int PITCH = ROWB + 16;         // LDS row pitch (bank spread)
+  static constexpr int VPR = ROWB / 16;           // 16-byte vectors per row
+};
+
+struct TileMeta {
+  int32_t seq[kPQT];
+  int32_t n[kPQT];
+  uint32_t tau[kPQT];
+  uint8_t active[kPQT];
+  uint8_t done[kPQT];
+  int cur_seq, n_hi, n_lo;
+};
+
+// Rows of the tile: sequence and candidate count (0 for rows past the
+// batch).  Returns false if the tile has no rows.
+__device__ __forceinline__ void load_tile_meta(const PIdxArgs& a, int tile, TileMeta& tm,
+                                               bool with_tau) {
+  for (int i = threadIdx.x; i < kPQT; i += blockDim.x) {
+    const int rl = tile * kPQT + i;
+    const bool ok = rl < a.rows;
+    const int row = a.row0 + rl;
+    tm.seq[i] = ok ? a.idx.seq_of(row) : -1;
+    tm.n[i] = ok ? a.idx.pos_of(row) / kBlock : 0;
+    tm.tau[i] = (ok && with_tau) ? a.tau[rl] : 0u;
+    tm.done[i] = ok ? 0 : 1;
+  }
+  __syncthreads();
+}
+
+// Next sequence of the tile still to process (rows of one sequence share
+// the staged pooled keys); false when every row is done.
+__device__ __forceinline__ bool next_pass(TileMeta& tm) {
+  if (threadIdx.x == 0) {
+    int cur = -1;
+    for (int i = 0; i < kPQT; ++i)
+      if (!tm.done[i]) {
+        cur = tm.seq[i];
+        break;
+      }
+    tm.cur_seq = cur;
+  }
+  __syncthreads();
+  const int cur = tm.cur_seq;
+  if (cur < 0) return false;
+  for (int i = threadIdx.x; i < kPQT; i += blockDim.x) {
+    const bool act = !tm.done[i] && tm.seq[i] == cur;
+    tm.active[i] = act;
+    if (act) tm.done[i] = 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int hi = 0, lo = 0x7fffffff;
+    for (int i = 0; i < kPQT; ++i)
+      if (tm.active[i]) {
+        hi = max(hi, tm.n[i]);
+        lo = min(lo, tm.n[i]);
+      }
+    tm.n_hi = hi;
+    tm.n_lo = lo;
+  }
+  __syncthreads();
+  return true;
+}
+
+// sample stride of a pass: the largest power of two s <= kPMaxStride with
+// ceil(n_lo / 256 / s) * 16 >= 2 * top_k (or 1)
+__device__ __forceinline__ int pass_stride(int n_lo, int top_k) {
+  int s = 1;
+  while (s < kPMaxStride && ((n_lo + kPGrp * 2 * s - 1) / (kPGrp * 2 * s)) * 16 >= 2 * top_k)
+    s *= 2;
+  return s;
+}
+
+struct KeyArrayL {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
+};
+
+}  // namespace
+
+// P1 (FILTER = false) and P3 (FILTER = true).  Grid (splits, tiles).
+template <int DI, bool FILTER>
+__global__ void __launch_bounds__(256) pidx_kernel(PIdxArgs a) {
+  using Gm = PGeom<DI>;
+  __shared__ __align__(16) unsigned char kst[kPGrp * Gm::PITCH];
+  __shared__ int32_t pages[kPGrp];
+  __shared__ TileMeta tm;
+  const int split = blockIdx.x, tile = blockIdx.y;
+  const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
+  if (tile * kPQT >= a.rows) return;
+  load_tile_meta(a, tile, tm, FILTER);
+  const bf16_t* kbar = static_cast<const bf16_t*>(a.idx.kbar);
+  const bf16_t* qidx = static_cast<const bf16_t*>(a.idx.q_idx);
+  const int hi_n = a.idx.hi;
+  while (next_pass(tm)) {
+    const int seq = tm.cur_seq;
+    const int n_groups = (tm.n_hi + kPGrp - 1) / kPGrp;
+    const int s = FILTER ? 1 : a.tile_stride[tile];
+    if (!FILTER && threadIdx.x == 0 && split == 0) {
+      // the stride of this pass is a property of its rows; P2 reads it
+      for (int i = 0; i < kPQT; ++i)
+        if (tm.active[i]) a.row_stride[tile * kPQT + i] = s;
+    }
+    const int gps = (n_groups + a.splits - 1) / a.splits;
+    const int g0 = split * gps, g1 = min(n_groups, g0 + gps);
+    // A fragments of this wave's 8 tiles of 4 queries x 4 heads, weights,
+    // candidate counts, thresholds and survivor counts of the lane's query
+    u32x4_t af[8][Gm::KS];
+    float wq[8][4];
+    int nq[8];
+    uint32_t tq[8], run[8], lmax[8];
+#pragma unroll
+    for (int at = 0; at < 8; ++at) {
+      const int qa = w * 32 + at * 4 + c16 / 4, ha = c16 % 4;  // A row: query, head
+      const bool oka = tm.active[qa] && ha < hi_n;
+      const bf16_t* qp = qidx + ((int64_t)(a.row0 + tile * kPQT + qa) * hi_n + ha) * DI;
+#pragma unroll
+      for (int ks = 0; ks < Gm::KS; ++ks)
+        af[at][ks] = oka ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      const int qc = w * 32 + at * 4 + g;  // C rows: the lane's query
+      const bool okc = tm.active[qc];
+      const float* wp = a.idx.w + (int64_t)(a.row0 + tile * kPQT + qc) * hi_n;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wq[at][h] = (okc && h < hi_n) ? wp[h] : 0.0f;
+      nq[at] = okc ? tm.n[qc] : 0;
+      tq[at] = tm.tau[qc];
+      run[at] = 0u;
+      lmax[at] = 0u;
+    }
+    const int region = kPSurvCap / a.splits;
+    for (int G = g0; G < g1; ++G) {
+      if (!FILTER && (G % s) != 0) continue;
+      // stage the 256 pooled keys of group G (their pages first)
+      const int b0 = G * kPGrp;
+      const int bpp_sh = a.idx.pm.page_shift - 2;  // log2(blocks per page)
+      const int pg0 = b0 >> bpp_sh;
+      const int npg = ((min(b0 + kPGrp, tm.n_hi) - 1) >> bpp_sh) - pg0 + 1;
+      __syncthreads();
+      for (int i = threadIdx.x; i < npg; i += blockDim.x)
+        pages[i] = a.idx.pm.table[(int64_t)seq * a.idx.pm.max_pages + pg0 + i];
+      __syncthreads();
+      for (int v = threadIdx.x; v < kPGrp * Gm::VPR; v += blockDim.x) {
+        const int bi = v / Gm::VPR, part = v % Gm::VPR, b = b0 + bi;
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (b < tm.n_hi) {
+          const int64_t slot = ((int64_t)pages[(b >> bpp_sh) - pg0] << bpp_sh) +
+                               (b & ((1 << bpp_sh) - 1));
+          x = *reinterpret_cast<const u32x4_t*>(kbar + slot * DI + part * 8);
+        }
+        *reinterpret_cast<u32x4_t*>(kst + bi * Gm::PITCH + part * 16) = x;
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int t16 = 0; t16 < kPGrp / 16; ++t16) {
+        u32x4_t bf[Gm::KS];
+        const unsigned char* rowp = kst + (t16 * 16 + c16) * Gm::PITCH;
+#pragma unroll
+        for (int ks = 0; ks < Gm::KS; ++ks)
+          bf[ks] = *reinterpret_cast<const u32x4_t*>(rowp + 64 * ks + 16 * g);
+        const int b = b0 + t16 * 16 + c16;
+#pragma unroll
+        for (int at = 0; at < 8; ++at) {
+          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < Gm::KS; ++ks) c = mfma_bf16(af[at][ks], bf[ks], c);
+          float sc = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) sc = fmaf(wq[at][h], fmaxf(c[h], 0.0f), sc);
+          const uint32_t key = (b < nq[at]) ? score_key(sc) : 0u;
+          if (!FILTER) {
+            lmax[at] = max(lmax[at], key);
+          } else {
+            const bool sv = key != 0u && key >= tq[at];
+            const uint64_t m = ballot(sv);
+            const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
+            if (mg != 0u) {
+              const uint32_t pos = run[at] + __popc(mg & ((1u << c16) - 1u));
+              if (sv && pos < (uint32_t)region) {
+                const int rl = tile * kPQT + w * 32 + at * 4 + g;
+                a.surv[((int64_t)rl * a.splits + split) * region + pos] =
+                    ((uint64_t)(uint32_t)b << 32) | key;
+              }
+              run[at] += __popc(mg);
+            }
+          }
+        }
+      }
+      if (!FILTER) {
+        // union entry (G / s) * 16 + lane of the lane's query
+#pragma unroll
+        for (int at = 0; at < 8; ++at) {
+          const int qc = w * 32 + at * 4 + g;
+          const int rl = tile * kPQT + qc;
+          const int u = (G / s) * 16 + c16;
+          if (tm.active[qc] && u < kPUnion) a.uni[(int64_t)rl * kPUnion + u] = lmax[at];
+          lmax[at] = 0u;
+        }
+      }
+    }
+    if (FILTER && c16 == 0) {
+#pragma unroll
+      for (int at = 0; at < 8; ++at) {
+        const int qc = w * 32 + at * 4 + g;
+        if (tm.active[qc]) a.surv_cnt[(int64_t)(tile * kPQT + qc) * a.splits + split] = run[at];
+      }
+    }
+  }
+}
+
+// Sample stride per tile: from the smallest candidate count of the tile's
+// first sequence (P1 of a tile uses one stride for all its passes).
+__global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
+  __shared__ int lo;
+  const int tile = blockIdx.x;
+  if (threadIdx.x == 0) lo = 0x7fffffff;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPQT; i += blockDim.x) {
+    const int rl = tile * kPQT + i;
+    if (rl < a.rows) atomicMin(&lo, a.idx.pos_of(a.row0 + rl) / kBlock);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.tile_stride[tile] = pass_stride(lo, a.top_k);
+}
+
+// P2: tau per row from its union of group maxima.
+__global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
+  __shared__ uint32_t u[kPUnion];
+  __shared__ SelShared sh;
+  const int rl = blockIdx.x, row = a.row0 + rl;
+  const int n = a.idx.pos_of(row) / kBlock;
+  if (n <= a.top_k) return;
+  const int s = a.row_stride[rl];
+  const int n_groups = (n + kPGrp - 1) / kPGrp;
+  const int un = min(kPUnion, ((n_groups + s - 1) / s) * 16);
+  const uint32_t* src = a.uni + (int64_t)rl * kPUnion;
+  for (int e = threadIdx.x; e < un; e += blockDim.x) u[e] = src[e];
+  __syncthreads();
+  uint32_t tau = 0u;
+  if (un >= a.top_k) {
+    int r;
+    radix_kth(KeyArrayL{u}, un, a.top_k, sh, tau, r);
+  }
+  if (threadIdx.x == 0) a.tau[rl] = tau;
+}
+
+// Key of candidate e recomputed by this lane alone (P4's rare fallback).
+template <int DI>
+struct PRecomputed {
+  const PIdxArgs* a;
+  int row, seq;
+  __device__ __forceinline__ uint32_t operator()(int e) const {
+    const bf16_t* kb = static_cast<const bf16_t*>(a->idx.kbar) + a->idx.pm.block_slot(seq, e) * DI;
+    const bf16_t* qr = static_cast<const bf16_t*>(a->idx.q_idx) + (int64_t)row * a->idx.hi * DI;
+    float s = 0.0f;
+    for (int h = 0; h < a->idx.hi; ++h) {
+      float d = 0.0f;
+      for (int c = 0; c < DI; ++c) d = fmaf(to_f32(qr[h * DI + c]), to_f32(kb[c]), d);
+      s = fmaf(a->idx.w[(int64_t)row * a->idx.hi + h], fmaxf(d, 0.0f), s);
+    }
+    return score_key(s);
+  }
+};
+
+struct IdSelf {
+  __device__ __forceinline__ int32_t operator()(int e) const { return e; }
+};
+struct IdArrayL {
+  const int32_t* id;
+  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
+};
+
+// P4: gather, exact select, ordered emission.
+template <int DI>
+__global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
+  __shared__ uint32_t ck[kPSurvCap];
+  __shared__ int32_t ci[kPSurvCap];
+  __shared__ uint32_t offs[kPMaxSplits + 1];
+  __shared__ SelShared sh;
+  const int rl = blockIdx.x, row = a.row0 + rl;
+  const int n = a.idx.pos_of(row) / kBlock;
+  int32_t* sel_row = a.sel + (int64_t)row * a.top_k;
+  if (n <= a.top_k) {
+    for (int j = threadIdx.x; j < a.top_k; j += blockDim.x) sel_row[j] = j < n ? j : -1;
+    if (threadIdx.x == 0) a.n_sel[row] = n;
+    return;
+  }
+  const int region = kPSurvCap / a.splits;
+  if (threadIdx.x == 0) {
+    uint32_t o = 0;
+    bool over = false;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const uint32_t c = a.surv_cnt[(int64_t)rl * a.splits + sp];
+      over |= c > (uint32_t)region;
+      offs[sp] = o;
+      o += c;
+    }
+    offs[a.splits] = over ? 0xffffffffu : o;
+  }
+  __syncthreads();
+  const uint32_t m = offs[a.splits];
+  if (m != 0xffffffffu && m >= (uint32_t)a.top_k) {
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const uint32_t cnt = ((sp + 1 < a.splits) ? offs[sp + 1] : m) - offs[sp];
+      const uint64_t* src = a.surv + ((int64_t)rl * a.splits + sp) * region;
+      for (uint32_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+        const uint64_t v = src[i];
+        ck[offs[sp] + i] = (uint32_t)v;
+        ci[offs[sp] + i] = (int32_t)(v >> 32);
+      }
+    }
+    __syncthreads();
+    uint32_t thr;
+    int r;
+    radix_kth(KeyArrayL{ck}, (int)m, a.top_k, sh, thr, r);
+    emit_topk(KeyArrayL{ck}, IdArrayL{ci}, (int)m, thr, r, sel_row, a.top_k, sh);
+  } else {
+    // survivors overflowed their slots (or fewer than k, which a valid tau
+    // excludes): exact select over every candidate
+    const PRecomputed<DI> get{&a, row, a.idx.seq_of(row)};
+    uint32_t thr;
+    int r;
+    radix_kth(get, n, a.top_k, sh, thr, r);
+    emit_topk(get, IdSelf{}, n, thr, r, sel_row, a.top_k, sh);
+  }
+  if (threadIdx.x == 0) a.n_sel[row] = a.top_k;
+}
+
+bool pidx_supported(int dtype, int di, int hi) {
+  return dtype == QSA_BF16 && (di == 64 || di == 128) && hi >= 1 && hi <= 4;
+}
+
+void run_pidx(const PIdxArgs& a, int di, hipStream_t st) {
+  const int tiles = (a.rows + kPQT - 1) / kPQT;
+  dim3 grid((unsigned)a.splits, (unsigned)tiles);
+  hipLaunchKernelGGL(pidx_stride_kernel, dim3(tiles), dim3(256), 0, st, a);
+  if (di == 64) {
+    hipLaunchKernelGGL((pidx_kernel<64, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_select_kernel<64>), dim3(a.rows), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_select_kernel<128>), dim3(a.rows), dim3(256), 0, st, a);
+  }
+}
+
+}  // namespace qsa

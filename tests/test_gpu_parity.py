@@ -96,14 +96,20 @@ def _check_topk(pb, st):
         assert_sel_row(sel[i], int(n[i]), pb.oracle_select(i), pb.wl.top_k)
 
 
+# 80 rows: fused top-k of at least 64 rows runs on the matrix-core indexer
+MIXED80_POS = sorted(MIXED_POS * 4)
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
-@pytest.mark.parametrize("case", ["tiny", "decode_8x32k", "mixed"])
+@pytest.mark.parametrize("case", ["tiny", "decode_8x32k", "mixed", "mixed80"])
 def test_topk_bit_exact(gpu, case, fused):
     _say(f"topk {case} fused={fused}")
     if case == "tiny":
         pb = Problem(WL["tiny_decode"], gpu)
     elif case == "decode_8x32k":
         pb = Problem(WL["decode_8x32k"], gpu)
+    elif case == "mixed80":
+        pb = Problem(MIXED, gpu, [0] * len(MIXED80_POS), MIXED80_POS)
     else:
         pb = Problem(MIXED, gpu, [0] * len(MIXED_POS), MIXED_POS)
     pb.pool_all()
@@ -120,14 +126,15 @@ def test_topk_bit_exact(gpu, case, fused):
     _check_topk(pb, st)
 
 
+@pytest.mark.parametrize("rows", [4, 64], ids=["4rows", "64rows"])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
-@pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190)])
-def test_topk_ties_lower_id_wins(gpu, n_tied, first, fused):
-    """Many blocks with identical top scores: the lowest ids win.  1024 tied
-    blocks in one chunk overflow its survivor slots (exact fallback)."""
-    _say(f"ties {n_tied} {first} fused={fused}")
+@pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190), (9000, 100)])
+def test_topk_ties_lower_id_wins(gpu, n_tied, first, fused, rows):
+    """Many blocks with identical top scores: the lowest ids win.  Large tie
+    groups overflow the survivor slots (exact fallback paths)."""
+    _say(f"ties {n_tied} {first} fused={fused} rows={rows}")
     wl = MIXED.replace(n_ctx=80004)
-    pos = [20000 * 4 + 1, 9000 * 4 + 3, 8000 * 4, 600 * 4 + 2]
+    pos = [20000 * 4 + 1, 9000 * 4 + 3, 8000 * 4, 600 * 4 + 2] * (rows // 4)
     pb = Problem(wl, gpu, [0] * len(pos), pos)
     pat = (3.0 * pb.cache.direction[0]).to(torch.bfloat16)
     for b in range(first, first + n_tied):
@@ -147,11 +154,12 @@ def test_topk_ties_lower_id_wins(gpu, n_tied, first, fused):
     _check_topk(pb, st)
 
 
+@pytest.mark.parametrize("rows", [4, 64], ids=["4rows", "64rows"])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
-def test_topk_all_scores_equal(gpu, fused):
+def test_topk_all_scores_equal(gpu, fused, rows):
     """q_idx = 0 gives every block score 0: ids 0..k-1 are selected."""
-    _say(f"all-equal fused={fused}")
-    pos = [3, 2100, 30000, 80003]
+    _say(f"all-equal fused={fused} rows={rows}")
+    pos = [3, 2100, 30000, 80003] * (rows // 4)
     pb = Problem(MIXED.replace(n_ctx=80004), gpu, [0] * len(pos), pos)
     pb.qs.q_idx.zero_()
     pb.pool_all()
