@@ -82,10 +82,11 @@ struct PidxPlan {
 
 PidxPlan pidx_plan(const qsa_queries* qm) {
   PidxPlan p;
-  p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
+  p.rows = qm->n_rows < kPRowBatch ? qm->n_rows : kPRowBatch;
   if (p.rows < 1) p.rows = 1;
   const int tiles = (p.rows + kPQT - 1) / kPQT;
-  int sp = 256 / tiles;
+  // enough workgroups for four per CU
+  int sp = (1024 + tiles - 1) / tiles;
   p.splits = sp < 1 ? 1 : (sp > kPMaxSplits ? kPMaxSplits : sp);
   size_t o = 0;
   p.off_uni = o;     o = align256(o + (size_t)p.rows * kPUnion * 4);

@@ -78,13 +78,15 @@ struct TopkArgs {
 };
 
 // ---- MFMA prefill indexer (index_mfma.hip)
-constexpr int kPQT = 128;         // query rows per workgroup tile (4 waves x 32)
+constexpr int kPQT = 128;         // query rows per workgroup tile (8 waves x 16)
+constexpr int kPThreads = 512;    // threads of a scoring workgroup
 constexpr int kPGrp = 256;        // pooled keys staged per group
 constexpr int kPUnion = 4096;     // union entries (group maxima) per row
 constexpr int kPSurvCap = 8192;   // survivor slots per row, over all splits
 constexpr int kPMaxStride = 8;    // largest group sampling stride of P1
-constexpr int kPMaxSplits = 8;    // block splits per tile
+constexpr int kPMaxSplits = 16;   // block splits per tile
 constexpr int kPMinRows = 64;     // fused top-k of at least this many rows uses it
+constexpr int kPRowBatch = 32768; // rows per launch
 
 struct PIdxArgs {
   IdxArgs idx;

@@ -14,7 +14,7 @@
 //   4 queries x 4 heads = 16 rows -- and B = 16 pooled-key rows.  Lane l of
 //   the 16x16 result holds the four head dot products of query l/16 with
 //   block l%16, so the ReLU and the weighted head sum are in-lane.
-// A workgroup (4 waves x 32 queries) stages 256 pooled keys (one "group")
+// A workgroup (8 waves x 16 queries) stages 256 pooled keys (one "group")
 // at a time in LDS and runs them against its 128 queries.
 //
 // Exact top-k in four launches per batch of rows:
@@ -28,6 +28,8 @@
 //   P4  per row: survivors gathered in block order -> exact radix select and
 //       ordered emission (select.hpp); a row whose survivors overflowed its
 //       slots falls back to an exact select over recomputed keys.
+#include <type_traits>
+
 #include "index.hpp"
 #include "select.hpp"
 
@@ -121,6 +123,14 @@ __device__ __forceinline__ int pass_stride(int n_lo, int top_k) {
   return s;
 }
 
+// Order-preserving key of a score, as score_key() but in four operations:
+// adding +0.0 turns -0.0 into +0.0; non-negative floats get the sign bit
+// set, negative ones are inverted.  Every key of a real score is >= 1.
+__device__ __forceinline__ uint32_t ordered_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 struct KeyArrayL {
   const uint32_t* k;
   __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
@@ -128,12 +138,18 @@ struct KeyArrayL {
 
 }  // namespace
 
-// P1 (FILTER = false) and P3 (FILTER = true).  Grid (splits, tiles).
+// Inverse of ordered_key: the float whose key is k (k >= 1).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// P1 (FILTER = false) and P3 (FILTER = true).  Grid (splits, tiles); 8 waves
+// of 16 queries (4 MFMA tiles of 4 queries x 4 heads) per workgroup.
 template <int DI, bool FILTER>
-__global__ void __launch_bounds__(256) pidx_kernel(PIdxArgs a) {
+__global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxArgs a) {
   using Gm = PGeom<DI>;
+  constexpr int AT = kPQT / (kPThreads / kWave) / 4;  // MFMA tiles per wave
   __shared__ __align__(16) unsigned char kst[kPGrp * Gm::PITCH];
-  __shared__ int32_t pages[kPGrp];
   __shared__ TileMeta tm;
   const int split = blockIdx.x, tile = blockIdx.y;
   const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
@@ -142,6 +158,7 @@ __global__ void __launch_bounds__(256) pidx_kernel(PIdxArgs a) {
   const bf16_t* kbar = static_cast<const bf16_t*>(a.idx.kbar);
   const bf16_t* qidx = static_cast<const bf16_t*>(a.idx.q_idx);
   const int hi_n = a.idx.hi;
+  const float kNegInf = -__builtin_inff();
   while (next_pass(tm)) {
     const int seq = tm.cur_seq;
     const int n_groups = (tm.n_hi + kPGrp - 1) / kPGrp;
@@ -153,52 +170,67 @@ __global__ void __launch_bounds__(256) pidx_kernel(PIdxArgs a) {
     }
     const int gps = (n_groups + a.splits - 1) / a.splits;
     const int g0 = split * gps, g1 = min(n_groups, g0 + gps);
-    // A fragments of this wave's 8 tiles of 4 queries x 4 heads, weights,
-    // candidate counts, thresholds and survivor counts of the lane's query
-    u32x4_t af[8][Gm::KS];
-    float wq[8][4];
-    int nq[8];
-    uint32_t tq[8], run[8], lmax[8];
+    // A fragments of this wave's AT tiles of 4 queries x 4 heads, and for the
+    // lane's query (C rows): weights, threshold as a float (-inf keeps
+    // everything, NaN nothing) and survivor count
+    u32x4_t af[AT][Gm::KS];
+    float wq[AT][4], tf[AT], lmax[AT];
+    uint32_t run[AT];
 #pragma unroll
-    for (int at = 0; at < 8; ++at) {
-      const int qa = w * 32 + at * 4 + c16 / 4, ha = c16 % 4;  // A row: query, head
+    for (int at = 0; at < AT; ++at) {
+      const int qa = w * (4 * AT) + at * 4 + c16 / 4, ha = c16 % 4;  // A row: query, head
       const bool oka = tm.active[qa] && ha < hi_n;
       const bf16_t* qp = qidx + ((int64_t)(a.row0 + tile * kPQT + qa) * hi_n + ha) * DI;
 #pragma unroll
       for (int ks = 0; ks < Gm::KS; ++ks)
         af[at][ks] = oka ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks + 8 * g)
                          : u32x4_t{0u, 0u, 0u, 0u};
-      const int qc = w * 32 + at * 4 + g;  // C rows: the lane's query
+      const int qc = w * (4 * AT) + at * 4 + g;
       const bool okc = tm.active[qc];
       const float* wp = a.idx.w + (int64_t)(a.row0 + tile * kPQT + qc) * hi_n;
 #pragma unroll
       for (int h = 0; h < 4; ++h) wq[at][h] = (okc && h < hi_n) ? wp[h] : 0.0f;
-      nq[at] = okc ? tm.n[qc] : 0;
-      tq[at] = tm.tau[qc];
+      const uint32_t tk = tm.tau[qc];
+      tf[at] = !okc ? __builtin_nanf("") : (tk == 0u ? kNegInf : key_float(tk));
       run[at] = 0u;
-      lmax[at] = 0u;
+      lmax[at] = kNegInf;
     }
     const int region = kPSurvCap / a.splits;
-    for (int G = g0; G < g1; ++G) {
-      if (!FILTER && (G % s) != 0) continue;
-      // stage the 256 pooled keys of group G (their pages first)
+    const int bpp_sh = a.idx.pm.page_shift - 2;  // log2(blocks per page)
+    const int n_hi = tm.n_hi;
+    // blocks at or past a row's candidate count only occur in tiles that
+    // reach past the pass's smallest count
+    const int n_lo_pass = __builtin_amdgcn_readfirstlane(tm.n_lo);
+    constexpr int VPT = kPGrp * Gm::VPR / kPThreads;
+    const int64_t tbase = (int64_t)seq * a.idx.pm.max_pages;
+    auto first_group = [&](int G) {
+      while (G < g1 && !FILTER && (G % s) != 0) ++G;
+      return G;
+    };
+    for (int G = first_group(g0); G < g1; G = first_group(G + 1)) {
       const int b0 = G * kPGrp;
-      const int bpp_sh = a.idx.pm.page_shift - 2;  // log2(blocks per page)
-      const int pg0 = b0 >> bpp_sh;
-      const int npg = ((min(b0 + kPGrp, tm.n_hi) - 1) >> bpp_sh) - pg0 + 1;
-      __syncthreads();
-      for (int i = threadIdx.x; i < npg; i += blockDim.x)
-        pages[i] = a.idx.pm.table[(int64_t)seq * a.idx.pm.max_pages + pg0 + i];
-      __syncthreads();
-      for (int v = threadIdx.x; v < kPGrp * Gm::VPR; v += blockDim.x) {
-        const int bi = v / Gm::VPR, part = v % Gm::VPR, b = b0 + bi;
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (b < tm.n_hi) {
-          const int64_t slot = ((int64_t)pages[(b >> bpp_sh) - pg0] << bpp_sh) +
-                               (b & ((1 << bpp_sh) - 1));
-          x = *reinterpret_cast<const u32x4_t*>(kbar + slot * DI + part * 8);
+      __syncthreads();  // the previous group's LDS reads are done
+      {
+        // pooled keys of the group -> LDS (other workgroups on the CU
+        // compute meanwhile)
+        u32x4_t v[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          const int vi = threadIdx.x + kPThreads * j;
+          const int b = b0 + vi / Gm::VPR, part = vi % Gm::VPR;
+          v[j] = u32x4_t{0u, 0u, 0u, 0u};
+          if (b < n_hi) {
+            const int32_t pg = a.idx.pm.table[tbase + (b >> bpp_sh)];
+            const int64_t slot = ((int64_t)pg << bpp_sh) + (b & ((1 << bpp_sh) - 1));
+            v[j] = *reinterpret_cast<const u32x4_t*>(kbar + slot * DI + part * 8);
+          }
         }
-        *reinterpret_cast<u32x4_t*>(kst + bi * Gm::PITCH + part * 16) = x;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          const int vi = threadIdx.x + kPThreads * j;
+          *reinterpret_cast<u32x4_t*>(kst + (vi / Gm::VPR) * Gm::PITCH + (vi % Gm::VPR) * 16) =
+              v[j];
+        }
       }
       __syncthreads();
 #pragma unroll 1
@@ -209,49 +241,68 @@ __global__ void __launch_bounds__(256) pidx_kernel(PIdxArgs a) {
         for (int ks = 0; ks < Gm::KS; ++ks)
           bf[ks] = *reinterpret_cast<const u32x4_t*>(rowp + 64 * ks + 16 * g);
         const int b = b0 + t16 * 16 + c16;
+        f32x4_t c[AT];
 #pragma unroll
-        for (int at = 0; at < 8; ++at) {
-          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        for (int at = 0; at < AT; ++at) {
+          c[at] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < Gm::KS; ++ks) c = mfma_bf16(af[at][ks], bf[ks], c);
-          float sc = 0.0f;
+          for (int ks = 0; ks < Gm::KS; ++ks) c[at] = mfma_bf16(af[at][ks], bf[ks], c[at]);
+        }
+        // per tile: ReLU, weighted head sum, then the union maximum (P1) or
+        // the survivor test (P3); IN_RANGE: every block is a candidate of
+        // every row of the pass
+        auto epilogue = [&](auto in_range) {
 #pragma unroll
-          for (int h = 0; h < 4; ++h) sc = fmaf(wq[at][h], fmaxf(c[h], 0.0f), sc);
-          const uint32_t key = (b < nq[at]) ? score_key(sc) : 0u;
-          if (!FILTER) {
-            lmax[at] = max(lmax[at], key);
-          } else {
-            const bool sv = key != 0u && key >= tq[at];
-            const uint64_t m = ballot(sv);
-            const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
-            if (mg != 0u) {
-              const uint32_t pos = run[at] + __popc(mg & ((1u << c16) - 1u));
-              if (sv && pos < (uint32_t)region) {
-                const int rl = tile * kPQT + w * 32 + at * 4 + g;
-                a.surv[((int64_t)rl * a.splits + split) * region + pos] =
-                    ((uint64_t)(uint32_t)b << 32) | key;
+          for (int at = 0; at < AT; ++at) {
+            float sc = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              sc = fmaf(wq[at][h], __builtin_amdgcn_fmed3f(c[at][h], 0.0f, 3.0e38f), sc);
+            bool in = true;
+            if constexpr (!decltype(in_range)::value) in = b < tm.n[w * (4 * AT) + at * 4 + g];
+            if (!FILTER) {
+              lmax[at] = in ? fmaxf(lmax[at], sc) : lmax[at];
+            } else {
+              // a float compare is the key compare: -0 and +0 compare
+              // equal, and NaN thresholds (rows not in this pass) keep nothing
+              const bool sv = in && sc >= tf[at];
+              const uint64_t m = ballot(sv);
+              if (m != 0ull) {
+                const uint64_t gm = m & (0xffffull << (16 * g));
+                const uint32_t pos = run[at] + lanes_below(gm);
+                if (sv && pos < (uint32_t)region) {
+                  const int rl = tile * kPQT + w * (4 * AT) + at * 4 + g;
+                  a.surv[((int64_t)rl * a.splits + split) * region + pos] =
+                      ((uint64_t)(uint32_t)b << 32) | ordered_key(sc);
+                }
+                run[at] += (uint32_t)__popcll(gm);
               }
-              run[at] += __popc(mg);
             }
           }
-        }
+        };
+        if (b0 + t16 * 16 + 16 <= n_lo_pass)  // wave-uniform
+          epilogue(std::true_type{});
+        else
+          epilogue(std::false_type{});
       }
       if (!FILTER) {
-        // union entry (G / s) * 16 + lane of the lane's query
+        // union entry (G / s) * 16 + lane of the lane's query; key 0 where
+        // the lane saw no candidate
 #pragma unroll
-        for (int at = 0; at < 8; ++at) {
-          const int qc = w * 32 + at * 4 + g;
+        for (int at = 0; at < AT; ++at) {
+          const int qc = w * (4 * AT) + at * 4 + g;
           const int rl = tile * kPQT + qc;
           const int u = (G / s) * 16 + c16;
-          if (tm.active[qc] && u < kPUnion) a.uni[(int64_t)rl * kPUnion + u] = lmax[at];
-          lmax[at] = 0u;
+          const uint32_t key = lmax[at] == kNegInf ? 0u : ordered_key(lmax[at]);
+          if (tm.active[qc] && u < kPUnion) a.uni[(int64_t)rl * kPUnion + u] = key;
+          lmax[at] = kNegInf;
         }
       }
     }
     if (FILTER && c16 == 0) {
 #pragma unroll
-      for (int at = 0; at < 8; ++at) {
-        const int qc = w * 32 + at * 4 + g;
+      for (int at = 0; at < AT; ++at) {
+        const int qc = w * (4 * AT) + at * 4 + g;
         if (tm.active[qc]) a.surv_cnt[(int64_t)(tile * kPQT + qc) * a.splits + split] = run[at];
       }
     }
@@ -385,14 +436,14 @@ void run_pidx(const PIdxArgs& a, int di, hipStream_t st) {
   dim3 grid((unsigned)a.splits, (unsigned)tiles);
   hipLaunchKernelGGL(pidx_stride_kernel, dim3(tiles), dim3(256), 0, st, a);
   if (di == 64) {
-    hipLaunchKernelGGL((pidx_kernel<64, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<64, false>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<64>), dim3(a.rows), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<128>), dim3(a.rows), dim3(256), 0, st, a);
   }
 }
