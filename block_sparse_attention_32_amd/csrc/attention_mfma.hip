@@ -14,8 +14,9 @@
 //     that lane l's eight k-slots are exactly the eight tokens whose scores
 //     lane l holds; A = V^T read from an LDS copy of the tile's V rows.
 //
-// Workgroups: 4 waves per (row, split).  With n_splits > 1 the split
-// partials go to the workspace and the last split of the row merges them.
+// Workgroups: 4 waves per (row, split).  With n_splits > 1 (the SPLIT
+// instances) the split partials go to the workspace and the last split of
+// the row merges them.
 #include "attention.hpp"
 
 namespace qsa {
@@ -35,96 +36,91 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-constexpr int kMergeChunk = 128;  // splits staged in LDS per merge pass
-
-// Merge of a row's split partials (m in log2 units, l, unnormalised acc),
-// run by the last split workgroup after its acquire: splits are taken in
-// chunks; per head the running maximum, sum and per-split factors live in
-// LDS; each thread keeps running sums for its output elements and issues
-// the loads of eight splits before using them.
+// Split partials of a row, [split][head] x (D floats of unnormalised acc,
+// then (m in log2 units, l)), are written and merged by 256 threads that
+// each own one head and D/16 contiguous dims of it (hq <= 16).
 template <int D>
-__device__ void merge_splits(const AttnArgs& a, int row, float* sm, bf16_t* orow) {
-  const int hq = a.hq, S = a.n_splits;
-  float* sm_m = sm;                          // [kMergeChunk][16]
-  float* sm_f = sm + kMergeChunk * 16;       // [kMergeChunk][16]
-  float* run = sm + 2 * kMergeChunk * 16;    // [16][3]: M, L, rescale
+struct MergeLane {
+  static constexpr int ND = D / 16;  // dims per thread
+  int h, d0;
+  bool on;
+  __device__ MergeLane(int hq) : h(threadIdx.x / 16), d0((threadIdx.x % 16) * ND), on(h < hq) {}
+};
+
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+  return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+
+constexpr int kMergeBatch = 8;  // splits whose partials are in flight together
+
+// Merge of a row's split partials, run by the last split workgroup after its
+// acquire.  Each thread keeps a running (M, L, O[ND]) for its head and dims;
+// the partials of the next kMergeBatch splits are loaded while the current
+// batch is folded in.
+template <int D>
+__device__ void merge_splits(const AttnArgs& a, int row, bf16_t* orow) {
+  constexpr int ND = MergeLane<D>::ND;
+  constexpr int NV = ND / 2;  // 8-byte loads per split
+  const MergeLane<D> ml(a.hq);
+  if (!ml.on) return;
+  const int S = a.n_splits, hq = a.hq;
   const int64_t rb = (int64_t)row * S * hq;
-  constexpr int PER = (16 * D + 255) / 256;  // outputs per thread
-  float O[PER];
+  const uint64_t* pml = reinterpret_cast<const uint64_t*>(a.part_ml) + rb + ml.h;
+  const uint64_t* pacc = reinterpret_cast<const uint64_t*>(a.part_acc + (rb + ml.h) * D + ml.d0);
+  const int64_t acc_step = (int64_t)hq * D / 2;  // uint64 per split
+  float M = -INFINITY, L = 0.0f, O[ND];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) O[j] = 0.0f;
-  if (threadIdx.x < hq) {
-    run[threadIdx.x * 3 + 0] = -INFINITY;
-    run[threadIdx.x * 3 + 1] = 0.0f;
-  }
-  for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
-    const int ns = min(kMergeChunk, S - s0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < ns * hq; i += blockDim.x) {
-      const int s = i / hq, h = i % hq;
-      const float* ml = a.part_ml + (rb + (int64_t)(s0 + s) * hq + h) * 2;
-      sm_m[s * 16 + h] = ml[0];
-      sm_f[s * 16 + h] = ml[1];  // l for now
+  for (int j = 0; j < ND; ++j) O[j] = 0.0f;
+  uint64_t cm[kMergeBatch], cv[kMergeBatch][NV];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool ok = s0 + u < S;
+      cm[u] = ok ? pml[(int64_t)(s0 + u) * hq] : pack2(-INFINITY, 0.0f);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) cv[u][j] = ok ? pacc[(s0 + u) * acc_step + j] : 0ull;
     }
-    __syncthreads();
-    if (threadIdx.x < hq) {
-      const int h = threadIdx.x;
-      float Mc = -INFINITY;
-      for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, sm_m[s * 16 + h]);
-      const float Mr = run[h * 3 + 0];
-      const float Mn = fmaxf(Mr, Mc);
-      const float rs = (Mr == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Mr - Mn);
-      float L = run[h * 3 + 1] * rs;
-      for (int s = 0; s < ns; ++s) {
-        const float ms = sm_m[s * 16 + h];
-        const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - Mn);
-        L = fmaf(sm_f[s * 16 + h], f, L);
-        sm_f[s * 16 + h] = f;
-      }
-      run[h * 3 + 0] = Mn;
-      run[h * 3 + 1] = L;
-      run[h * 3 + 2] = rs;
+  };
+  load(0);
+  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+    uint64_t bm[kMergeBatch], bv[kMergeBatch][NV];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      bm[u] = cm[u];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) bv[u][j] = cv[u][j];
     }
-    __syncthreads();
-    // rescale, then accumulate eight splits at a time: all PER x 8 loads of
-    // a batch are issued before any is used
+    if (s0 + kMergeBatch < S) load(s0 + kMergeBatch);
+    float Mc = M;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int oi = threadIdx.x + 256 * j;
-      if (oi < hq * D) O[j] *= run[(oi / D) * 3 + 2];
-    }
-    for (int sb = 0; sb < ns; sb += 8) {
-      const int nb = min(8, ns - sb);
-      float v[PER][8];
+    for (int u = 0; u < kMergeBatch; ++u) Mc = fmaxf(Mc, lo_f(bm[u]));
+    if (Mc == -INFINITY) continue;  // nothing attended yet
+    const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+    L *= rs;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int oi = threadIdx.x + 256 * j;
-        const int h = oi / D, d = oi % D;
-        const float* src = a.part_acc + (rb + (int64_t)(s0 + sb) * hq + h) * D + d;
+    for (int j = 0; j < ND; ++j) O[j] *= rs;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[j][u] = (oi < hq * D && u < nb) ? src[(int64_t)u * hq * D] : 0.0f;
-      }
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float mu = lo_f(bm[u]);
+      const float f = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - Mc);
+      L = fmaf(hi_f(bm[u]), f, L);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int oi = threadIdx.x + 256 * j;
-        const int h = (oi < hq * D) ? oi / D : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (u < nb) O[j] = fmaf(v[j][u], sm_f[(sb + u) * 16 + h], O[j]);
+      for (int j = 0; j < NV; ++j) {
+        O[2 * j] = fmaf(lo_f(bv[u][j]), f, O[2 * j]);
+        O[2 * j + 1] = fmaf(hi_f(bv[u][j]), f, O[2 * j + 1]);
       }
     }
+    M = Mc;
   }
-  __syncthreads();
+  const float inv = 1.0f / L;
+  bf16_t* o = orow + ml.h * D + ml.d0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int oi = threadIdx.x + 256 * j;
-    if (oi >= hq * D) break;
-    orow[oi] = f32_to_bf16(O[j] / run[(oi / D) * 3 + 1]);
-  }
+  for (int j = 0; j < ND; ++j) o[j] = f32_to_bf16(O[j] * inv);
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
@@ -289,31 +285,41 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   }
   __syncthreads();
   bf16_t* orow = static_cast<bf16_t*>(a.out) + (int64_t)row * hq * D;
-  const int64_t pbase = ((int64_t)row * a.n_splits + split) * hq;
-  for (int oi = threadIdx.x; oi < hq * D; oi += blockDim.x) {
-    const int h = oi / D, d = oi % D, hk_ = h / G, hh = h % G;
+  // combine the waves of each KV head: thread = (head, D/16 dims)
+  const MergeLane<D> lane(hq);
+  constexpr int ND = MergeLane<D>::ND;
+  if (lane.on) {
+    const int hk_ = lane.h / G, hh = lane.h % G;
     float M = -INFINITY;
     for (int j = 0; j < wph; ++j) M = fmaxf(M, mrg[((hk_ + j * hkv) * 16 + hh) * (D + 2) + D]);
-    float L = 0.0f, O = 0.0f;
+    float L = 0.0f, O[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) O[i] = 0.0f;
     for (int j = 0; j < wph; ++j) {
       const float* o = mrg + ((hk_ + j * hkv) * 16 + hh) * (D + 2);
       const float f = (o[D] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(o[D] - M);
       L = fmaf(o[D + 1], f, L);
-      O = fmaf(o[d], f, O);
+#pragma unroll
+      for (int i = 0; i < ND; ++i) O[i] = fmaf(o[lane.d0 + i], f, O[i]);
     }
-    if (a.n_splits == 1) {
-      orow[oi] = f32_to_bf16(O / L);
+    if constexpr (!SPLIT) {
+      const float inv = 1.0f / L;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) orow[lane.h * D + lane.d0 + i] = f32_to_bf16(O[i] * inv);
     } else {
-      st_agent(a.part_acc + pbase * D + oi, O);
-      if (d == 0) {
-        st_agent(a.part_ml + (pbase + h) * 2, M);
-        st_agent(a.part_ml + (pbase + h) * 2 + 1, L);
-      }
+      // partials are read by another workgroup: agent-scope stores, 8 bytes
+      // at a time
+      const int64_t pbase = ((int64_t)row * a.n_splits + split) * hq + lane.h;
+      uint64_t* pacc = reinterpret_cast<uint64_t*>(a.part_acc + pbase * D + lane.d0);
+#pragma unroll
+      for (int i = 0; i < ND / 2; ++i) st_agent(pacc + i, pack2(O[2 * i], O[2 * i + 1]));
+      if (lane.d0 == 0) st_agent(reinterpret_cast<uint64_t*>(a.part_ml) + pbase, pack2(M, L));
     }
   }
-  if (a.n_splits == 1) return;
-  if (!arrive_last(a.cnt + row, (uint32_t)a.n_splits, &flag)) return;
-  merge_splits<D>(a, row, reinterpret_cast<float*>(lds), orow);
+  if constexpr (SPLIT) {
+    if (!arrive_last(a.cnt + row, (uint32_t)a.n_splits, &flag)) return;
+    merge_splits<D>(a, row, orow);
+  }
 }
 
 bool attn_mfma_supported(int dtype, int hq, int hkv, int d) {
@@ -323,13 +329,23 @@ bool attn_mfma_supported(int dtype, int hq, int hkv, int d) {
 
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st) {
   dim3 grid((unsigned)a.n_splits, (unsigned)n_rows);
+  const bool split = a.n_splits > 1;
+#define QSA_ATTN_LAUNCH(DD, DN, SP) \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP>), grid, dim3(256), 0, st, a)
   if (d == 128) {
-    if (dense) hipLaunchKernelGGL((attn_mfma_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<128, false>), grid, dim3(256), 0, st, a);
+    if (dense) {
+      if (split) QSA_ATTN_LAUNCH(128, true, true); else QSA_ATTN_LAUNCH(128, true, false);
+    } else {
+      if (split) QSA_ATTN_LAUNCH(128, false, true); else QSA_ATTN_LAUNCH(128, false, false);
+    }
   } else {
-    if (dense) hipLaunchKernelGGL((attn_mfma_kernel<64, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<64, false>), grid, dim3(256), 0, st, a);
+    if (dense) {
+      if (split) QSA_ATTN_LAUNCH(64, true, true); else QSA_ATTN_LAUNCH(64, true, false);
+    } else {
+      if (split) QSA_ATTN_LAUNCH(64, false, true); else QSA_ATTN_LAUNCH(64, false, false);
+    }
   }
+#undef QSA_ATTN_LAUNCH
 }
 
 }  // namespace qsa
