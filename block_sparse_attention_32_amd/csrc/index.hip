@@ -20,6 +20,8 @@
 // of kChunk consecutive blocks of one query row: it first stages the
 // chunk's page ids in LDS, then issues every pooled-key load of the chunk
 // before using any, so one round trip to memory covers the whole chunk.
+#include <type_traits>
+
 #include "index.hpp"
 #include "select.hpp"
 
@@ -93,6 +95,52 @@ struct IdxQuery {
   }
 };
 
+// bfloat16 rows: G = Di / 16 lanes per pooled key, each holding two
+// 16-byte pieces of it -- dims [8p, 8p + 8) and [8(p + G), 8(p + G) + 8) of
+// lane p of the group, so each of the two loads of a group reads one
+// contiguous half of the row.  Dot products use v_dot2_f32_bf16 on packed
+// pairs (products exact in fp32, accumulated in fp32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int DI, int HI>
+struct IdxQueryBf16 {
+  static constexpr int G = DI / 16;
+  uint32_t q[HI][8];
+  float w[HI];
+  __device__ __forceinline__ void load(const bf16_t* q_idx_row, const float* w_row, int hi,
+                                       int part) {
+#pragma unroll
+    for (int h = 0; h < HI; ++h) {
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+      w[h] = 0.0f;
+      if (h < hi) {
+        a = *reinterpret_cast<const uint4*>(q_idx_row + h * DI + 8 * part);
+        b = *reinterpret_cast<const uint4*>(q_idx_row + h * DI + 8 * (part + G));
+        w[h] = w_row[h];
+      }
+      q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
+      q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
+    }
+  }
+  __device__ __forceinline__ float score(const uint4& x0, const uint4& x1) const {
+    const uint32_t x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < HI; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = dot2_bf16(q[h][i], x[i], acc);
+      acc = group_sum<G>(acc);
+      s = fmaf(w[h], fmaxf(acc, 0.0f), s);
+    }
+    return canon_zero(s);
+  }
+};
+
 __device__ __forceinline__ float key_to_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
@@ -108,16 +156,39 @@ __device__ __forceinline__ void stage_pages(const PageMap& pm, int seq, int c0, 
   __syncthreads();
 }
 
+// Query side of one row for element type T: fp32 rows use IdxQuery,
+// bfloat16 rows the packed-pair IdxQueryBf16.
+template <typename T, int DI, int HI>
+struct RowQuery {
+  using type = IdxQuery<T, DI, HI>;
+  static constexpr int G = type::G;
+};
+template <int DI, int HI>
+struct RowQuery<bf16_t, DI, HI> {
+  using type = IdxQueryBf16<DI, HI>;
+  static constexpr int G = type::G;
+};
+
+template <typename T, int DI, int HI>
+__device__ __forceinline__ void load_row_query(typename RowQuery<T, DI, HI>::type& iq,
+                                               const IdxArgs& a, int row) {
+  iq.load(static_cast<const T*>(a.q_idx) + (int64_t)row * a.hi * DI, a.w + (int64_t)row * a.hi,
+          a.hi, threadIdx.x % RowQuery<T, DI, HI>::G);
+}
+
 // Scores of blocks [c0, c0 + kChunk) of one row, computed by the whole
-// workgroup into keys[] (ordered keys; blocks >= n get key 0).
+// workgroup into keys[] (ordered keys; blocks >= n get key 0).  All of a
+// thread's loads of a pass are issued before any is used.
 template <typename T, int DI, int HI>
 __device__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
-                             const IdxQuery<T, DI, HI>& iq, int32_t* pages, uint32_t* keys) {
-  constexpr int V = Vec<T>::N;
-  constexpr int G = DI / V;
+                             const typename RowQuery<T, DI, HI>::type& iq, int32_t* pages,
+                             uint32_t* keys) {
+  constexpr bool kBf = std::is_same<T, bf16_t>::value;
+  constexpr int G = RowQuery<T, DI, HI>::G;
+  constexpr int LPR = kBf ? 2 : 1;        // 16-byte loads per lane per row
   constexpr int RPI = 256 / G;            // rows per workgroup iteration
   constexpr int NIT = kChunk / RPI;       // iterations per chunk
-  constexpr int U = NIT < 32 ? NIT : 32;  // loads in flight per thread
+  constexpr int U = NIT * LPR < 32 ? NIT : 32 / LPR;  // iterations in flight
   stage_pages(a.pm, seq, c0, n, pages);
   const T* kbar = static_cast<const T*>(a.kbar);
   const int gi = threadIdx.x / G, part = threadIdx.x % G;
@@ -125,7 +196,7 @@ __device__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
   const int bsh = a.pm.page_shift - 2;  // log2(blocks per page)
 #pragma unroll 1
   for (int it0 = 0; it0 < NIT; it0 += U) {
-    uint4 raw[U];
+    uint4 raw[U][LPR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = c0 + (it0 + u) * RPI + gi;
@@ -133,27 +204,29 @@ __device__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
         const int64_t slot =
             ((int64_t)pages[((b * kBlock) >> a.pm.page_shift) - first] << bsh) +
             (b & ((1 << bsh) - 1));
-        raw[u] = *reinterpret_cast<const uint4*>(kbar + slot * DI + part * V);
+        const T* rowp = kbar + slot * DI;
+        if constexpr (kBf) {
+          raw[u][0] = *reinterpret_cast<const uint4*>(rowp + 8 * part);
+          raw[u][LPR - 1] = *reinterpret_cast<const uint4*>(rowp + 8 * (part + G));
+        } else {
+          raw[u][0] = *reinterpret_cast<const uint4*>(rowp + 4 * part);
+        }
       } else {
-        raw[u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < LPR; ++j) raw[u][j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float x[V];
-      if constexpr (V == 8) {
-        float t8[8];
-        Vec<bf16_t>::unpack(raw[u], t8);
-#pragma unroll
-        for (int i = 0; i < V; ++i) x[i] = t8[i];
+      float s;
+      if constexpr (kBf) {
+        s = iq.score(raw[u][0], raw[u][LPR - 1]);
       } else {
-        x[0] = __uint_as_float(raw[u].x);
-        x[1] = __uint_as_float(raw[u].y);
-        x[2] = __uint_as_float(raw[u].z);
-        x[3] = __uint_as_float(raw[u].w);
+        float x[4] = {__uint_as_float(raw[u][0].x), __uint_as_float(raw[u][0].y),
+                      __uint_as_float(raw[u][0].z), __uint_as_float(raw[u][0].w)};
+        s = iq.score(x);
       }
       const int i = (it0 + u) * RPI + gi;
-      const float s = iq.score(x);
       if (part == 0) keys[i] = (c0 + i < n) ? score_key(s) : 0u;
     }
   }
@@ -169,9 +242,8 @@ __global__ void __launch_bounds__(256) scores_kernel(IdxArgs a, float* scores, i
   const int n = a.pos_of(row) / kBlock;
   const int c0 = blockIdx.x * kChunk;
   if (c0 >= n) return;
-  IdxQuery<T, DI, HI> iq;
-  iq.load(static_cast<const T*>(a.q_idx) + (int64_t)row * a.hi * DI, a.w + (int64_t)row * a.hi,
-          a.hi, threadIdx.x % IdxQuery<T, DI, HI>::G);
+  typename RowQuery<T, DI, HI>::type iq;
+  load_row_query<T, DI, HI>(iq, a, row);
   chunk_scores<T, DI, HI>(a, seq, n, c0, iq, pages, keys);
   float* out = scores + (int64_t)row * ld + c0;
   for (int i = threadIdx.x; i < kChunk && c0 + i < n; i += blockDim.x)
@@ -308,9 +380,8 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
       keys[i] = (c0 + i < p.n) ? score_key(given[c0 + i]) : 0u;
     __syncthreads();
   } else {
-    IdxQuery<T, DI, HI> iq;
-    iq.load(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI,
-            t.idx.w + (int64_t)row * t.idx.hi, t.idx.hi, threadIdx.x % IdxQuery<T, DI, HI>::G);
+    typename RowQuery<T, DI, HI>::type iq;
+    load_row_query<T, DI, HI>(iq, t.idx, row);
     chunk_scores<T, DI, HI>(t.idx, p.seq, p.n, c0, iq, pages, keys);
     if (keep) {
       for (int i = threadIdx.x; i < kChunk && c0 + i < p.n; i += blockDim.x)
@@ -358,11 +429,27 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   const int jw = p.jw, nw = p.W * kSelWaves, un = nw * jw;
   uint32_t* ukey = dkeys;                                   // [kUnionCap]
   int32_t* uid = reinterpret_cast<int32_t*>(dkeys + kUnionCap);  // [kUnionCap]
-  for (int e = threadIdx.x; e < un; e += blockDim.x) {
-    const uint64_t v = tops[e];
-    ukey[e] = (uint32_t)v;
-    uid[e] = (int32_t)(v >> 32);
+  // per run: index into sat_w of a saturated run, else 0xff (nw <= kUnionCap
+  // bytes fit in the chunk's key buffer, no longer needed)
+  uint8_t* sat_of = reinterpret_cast<uint8_t*>(keys);
+  {
+    constexpr int UPT = kUnionCap / kSelThreads;
+    uint64_t v[UPT];  // all loads in flight before any is used
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int e = threadIdx.x + kSelThreads * i;
+      v[i] = e < un ? tops[e] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int e = threadIdx.x + kSelThreads * i;
+      if (e < un) {
+        ukey[e] = (uint32_t)v[i];
+        uid[e] = (int32_t)(v[i] >> 32);
+      }
+    }
   }
+  for (int gw = threadIdx.x; gw < nw; gw += kSelThreads) sat_of[gw] = 0xff;
   if (threadIdx.x == 0) n_sat = 0u;
   __syncthreads();
   // tau: the k-th largest published key, low bits past two digits cleared
@@ -371,16 +458,15 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
     int r;
     radix_kth(KeyArray{ukey}, un, t.top_k, sh, tau, r, 2);
   }
-  // runs (waves) owned by this thread: [w0, w1)
-  const int q = (nw + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(nw, (int)threadIdx.x * q), w1 = min(nw, w0 + q);
   // a run whose last published key still reaches tau is saturated
-#pragma unroll 1
-  for (int gw = w0; gw < w1; ++gw) {
+  for (int gw = threadIdx.x; gw < nw; gw += kSelThreads) {
     const uint32_t last = ukey[gw * jw + jw - 1];
     if (last >= tau && last != 0u) {
       const uint32_t sidx = atomicAdd(&n_sat, 1u);
-      if (sidx < (uint32_t)kMaxSat) sat_w[sidx] = gw;
+      if (sidx < (uint32_t)kMaxSat) {
+        sat_w[sidx] = gw;
+        sat_of[gw] = (uint8_t)sidx;
+      }
     }
   }
   __syncthreads();
@@ -398,20 +484,26 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
       sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
     __syncthreads();
   }
-  // survivors of an unsaturated run are its leading entries with key >= tau
+  // runs (waves) owned by this thread: [w0, w1).  The survivors of an
+  // unsaturated run are its leading entries with key >= tau (a run lists
+  // its keys best first, key 0 = nothing left).
+  const int q = (nw + kSelThreads - 1) / kSelThreads;
+  const int w0 = min(nw, (int)threadIdx.x * q), w1 = min(nw, w0 + q);
+  auto run_survivors = [&](int gw) {
+    int c2 = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJw; ++j)
+      if (j < jw) {
+        const uint32_t k = ukey[gw * jw + j];
+        c2 += (k >= tau && k != 0u) ? 1 : 0;
+      }
+    return c2;
+  };
   uint32_t mine = 0;
 #pragma unroll 1
   for (int gw = w0; gw < w1; ++gw) {
-    const uint32_t* rk = ukey + gw * jw;
-    if (rk[jw - 1] >= tau && rk[jw - 1] != 0u) {
-#pragma unroll 1
-      for (int i = 0; i < ns; ++i)
-        if (sat_w[i] == gw) mine += sat_cnt[i];
-    } else {
-      int c2 = 0;
-      while (c2 < jw && rk[c2] >= tau && rk[c2] != 0u) ++c2;
-      mine += (uint32_t)c2;
-    }
+    const int si = sat_of[gw];
+    mine += (si != 0xff) ? sat_cnt[si] : (uint32_t)run_survivors(gw);
   }
   uint32_t m_total;
   uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
@@ -419,25 +511,28 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   if (fits) {
 #pragma unroll 1
     for (int gw = w0; gw < w1; ++gw) {
-      const uint32_t* rk = ukey + gw * jw;
-      const int32_t* ri = uid + gw * jw;
-      if (rk[jw - 1] >= tau && rk[jw - 1] != 0u) {
-#pragma unroll 1
-        for (int i = 0; i < ns; ++i)
-          if (sat_w[i] == gw) {
-            sat_off[i] = off;
-            off += sat_cnt[i];
-          }
+      const int si = sat_of[gw];
+      if (si != 0xff) {
+        sat_off[si] = off;
+        off += sat_cnt[si];
         continue;
       }
+      // the run's survivors, best first, go to ascending-id places
+      uint32_t rk[kMaxJw];
+      int32_t ri[kMaxJw];
       int c2 = 0;
-      while (c2 < jw && rk[c2] >= tau && rk[c2] != 0u) ++c2;
-      // the run lists its survivors best first: place them by ascending id
-#pragma unroll 1
-      for (int i = 0; i < c2; ++i) {
+#pragma unroll
+      for (int j = 0; j < kMaxJw; ++j) {
+        rk[j] = j < jw ? ukey[gw * jw + j] : 0u;
+        ri[j] = j < jw ? uid[gw * jw + j] : 0;
+        c2 += (rk[j] >= tau && rk[j] != 0u) ? 1 : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < kMaxJw; ++i) {
+        if (i >= c2) break;
         uint32_t rank = 0;
-#pragma unroll 1
-        for (int j = 0; j < c2; ++j) rank += ri[j] < ri[i] ? 1u : 0u;
+#pragma unroll
+        for (int j = 0; j < kMaxJw; ++j) rank += (j < c2 && ri[j] < ri[i]) ? 1u : 0u;
         skey[off + rank] = rk[i];
         sid[off + rank] = ri[i];
       }
@@ -462,7 +557,11 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
     }
     __syncthreads();
   }
-  if (fits) {
+  if (fits && m_total == (uint32_t)t.top_k) {
+    // exactly k survivors: all of them, already in id order
+    for (int j = threadIdx.x; j < t.top_k; j += kSelThreads) sel_row[j] = sid[j];
+    if (threadIdx.x == 0) t.n_sel[row] = t.top_k;
+  } else if (fits) {
     uint32_t thr;
     int r;
     radix_kth(KeyArray{skey}, (int)m_total, t.top_k, sh, thr, r);
