@@ -2,10 +2,11 @@
 
 A step is one pass of the whole path over one batch of synthetic query rows,
 with the cache already resident in HBM:
-  decode : pool the newest complete block -> indexer scores -> exact top-k
-           -> split-K sparse attention (one query row per sequence)
-  prefill: pool the chunk's complete blocks -> fused scores + top-k
-           -> per-row sparse attention (one chunk of query rows)
+  decode : pool the newest complete block -> fused indexer scores and exact
+           top-k -> split-K sparse attention (one query row per sequence)
+  prefill: for every chunk of the prefill in order: pool the chunk's complete
+           blocks -> fused scores + top-k -> per-row sparse attention
+The default workload is the full 1M-token prefill (32 chunks of 32,768 rows).
 
 Prints one JSON line: query-tokens/s, per-call kernel times from HIP events
 on the launch stream, the roofline of the dominant kernel, the dense-GQA
@@ -17,7 +18,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,11 +31,11 @@ sys.path.insert(0, ROOT)
 
 from block_sparse_attention_32_amd import binding as B  # noqa: E402
 from block_sparse_attention_32_amd import workloads as W  # noqa: E402
+from block_sparse_attention_32_amd.rocprof_summary import source_hash, traffic_for  # noqa: E402
 
 METRIC = "QSA decode/prefill query-tokens/s at 128K & 1M ctx; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA
-PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
@@ -62,30 +62,11 @@ class Timer:
                 for k, v in self.pairs.items()}
 
 
-def source_hash(*files) -> str:
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "block_sparse_attention_32_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_for(kernel: str, workload: str, src_hash: str):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
-    taken on the current kernel source (else null)."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("source_hash") != src_hash:
-        return None
-    return d.get("hbm_bytes_per_launch")
-
-
 # ------------------------------------------------------------------ decode
 
-def run_decode(wl: W.Workload, steps: int, warmup: int, dev):
+def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
+    """One step = pool the newest complete block -> fused indexer scores and
+    exact top-k -> split-K sparse attention, for one query row per sequence."""
     from block_sparse_attention_32_amd import pipeline as P
     log(f"[bench] drawing {wl.name} cache on {dev}")
     cache = W.make_cache(wl, device=dev)
@@ -96,17 +77,38 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev):
     n_blocks = wl.total_len // 4
     P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
     step = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "decode")
-    max_n = max(pos) // 4
-    scores = torch.empty((rows.n_rows, max_n), dtype=torch.float32, device=dev)
     newest = torch.full((wl.n_seqs,), n_blocks - 1, dtype=torch.int32, device=dev)
 
     def one(timer=None):
         call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
         call("pool", B.qsa_pool_blocks, cv, newest, 1)
-        call("scores", B.qsa_index_scores, cv, rows, qs.q_idx, qs.w, scores)
-        call("topk", step.select, scores)
+        call("topk", step.select)          # fused: scores computed inside
         call("attn", step.attend)
 
+    wall, kern = _timed(one, steps, warmup)
+    n_sel = step.n_sel.cpu().numpy()
+    n_tok = int(sum(4 * int(n) + p % 4 + 1 for n, p in zip(n_sel, pos)))
+    cand = sum(p // 4 for p in pos)
+    esz = 2 if wl.dtype == "bf16" else 4
+    work = {
+        "topk": {"bytes": cand * wl.di * esz, "bound": "hbm", "kernel": "topk_kernel",
+                 "files": ("index.hip", "index.hpp", "select.hpp", "common.hpp")},
+        "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm",
+                 "kernel": "attn_mfma_kernel",
+                 "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
+        "pool": {"bytes": wl.n_seqs * 5 * wl.di * esz, "bound": "hbm", "kernel": "pool_kernel",
+                 "files": ("index.hip", "index.hpp", "common.hpp")},
+    }
+    dense_ms = None
+    if dense:
+        ds = P.DenseStep(cv, rows, qs.q, wl.scale, "decode")
+        dense_ms = _dense_time(ds.run, max(5, steps // 4))
+    ctx = {"rows": rows.n_rows, "cache": cache, "qs": qs, "pos": pos, "launches": 1,
+           "dense_ms": dense_ms, "dense_note": "split-K flash-decode over all tokens"}
+    return wall, kern, work, ctx
+
+
+def _timed(one, steps, warmup):
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
@@ -116,45 +118,26 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer = Timer()
-    for _ in range(steps):
+    for _ in range(max(1, min(steps, 50))):
         one(timer)
     torch.cuda.synchronize()
-    kern = timer.avg_us()
+    return wall, timer
 
-    # dense GQA flash-decode on the same inputs (comparison baseline)
-    dense = P.DenseStep(cv, rows, qs.q, wl.scale, "decode")
-    for _ in range(max(2, warmup // 2)):
-        dense.run()
-    torch.cuda.synchronize()
-    n_dense = max(5, steps // 4)
-    t1 = time.perf_counter()
-    for _ in range(n_dense):
-        dense.run()
-    torch.cuda.synchronize()
-    dense_ms = 1e3 * (time.perf_counter() - t1) / n_dense
 
-    n_sel = step.n_sel.cpu().numpy()
-    n_tok = int(sum(4 * int(n) + p % 4 + 1 for n, p in zip(n_sel, pos)))
-    esz = 2 if wl.dtype == "bf16" else 4
-    work = {
-        "scores": {"bytes": sum(p // 4 for p in pos) * wl.di * esz, "bound": "hbm"},
-        "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm"},
-        "topk": {"bytes": sum(p // 4 for p in pos) * 4, "bound": "hbm"},
-        "pool": {"bytes": wl.n_seqs * 5 * wl.di * esz, "bound": "hbm"},
-    }
-    kernels = {"scores": "scores_kernel", "attn": "attn_kernel", "topk": "topk_pass_a+b",
-               "pool": "pool_kernel"}
-    files = {"scores": ("index.hip", "index.hpp", "common.hpp"),
-             "attn": ("attention.hip", "attention.hpp", "common.hpp"),
-             "topk": ("index.hip", "index.hpp", "select.hpp", "common.hpp"),
-             "pool": ("index.hip", "index.hpp", "common.hpp")}
-    ctx = dict(rows=rows.n_rows, sel=(step, cache, qs, pos))
-    return wall, kern, work, kernels, files, dense_ms, ctx
+def _dense_time(fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return 1e3 * (time.perf_counter() - t0) / reps
 
 
 # ------------------------------------------------------------------ prefill
 
-def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense_too: bool = True):
+def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True,
+                dense_budget_s: float = 60.0):
     """One step = the whole prefill of wl: every chunk of query rows in
     order (pool the chunk's new blocks -> fused scores + top-k -> per-row
     sparse attention).  The existing context (if any) is pooled at set-up."""
@@ -171,81 +154,135 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense_too: bool = 
         st = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "prefill")
         b0 = pos[0] // 4
         begin = torch.full((1,), b0, dtype=torch.int32, device=dev)
-        chunks.append((st, begin, (pos[-1] + 1) // 4 - b0, pos))
+        chunks.append((st, begin, (pos[-1] + 1) // 4 - b0, pos, qs, rows))
     if wl.n_ctx:
         P.pool_all(cv, 1, wl.n_ctx // 4, dev)               # set-up, untimed
 
     def one(timer=None):
         call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
-        for st, begin, nb, _ in chunks:
+        for st, begin, nb, *_ in chunks:
             call("pool", B.qsa_pool_blocks, cv, begin, nb)
             call("topk", st.select)
             call("attn", st.attend)
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        one()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    timer = Timer()
-    one(timer)
-    torch.cuda.synchronize()
-    kern = {k: v * len(chunks) for k, v in timer.avg_us().items()}   # per step
+    wall, kern = _timed(one, steps, warmup)
     rows_total = sum(len(c[3]) for c in chunks)
     n_tok = 0
     cand = 0
-    for st, _, _, pos in chunks:
+    dense_flop = []
+    for st, _, _, pos, _, _ in chunks:
         ns = st.n_sel.cpu().numpy().astype(np.int64)
         p_ = np.asarray(pos, dtype=np.int64)
         n_tok += int((4 * ns + p_ % 4 + 1).sum())
         cand += int((p_ // 4).sum())
+        dense_flop.append(4.0 * wl.hq * wl.d * float((p_ + 1).sum()))
     esz = 2 if wl.dtype == "bf16" else 4
     work = {
         "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "flops": 4 * wl.hq * wl.d * n_tok,
-                 "bound": "hbm"},
-        "topk": {"flops": 2 * wl.hi * wl.di * cand, "bound": "alu"},
-        "pool": {"bytes": (wl.n_new // 4) * 5 * wl.di * esz, "bound": "hbm"},
+                 "bound": "hbm", "kernel": "attn_mfma_kernel",
+                 "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
+        "topk": {"flops": 2 * wl.hi * wl.di * cand, "bound": "mfma",
+                 "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_kernel",
+                 "files": ("index_mfma.hip", "index.hpp", "select.hpp", "common.hpp")},
+        "pool": {"bytes": (wl.n_new // 4) * 5 * wl.di * esz, "bound": "hbm",
+                 "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
     }
-    return wall, kern, work, rows_total, chunks, cache
+    # dense GQA attention over the same rows, chunk by chunk in order while
+    # the next chunk's projected time fits the budget; the rest is
+    # extrapolated by flops
+    ctx = {"rows": rows_total, "cache": cache, "chunks": chunks, "launches": n_chunks,
+           "dense_ms": None}
+    if not dense:
+        return wall, kern, work, ctx
+    measured = {}
+    t_start = time.perf_counter()
+    for ci in range(n_chunks):
+        if measured:
+            per_flop = sum(measured.values()) / sum(dense_flop[c] for c in measured)
+            left = dense_budget_s - (time.perf_counter() - t_start)
+            if per_flop * dense_flop[ci] * 1e-3 > left:
+                break
+        ds = P.DenseStep(cv, chunks[ci][5], chunks[ci][4].q, wl.scale, "prefill")
+        measured[ci] = _dense_time(ds.run, 1)
+        del ds
+    per_flop = sum(measured.values()) / sum(dense_flop[c] for c in measured)
+    dense_ms = per_flop * sum(dense_flop)
+    note = ("dense causal GQA over all chunks" if len(measured) == n_chunks else
+            f"dense causal GQA on chunks {sorted(measured)} of {n_chunks}, "
+            "extrapolated by flops")
+    ctx.update(dense_ms=dense_ms, dense_note=note,
+               dense_tflops=sum(dense_flop) / (dense_ms * 1e-3) / 1e12)
+    return wall, kern, work, ctx
 
 
 # ------------------------------------------------------------------ CPU oracle
 
-def cpu_baseline_decode(wl, ctx, budget_s=12.0):
-    """The oracle's decode step (pool the newest block, score every candidate,
-    select, attend) on rank 0's host cores, repeated for about budget_s."""
+def cpu_baseline(wl, ctx, budget_s=12.0):
+    """The oracle (numpy float64, one thread) on a bounded sample of the same
+    workload, scaled to query-tokens/s of the whole job."""
     import oracle as O
     from threadpoolctl import threadpool_limits
-    step, cache, qs, pos = ctx["sel"]
+    cache = ctx["cache"]
     log("[bench] cpu oracle: copying the cache to host")
-    seqs = []
-    for s in range(wl.n_seqs):
-        k, v, kidx = W.seq_view(cache, s)
-        seqs.append((k.float().cpu().numpy(), v.float().cpu().numpy(),
-                     kidx.double().cpu().numpy()))
-    q = qs.q.double().cpu().numpy()
-    q_idx = qs.q_idx.double().cpu().numpy()
-    w = qs.w.double().cpu().numpy()
-    kbars = [O.pool_blocks(kidx, wl.dtype) for _, _, kidx in seqs]   # set-up, untimed
-    done = 0
+    seqs = {}
+
+    def seq(s):
+        if s not in seqs:
+            k, v, kidx = W.seq_view(cache, s)
+            seqs[s] = [k.float().cpu().numpy(), v.float().cpu().numpy(),
+                       kidx.double().cpu().numpy(), None]
+        return seqs[s]
+
+    if wl.mode == "decode":
+        qs, pos = ctx["qs"], ctx["pos"]
+        rows = [(s, t, qs.q[i], qs.q_idx[i], qs.w[i]) for i, (s, t) in
+                enumerate(zip(qs.seq_id.cpu().tolist(), pos))][:64]
+        for s, *_ in rows:
+            e = seq(s)
+            if e[3] is None:
+                e[3] = O.pool_blocks(e[2], wl.dtype)        # set-up, untimed
+        pool_s = 0.0
+        sample = f"decode rows of {wl.name}, repeated"
+    else:
+        # whole-job pooling once (timed), then a seeded uniform sample of rows
+        e = seq(0)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            e[3] = O.pool_blocks(e[2], wl.dtype)
+            pool_s = time.perf_counter() - t0
+        rng = np.random.default_rng(wl.seed + 1)
+        rows = []
+        for _ in range(4096):
+            ci = int(rng.integers(len(ctx["chunks"])))
+            _, _, _, pos, qs, _ = ctx["chunks"][ci]
+            i = int(rng.integers(len(pos)))
+            rows.append((0, pos[i], qs.q[i], qs.q_idx[i], qs.w[i]))
+        sample = f"seeded uniform sample of {wl.name} rows"
+    rows = [(s, t, q.double().cpu().numpy(), qi.double().cpu().numpy(), w.double().cpu().numpy())
+            for s, t, q, qi, w in rows]
+    done, el = 0, 0.0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while True:
-            for i, t in enumerate(pos):
-                k, v, kidx = seqs[i]
-                nb = (t + 1) // 4
-                kbars[i][nb - 1:nb] = O.pool_blocks(kidx[: 4 * nb], wl.dtype, nb - 1, nb)
-                O.qsa_row(k, v, kbars[i], q[i], q_idx[i], w[i], t, wl.top_k, wl.scale)
+        while el < budget_s:
+            for s, t, q, qi, w in rows:
+                k, v, _, kbar = seq(s)
+                if wl.mode == "decode":
+                    nb = (t + 1) // 4
+                    kbar[nb - 1:nb] = O.pool_blocks(seq(s)[2][: 4 * nb], wl.dtype, nb - 1, nb)
+                O.qsa_row(k, v, kbar, q, qi, w, t, wl.top_k, wl.scale)
                 done += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    return {"value": done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode query rows of {wl.name} (full candidate range each), "
-                      f"{el:.1f} s, numpy float64 single-threaded"}
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+    per_row = el / done
+    job_s = pool_s + per_row * ctx["rows"]
+    return {"value": round(ctx["rows"] / job_s, 3), "unit": "query-tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} {sample} (score, select, attend; {el:.1f} s)"
+                      + (f" + whole-job pooling {pool_s:.1f} s; whole job "
+                         f"extrapolated as pooling + rows x mean row time"
+                         if wl.mode != "decode" else "") +
+                      "; numpy float64 single-threaded"}
 
 
 # ------------------------------------------------------------------ main
@@ -253,10 +290,11 @@ def cpu_baseline_decode(wl, ctx, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_1m", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="prefill_1m", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-GQA comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -270,6 +308,9 @@ def main():
     B.lib()  # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
+    decode = wl.mode == "decode"
+    steps = args.steps if args.steps is not None else (200 if decode else 3)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 1)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -277,55 +318,58 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if wl.mode != "decode":
-        wall, kern, work, rows_total, chunks, cache = run_prefill(wl, args.steps, args.warmup, dev)
-        ms = 1e3 * wall / args.steps
-        out = {
-            "metric": METRIC, "value": round(rows_total / (wall / args.steps), 1),
-            "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-            "config": {"workload": wl.name, "context": wl.n_ctx, "new_tokens": wl.n_new,
-                       "chunk": wl.chunk or wl.n_new, "hq": wl.hq, "hkv": wl.hkv,
-                       "head_dim": wl.d, "idx_heads": wl.hi, "idx_dim": wl.di,
-                       "top_k": wl.top_k, "page_size": wl.page_size,
-                       "parallelism": "single-gpu"},
-            "kernels_us": {k: round(v, 1) for k, v in kern.items()},
-            "work": work,
-        }
-        print(json.dumps(out), flush=True)
-        return
-    wall, kern, work, kernels, files, dense_ms, ctx = run_decode(wl, args.steps, args.warmup, dev)
-    ms = 1e3 * wall / args.steps
-    value = ctx["rows"] / (wall / args.steps)
-    dom = max(kern, key=kern.get)
+    if decode:
+        wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=not args.no_dense)
+    else:
+        wall, timer, work, ctx = run_prefill(wl, steps, warmup, dev, dense=not args.no_dense)
+    kern_call = timer.avg_us()                      # per API call
+    calls_per_step = ctx["launches"]
+    kern = {k: v * calls_per_step for k, v in kern_call.items()}   # per step
+    ms = 1e3 * wall / steps
+    value = ctx["rows"] / (wall / steps)
+    dom = max((k for k in kern if k in work), key=kern.get)
     wk = work[dom]
-    src_hash = source_hash(*files[dom])
-    achieved = wk["bytes"] / (kern[dom] * 1e-6) / 1e9
-    roof = {"kernel": kernels[dom], "bound": wk["bound"], "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for(kernels[dom], wl.name, src_hash),
-            "algorithmic_bytes": wk["bytes"], "avg_us": round(kern[dom], 2),
-            "source_hash": src_hash}
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline_decode(wl, ctx)
+    src_hash = source_hash(*wk["files"])
+    avg_us = kern_call[dom]
+    if wk["bound"] == "hbm":
+        per_launch = wk["bytes"] / calls_per_step
+        achieved, peak, unit = per_launch / (avg_us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        per_launch = wk["flops"] / calls_per_step
+        achieved, peak, unit = per_launch / (avg_us * 1e-6) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    roof = {"bound": wk["bound"], "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_for(wk["kernel"].split("+")[0], wl.name, src_hash),
+            "kernel": wk["kernel"], "algorithmic_per_launch": per_launch,
+            "avg_launch_us": round(avg_us, 2), "source_hash": src_hash}
+    cfg = {"workload": wl.name, "n_seqs": wl.n_seqs, "context": wl.n_ctx,
+           "new_tokens": wl.n_new, "query_rows_per_step": ctx["rows"],
+           "chunk": (wl.chunk or wl.n_new) if not decode else None,
+           "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "idx_heads": wl.hi, "idx_dim": wl.di,
+           "top_k": wl.top_k, "page_size": wl.page_size, "parallelism": "single-gpu"}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "n_seqs": wl.n_seqs, "context": wl.n_ctx,
-                   "query_rows": ctx["rows"], "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d,
-                   "idx_heads": wl.hi, "idx_dim": wl.di, "top_k": wl.top_k,
-                   "page_size": wl.page_size, "parallelism": "single-gpu"},
+        "dtype": wl.dtype, "data": "synthetic", "config": cfg,
         "roofline": roof,
-        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
-        "kernel_sum_us": round(sum(kern.values()), 2),
-        "dense_gqa": {"ms_per_step": round(dense_ms, 4),
-                      "speedup_sparse_over_dense": round(dense_ms / ms, 2)},
-        "cpu_baseline": cpu,
+        "kernels_us_per_step": {k: round(v, 2) for k, v in kern.items()},
     }
+    if not decode:
+        tk = work["topk"]
+        t_us = kern["topk"]
+        out["indexer_mfma"] = {"kernels": tk["kernel"], "flops_per_step": tk["flops"],
+                               "achieved_tflops": round(tk["flops"] / (t_us * 1e-6) / 1e12, 1),
+                               "peak_tflops": BF16_PEAK_TFLOPS,
+                               "frac": round(tk["flops"] / (t_us * 1e-6) / 1e12
+                                             / BF16_PEAK_TFLOPS, 4)}
+    if ctx["dense_ms"] is not None:
+        out["dense_gqa"] = {"ms_per_step": round(ctx["dense_ms"], 4),
+                            "speedup_sparse_over_dense": round(ctx["dense_ms"] / ms, 2),
+                            "how": ctx.get("dense_note", "")}
+        if "dense_tflops" in ctx:
+            out["dense_gqa"]["achieved_tflops"] = round(ctx["dense_tflops"], 1)
+    out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ctx)
     print(json.dumps(out), flush=True)
 
 

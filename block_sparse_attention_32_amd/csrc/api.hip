@@ -285,7 +285,10 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   const PidxPlan pp = pidx_plan(qm);
   const bool mfma = scores == nullptr && qm->n_rows >= kPMinRows &&
                     pidx_supported(c->dtype, c->idx_dim, n_idx_heads);
-  if (ws == nullptr || ws_bytes < (mfma ? pp.total : p.total)) return QSA_ERR_WORKSPACE;
+  // the documented size (qsa_workspace_size) covers both paths; anything
+  // smaller is rejected whichever path the call takes
+  const size_t need = p.total > pp.total ? p.total : pp.total;
+  if (ws == nullptr || ws_bytes < need) return QSA_ERR_WORKSPACE;
   if (qm->n_rows == 0) return QSA_OK;
   char* base = static_cast<char*>(ws);
   if (mfma) {
