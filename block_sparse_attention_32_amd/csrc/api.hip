@@ -208,7 +208,10 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
     a.part_ml = reinterpret_cast<float*>(base + p.off_ml);
     a.part_acc = reinterpret_cast<float*>(base + p.off_acc);
   }
-  if (p.mfma)
+  if (op == QSA_OP_DENSE_PREFILL &&
+      dense_flash_supported(c->dtype, hq, c->n_kv_heads, c->head_dim))
+    run_dense_flash(a, c->head_dim, qm->n_rows, as_stream(stream));
+  else if (p.mfma)
     run_attention_mfma(a, c->head_dim, dense, qm->n_rows, as_stream(stream));
   else
     run_attention(a, c->dtype, c->head_dim, dense, qm->n_rows, as_stream(stream));

@@ -68,4 +68,9 @@ constexpr int kVPitch = 272;        // LDS bytes per staged V row (256 + 16)
 bool attn_mfma_supported(int dtype, int hq, int hkv, int d);
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st);
 
+// Dense causal flash attention for many rows (dense_prefill.hip): bfloat16,
+// head_dim 64 or 128, Hq/Hkv dividing 16.
+bool dense_flash_supported(int dtype, int hq, int hkv, int d);
+void run_dense_flash(const AttnArgs& a, int d, int n_rows, hipStream_t st);
+
 }  // namespace qsa

@@ -1,0 +1,313 @@
+// Dense causal GQA flash attention for many query rows (the comparison
+// baseline of the sparse prefill; keieiax.jp glossary "Qwen Sparse
+// Attention", section 長文AIのコストと応答時間にどう影響する？: the reference
+// point is dense grouped-query attention).
+//
+// Same result as attn_mfma_kernel<D, true, false> (every token 0..pos of
+// the row's sequence, softmax(scale q.k) v, fp32 accumulation, round to
+// nearest-even), organised for many rows: a workgroup (8 waves) owns 256
+// query vectors -- (row, head) pairs of one KV head, G = Hq/Hkv heads per
+// row, so 256/G consecutive rows -- and walks the KV tokens 64 at a time.
+// Each 64-token tile of K (row-major) and V (transposed, dims x tokens) is
+// staged in LDS once for all 256 vectors, double-buffered: the next tile's
+// global loads are in flight while the current tile is computed.
+//
+// Per wave: 32 query vectors (two 16-column groups).
+//   S^T[64 tok x 16 vec] = K[64 x D] . Q^T       v_mfma_f32_16x16x32_bf16
+//     A = K rows from LDS, B = the query vectors held in registers
+//   O^T[D x 16 vec] += V^T[D x 64 tok] . P^T     v_mfma_f32_16x16x32_bf16
+//     B = the softmax numerators in the registers where S^T left them (the
+//     32 contraction slots of lane group g are tokens 4g..4g+3 of two
+//     16-token tiles, and V^T is read in that order)
+// Online softmax in log2 units; the sum of numerators is kept per lane
+// (four partial sums per column) and combined at the end.
+#include "attention.hpp"
+
+namespace qsa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kFTok = 64;                     // KV tokens per tile
+constexpr int kFNC = 2;                       // 16-vector column groups per wave
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * 64;
+constexpr int kFVec = kFWaves * kFNC * 16;    // query vectors per workgroup
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <int D>
+struct FGeom {
+  static constexpr int KS = D / 32;               // k steps of Q.K
+  static constexpr int NDT = D / 16;              // 16-dim tiles of the output
+  static constexpr int KPITCH = D * 2 + 16;       // bytes per staged K row
+  static constexpr int VPITCH = kFTok * 2 + 16;   // bytes per staged V^T row (one dim)
+  static constexpr int KBYTES = kFTok * KPITCH;
+  static constexpr int BUF = KBYTES + D * VPITCH; // one stage (K then V^T)
+  static constexpr int CPR = D / 8;               // 16-byte chunks per token row
+  static constexpr int CPT = kFTok * CPR / kFThreads;  // chunks per thread per tensor
+};
+
+struct FTile {
+  int32_t seq[kFVec];
+  int32_t pos[kFVec];
+  uint8_t done[kFVec];
+  uint8_t active[kFVec];
+  int cur_seq, kv_end, min_pos;
+};
+
+}  // namespace
+
+template <int D>
+__global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int n_rows) {
+  using Gm = FGeom<D>;
+  __shared__ __align__(16) unsigned char smem[2 * Gm::BUF];
+  __shared__ FTile ft;
+  const int G = a.hq / a.hkv;
+  const int TR = kFVec / G;  // rows per tile
+  // heaviest tiles (latest rows) first
+  const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;
+  const int hk = blockIdx.y;
+  const int r0 = tile * TR;
+  const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
+
+  for (int i = threadIdx.x; i < TR; i += blockDim.x) {
+    const int row = r0 + i;
+    const bool ok = row < n_rows;
+    ft.seq[i] = ok ? min(max(a.seq_id[row], 0), a.n_seqs - 1) : -1;
+    ft.pos[i] = ok ? min(max(a.pos[row], 0), a.max_pos) : -1;
+    ft.done[i] = ok ? 0 : 1;
+  }
+  __syncthreads();
+
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const int64_t rstride = (int64_t)a.hkv * D;
+  const bf16_t* kg = static_cast<const bf16_t*>(a.k) + hk * D;
+  const bf16_t* vg = static_cast<const bf16_t*>(a.v) + hk * D;
+
+  // rows of one sequence at a time (a tile normally holds one)
+  while (true) {
+    if (threadIdx.x == 0) {
+      int cur = -1;
+      for (int i = 0; i < TR; ++i)
+        if (!ft.done[i]) {
+          cur = ft.seq[i];
+          break;
+        }
+      int hi = -1, lo = 0x7fffffff;
+      for (int i = 0; i < TR; ++i) {
+        const bool act = cur >= 0 && !ft.done[i] && ft.seq[i] == cur;
+        ft.active[i] = act;
+        if (act) {
+          ft.done[i] = 1;
+          hi = max(hi, ft.pos[i]);
+          lo = min(lo, ft.pos[i]);
+        }
+      }
+      ft.cur_seq = cur;
+      ft.kv_end = hi + 1;
+      ft.min_pos = lo;
+    }
+    __syncthreads();
+    const int seq = ft.cur_seq;
+    if (seq < 0) break;
+    const int kv_end = ft.kv_end, min_pos = ft.min_pos;
+
+    // this lane's query columns: vector v = w*32 + c*16 + c16 -> (row, head)
+    u32x4_t qf[kFNC][Gm::KS];
+    int cpos[kFNC];
+#pragma unroll
+    for (int c = 0; c < kFNC; ++c) {
+      const int v = w * (kFNC * 16) + c * 16 + c16;
+      const int ri = v / G, hh = v % G;
+      const bool act = ri < TR && ft.active[ri];
+      cpos[c] = act ? ft.pos[ri] : -1;
+      const bf16_t* qp = static_cast<const bf16_t*>(a.q) +
+                         ((int64_t)(r0 + ri) * a.hq + hk * G + hh) * D + (D / 4) * g;
+#pragma unroll
+      for (int s = 0; s < Gm::KS; ++s)
+        qf[c][s] = act ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    float m[kFNC], lp[kFNC];
+    f32x4_t acc[kFNC][Gm::NDT];
+#pragma unroll
+    for (int c = 0; c < kFNC; ++c) {
+      m[c] = -INFINITY;
+      lp[c] = 0.0f;
+#pragma unroll
+      for (int n = 0; n < Gm::NDT; ++n) acc[c][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // staging: chunk ch = threadIdx.x + kFThreads i -> token ch / CPR, dims 8 (ch % CPR) ..
+    u32x4_t pk[Gm::CPT], pv[Gm::CPT];
+    auto fetch = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < Gm::CPT; ++i) {
+        const int ch = threadIdx.x + kFThreads * i;
+        const int j = t * kFTok + ch / Gm::CPR, part = ch % Gm::CPR;
+        pk[i] = u32x4_t{0u, 0u, 0u, 0u};
+        pv[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (j < kv_end) {
+          const int64_t slot = a.pm.token_slot(seq, j);
+          pk[i] = *reinterpret_cast<const u32x4_t*>(kg + slot * rstride + 8 * part);
+          pv[i] = *reinterpret_cast<const u32x4_t*>(vg + slot * rstride + 8 * part);
+        }
+      }
+    };
+    auto park = [&](unsigned char* buf) {
+      unsigned char* ks = buf;
+      unsigned char* vt = buf + Gm::KBYTES;
+#pragma unroll
+      for (int i = 0; i < Gm::CPT; ++i) {
+        const int ch = threadIdx.x + kFThreads * i;
+        const int jt = ch / Gm::CPR, part = ch % Gm::CPR;
+        *reinterpret_cast<u32x4_t*>(ks + jt * Gm::KPITCH + part * 16) = pk[i];
+        const uint32_t wv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(vt + (8 * part + e) * Gm::VPITCH + jt * 2) =
+              (uint16_t)(wv[e / 2] >> (16 * (e % 2)));
+      }
+    };
+
+    const int n_tiles = (kv_end + kFTok - 1) / kFTok;
+    fetch(0);
+    park(smem);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      unsigned char* buf = smem + (t & 1) * Gm::BUF;
+      if (t + 1 < n_tiles) fetch(t + 1);
+      const unsigned char* ks = buf;
+      const unsigned char* vt = buf + Gm::KBYTES;
+      // S^T: 4 token tiles x kFNC column groups
+      f32x4_t sc[kFNC][4];
+#pragma unroll
+      for (int c = 0; c < kFNC; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) sc[c][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int s = 0; s < Gm::KS; ++s) {
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+              ks + (16 * tt + c16) * Gm::KPITCH + ((D / 4) * g + 8 * s) * 2);
+#pragma unroll
+          for (int c = 0; c < kFNC; ++c) sc[c][tt] = mfma(kf, qf[c][s], sc[c][tt]);
+        }
+      }
+      // online softmax per column; tokens past a column's position (only
+      // in tiles that reach past the pass's smallest position) are masked
+      const int j0 = t * kFTok;
+      const bool need_mask = j0 + kFTok - 1 > min_pos;
+      u32x4_t pb[kFNC][2];
+      bool rescale = false;
+      float corr[kFNC];
+#pragma unroll
+      for (int c = 0; c < kFNC; ++c) {
+        // masked score of slot (tt, i): -inf past the column's position
+        auto score = [&](int tt, int i) {
+          const float v = sc[c][tt][i] * sl2;
+          return (need_mask && j0 + 16 * tt + 4 * g + i > cpos[c]) ? -INFINITY : v;
+        };
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, score(tt, i));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[c], mx);
+        const bool none = m_new == -INFINITY;  // nothing attended yet
+        corr[c] = none ? 1.0f : __builtin_amdgcn_exp2f(m[c] - m_new);
+        float ps = 0.0f;
+        uint32_t pw[8];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = none ? 0.0f : __builtin_amdgcn_exp2f(score(tt, i) - m_new);
+            const float p1 = none ? 0.0f : __builtin_amdgcn_exp2f(score(tt, i + 1) - m_new);
+            ps += p0 + p1;
+            pw[2 * tt + i / 2] = pack_bf16x2(p0, p1);
+          }
+        lp[c] = lp[c] * corr[c] + ps;
+        rescale |= corr[c] != 1.0f;
+        m[c] = m_new;
+        // k-slots of step kk: tokens 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          pb[c][kk] = u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
+      }
+      if (__ballot(rescale) != 0ull) {
+#pragma unroll
+        for (int c = 0; c < kFNC; ++c)
+#pragma unroll
+          for (int n = 0; n < Gm::NDT; ++n) acc[c][n] = acc[c][n] * corr[c];
+      }
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int n = 0; n < Gm::NDT; ++n) {
+        const unsigned char* vrow = vt + (16 * n + c16) * Gm::VPITCH;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * kk + 4 * g) * 2);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * kk + 16 + 4 * g) * 2);
+          const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int c = 0; c < kFNC; ++c) acc[c][n] = mfma(va, pb[c][kk], acc[c][n]);
+        }
+      }
+      if (t + 1 < n_tiles) park(smem + ((t + 1) & 1) * Gm::BUF);
+      __syncthreads();
+    }
+
+    // normalise and write: lane holds dims 16n + 4g + i of its column
+#pragma unroll
+    for (int c = 0; c < kFNC; ++c) {
+      float L = lp[c];
+      L += __shfl_xor(L, 16);
+      L += __shfl_xor(L, 32);
+      if (cpos[c] < 0) continue;
+      const int v = w * (kFNC * 16) + c * 16 + c16;
+      const int ri = v / G, hh = v % G;
+      bf16_t* o = static_cast<bf16_t*>(a.out) + ((int64_t)(r0 + ri) * a.hq + hk * G + hh) * D;
+      const float inv = 1.0f / L;
+#pragma unroll
+      for (int n = 0; n < Gm::NDT; ++n) {
+        const u32x2_t pr = {pack_bf16x2(acc[c][n][0] * inv, acc[c][n][1] * inv),
+                            pack_bf16x2(acc[c][n][2] * inv, acc[c][n][3] * inv)};
+        *reinterpret_cast<u32x2_t*>(o + 16 * n + 4 * g) = pr;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+bool dense_flash_supported(int dtype, int hq, int hkv, int d) {
+  if (dtype != QSA_BF16 || (d != 64 && d != 128)) return false;
+  if (hkv < 1 || hq % hkv != 0) return false;
+  const int G = hq / hkv;
+  return G <= 16 && 16 % G == 0;
+}
+
+void run_dense_flash(const AttnArgs& a, int d, int n_rows, hipStream_t st) {
+  const int G = a.hq / a.hkv;
+  const int tr = kFVec / G;
+  dim3 grid((unsigned)((n_rows + tr - 1) / tr), (unsigned)a.hkv);
+  if (d == 128)
+    hipLaunchKernelGGL(dense_flash_kernel<128>, grid, dim3(kFThreads), 0, st, a, n_rows);
+  else
+    hipLaunchKernelGGL(dense_flash_kernel<64>, grid, dim3(kFThreads), 0, st, a, n_rows);
+}
+
+}  // namespace qsa

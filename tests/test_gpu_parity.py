@@ -229,6 +229,30 @@ def test_dense_attention(gpu, mode):
         assert err <= TOL["bf16"], f"row {i} err={err}"
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (16, 4, 64), (8, 8, 128)])
+def test_dense_prefill_tiles(gpu, hq, hkv, d):
+    """Dense prefill (query-tiled flash kernel) over consecutive rows of two
+    sequences: a tile that spans the change of sequence, a ragged last
+    tile, rows at the very start of a sequence (one partly masked KV tile)
+    and rows deep into one (many KV tiles, masked only at the end)."""
+    _say(f"dense prefill tiles hq={hq} hkv={hkv} d={d}")
+    wl = MIXED.replace(n_ctx=3000, n_seqs=2, hq=hq, hkv=hkv, d=d)
+    seq_id = [0] * 70 + [1] * 45
+    pos = list(range(2930, 3000)) + list(range(0, 45))
+    pb = Problem(wl, gpu, seq_id, pos)
+    st = P.DenseStep(pb.cv, pb.rows, pb.qs.q, pb.wl.scale, "prefill")
+    st.out = torch.full_like(pb.qs.q, float("nan"))
+    st.run()
+    torch.cuda.synchronize()
+    got = f64(st.out)
+    worst = 0.0
+    for i in range(len(pos)):
+        err = np.abs(got[i] - pb.oracle_dense(i)).max()
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], f"row {i} (seq {seq_id[i]}, t={pos[i]}) err={err}"
+    _say(f"  max err {worst:.3g}")
+
+
 # ------------------------------------------------------------------ end to end
 
 def _e2e(pb, rows_to_check=None, mode=None):
