@@ -133,10 +133,11 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
   p.tile = p.mfma ? kMfmaTileTok : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
   const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
   if (split && p.mfma) {
-    // one 8-block tile per wave: 4 waves share a split across the KV heads;
-    // grow the split when rows x splits would exceed kMaxSplitWgs
+    // kMfmaSplitEnt entries per KV head and split (two tiles per wave at
+    // two waves per KV head); grow the split when rows x splits would
+    // exceed kMaxSplitWgs
     const int wph = 4 / c->n_kv_heads;
-    int eps = kMfmaTileEnt * wph;
+    int eps = kMfmaSplitEnt * wph / 2;
     while ((int64_t)rows * ((entries + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
     p.eps = eps;
     p.splits = (entries + eps - 1) / eps;

@@ -60,8 +60,9 @@ namespace qsa {
 
 // MFMA path (bfloat16, head_dim 64 or 128, up to 16 query heads per KV
 // head, 1, 2 or 4 KV heads): tile geometry.
-constexpr int kMfmaTileTok = 32;    // tokens per wave tile
-constexpr int kMfmaTileEnt = 8;     // token-list entries (blocks) per tile
+constexpr int kMfmaTileTok = 16;    // tokens per wave tile
+constexpr int kMfmaTileEnt = 4;     // token-list entries (blocks) per tile
+constexpr int kMfmaSplitEnt = 16;   // entries per split and KV head (split-K decode)
 constexpr int kMfmaEntChunk = 512;  // entries staged in LDS per pass
 constexpr int kVPitch = 272;        // LDS bytes per staged V row (256 + 16)
 

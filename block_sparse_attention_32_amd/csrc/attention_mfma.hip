@@ -3,16 +3,16 @@
 // Same computation as the generic kernel in attention.hip (the token set of
 // a row is its selected 4-token blocks plus its own block, read straight
 // from the paged cache, no mask; online softmax tile by tile), for bfloat16
-// caches.  A wave works on one KV head and 32 tokens at a time:
+// caches.  A wave works on one KV head and 16 tokens at a time, with the
+// next tile's K and V loads in flight while the current one is computed:
 //
-//   S^T[32 tok x 16 heads] = K[32 x D] . Q^T      v_mfma_f32_16x16x32_bf16
+//   S^T[16 tok x 16 heads] = K[16 x D] . Q^T      v_mfma_f32_16x16x32_bf16
 //     A = K rows loaded straight from the cache (16 B per lane per step),
 //     B = the group's query heads (padded to 16) held in registers.
-//   O^T[D x 16 heads] += V^T[D x 32 tok] . P^T     v_mfma_f32_16x16x32_bf16
+//   O^T[D x 16 heads] += V^T[D x 16 tok] . P^T     v_mfma_f32_16x16x16_bf16
 //     B = the softmax numerators, used in the registers where S^T left
-//     them: the token order inside the 32-wide contraction is chosen so
-//     that lane l's eight k-slots are exactly the eight tokens whose scores
-//     lane l holds; A = V^T read from an LDS copy of the tile's V rows.
+//     them (lane group g holds tokens 4g..4g+3, which are its four
+//     k-slots); A = V^T read from an LDS copy of the tile's V rows.
 //
 // Workgroups: 4 waves per (row, split).  With n_splits > 1 (the SPLIT
 // instances) the split partials go to the workspace and the last split of
@@ -32,9 +32,28 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// O^T step on 16 tokens: 16x16x16 bf16, k-slot 4g + i of lane group g
+__device__ __forceinline__ f32x4_t mfma16k16(u32x2_t a, u32x2_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bfloat16 pair, round to nearest even
+// (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+// A column's reference maximum only moves when a new score exceeds it by
+// more than this (log2 units): numerators stay below 2^kSlack, and the
+// accumulator is rescaled rarely.  Numerators and their sum use the same
+// reference, so the result does not depend on it.
+constexpr float kSlack = 8.0f;
 
 // Split partials of a row, [split][head] x (D floats of unnormalised acc,
 // then (m in log2 units, l)), are written and merged by 256 threads that
@@ -125,7 +144,9 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
   __shared__ int32_t ent_row[kMfmaEntChunk];
-  __shared__ __align__(16) unsigned char lds[4 * kMfmaTileTok * kVPitch];
+  constexpr int kStage = 4 * kMfmaTileTok * kVPitch;   // per-wave V tiles
+  constexpr int kMerge = 4 * 16 * (D + 2) * 4;         // per-wave results
+  __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
   __shared__ uint32_t flag;
   const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
   const int hkv = a.hkv, hq = a.hq, G = hq / hkv;
@@ -146,16 +167,17 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   const bf16_t* kg = static_cast<const bf16_t*>(a.k) + hk * D;
   const bf16_t* vg = static_cast<const bf16_t*>(a.v) + hk * D;
   const int64_t rstride = (int64_t)hkv * D;
+  const int64_t own_row = a.pm.token_slot(seq, b_own * kBlock);  // always present
 
-  // this lane's B fragment of Q^T: head c16 of the group, dims (D/4)g+8s..+8
-  // (lane group g covers the contiguous quarter (D/4)g .. (D/4)(g+1) of the
-  // head dimension across the KS steps; K uses the same order)
+  // this lane's B fragment of Q^T: head c16 of the group, dims 32s + 8g .. +8
+  // at step s (K uses the same order, so one load instruction reads 64
+  // contiguous bytes of each token row)
   u32x4_t qf[KS];
   {
     const bf16_t* qh = static_cast<const bf16_t*>(a.q) + ((int64_t)row * hq + hk * G + c16) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[s] = (c16 < G) ? ld16(qh + (D / 4) * g + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+      qf[s] = (c16 < G) ? ld16(qh + 32 * s + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
   }
   const float sl2 = a.scale * 1.4426950408889634f;  // scores in log2 units
   float m = -INFINITY, lsum = 0.0f;
@@ -176,95 +198,112 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
     const int n_tiles = (nloc + kMfmaTileEnt - 1) / kMfmaTileEnt;
-    for (int tile = wsub; tile < n_tiles; tile += wph) {
+    // A tile is 16 tokens (4 entries).  The K fragments (A operand: token
+    // c16, dims 32s + 8g) and the V rows (token g + 4i, 16-byte chunk
+    // c16) of the wave's next tile are loaded while the current one is
+    // computed.
+    //
+    // Loads are unconditional (straight-line code keeps the prefetch in
+    // flight): a token that is not attended -- past the own block's tail,
+    // or of an invalid list entry -- is read from the row's own first
+    // token instead, which is always in the cache; its score is masked to
+    // -inf and its numerator is 0, so it contributes nothing.
+    auto load_tile = [&](int tile, u32x4_t (&kf)[KS], u32x4_t (&vf)[4]) {
       const int e0 = tile * kMfmaTileEnt;
-      // K fragments: tokens 16*st + c16 of the tile, dims (D/4)g .. +D/4
-      u32x4_t kf[2][KS];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int tau = 16 * st + c16, el = e0 + tau / 4, ti = tau % 4;
+      {
+        const int el = e0 + c16 / 4, ti = c16 % 4;
         const int r0 = el < nloc ? ent_row[el] : -1;
         const bool ok = r0 >= 0 && ti < ((cb + el == n_list) ? tail : kBlock);
-        const bf16_t* p = kg + (int64_t)(r0 + ti) * rstride + (D / 4) * g;
+        const bf16_t* p = kg + (ok ? (int64_t)(r0 + ti) : own_row) * rstride + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[st][s] = ok ? ld16(p + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int s2 = 0; s2 < KS; ++s2) kf[s2] = ld16(p + 32 * s2);
       }
-      // V rows of the tile: token g + 4i, 16-byte chunk c16 (c16 < D/8)
-      u32x4_t vf[8];
+      const int cv = c16 < D / 8 ? c16 : 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int tau = g + 4 * i, el = e0 + tau / 4, ti = tau % 4;
         const int r0 = el < nloc ? ent_row[el] : -1;
-        const bool ok = c16 < D / 8 && r0 >= 0 && ti < ((cb + el == n_list) ? tail : kBlock);
-        vf[i] = ok ? ld16(vg + (int64_t)(r0 + ti) * rstride + 8 * c16) : u32x4_t{0u, 0u, 0u, 0u};
+        const bool ok = r0 >= 0 && ti < ((cb + el == n_list) ? tail : kBlock);
+        vf[i] = ld16(vg + (ok ? (int64_t)(r0 + ti) : own_row) * rstride + 8 * cv);
       }
-      // S^T: lane holds tokens 16*st + 4g + r for head c16
-      f32x4_t sc[2];
+    };
+    // one tile: S^T, online softmax, O^T update
+    auto compute = [&](int tile, const u32x4_t (&kf)[KS], const u32x4_t (&vf)[4]) {
+      const int e0 = tile * kMfmaTileEnt;
+      // S^T: lane holds tokens 4g + r (entry e0 + g) for head c16
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        sc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sc[st] = mfma16(kf[st][s], qf[s], sc[st]);
-      }
+      for (int s2 = 0; s2 < KS; ++s2) sc = mfma16(kf[s2], qf[s2], sc);
       if (c16 < D / 8) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
           *reinterpret_cast<u32x4_t*>(vs + (g + 4 * i) * kVPitch + 16 * c16) = vf[i];
       }
-      // online softmax (log2 domain)
-      float x[8];
+      float x[4];
       float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int el = e0 + 4 * st + g;  // entry of tokens 16*st + 4g .. +3
+      {
+        const int el = e0 + g;
         const int r0 = el < nloc ? ent_row[el] : -1;
         const int nt = r0 < 0 ? 0 : ((cb + el == n_list) ? tail : kBlock);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = r < nt ? sc[st][r] * sl2 : -INFINITY;
-          x[4 * st + r] = v;
+          const float v = r < nt ? sc[r] * sl2 : -INFINITY;
+          x[r] = v;
           mx = fmaxf(mx, v);
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      float corr = 1.0f, psum = 0.0f;
-      float p[8];
-      if (m_new == -INFINITY) {
+      // move the reference maximum (and rescale) only when some column
+      // needs it
+      const bool grow = mx > m + kSlack;
+      if (__ballot(grow) != 0ull) {
+        const float m_new = grow ? mx : m;
+        const float corr = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+        lsum *= corr;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = 0.0f;
-      } else {
-        corr = __builtin_amdgcn_exp2f(m - m_new);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
-          psum += p[j];
-        }
+        for (int n = 0; n < NDT; ++n) acc[n] = acc[n] * corr;
+        m = m_new;
       }
-      lsum = lsum * corr + psum;
-      m = m_new;
-      const u32x4_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                          pack_bf16(p[6], p[7])};
+      float p[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // m is -inf only while every score so far was masked (then x is too)
+        p[j] = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m);
+        psum += p[j];
+      }
+      lsum += psum;
+      const u32x2_t pb = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      // O^T += V^T . P^T; k-slot j of lane group g is token 4g + j (j < 4)
-      // or 16 + 4g + (j - 4)
+      // O^T += V^T . P^T; k-slot i of lane group g is token 4g + i
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {
         const unsigned char* col = vs + 2 * (16 * n + c16);
-        uint32_t h[8];
+        uint32_t h[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tok = (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4);
-          h[j] = *reinterpret_cast<const uint16_t*>(col + tok * kVPitch);
-        }
-        const u32x4_t va = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                            h[6] | (h[7] << 16)};
-        acc[n] = acc[n] * corr;
-        acc[n] = mfma16(va, pb, acc[n]);
+        for (int j = 0; j < 4; ++j)
+          h[j] = *reinterpret_cast<const uint16_t*>(col + (4 * g + j) * kVPitch);
+        const u32x2_t va = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        acc[n] = mfma16k16(va, pb, acc[n]);
       }
       __builtin_amdgcn_wave_barrier();
+    };
+    // two register sets alternate: the loads of the wave's next tile go to
+    // the set not being computed (the last tile reloads itself, so every
+    // step issues the same loads and the wait before a product covers only
+    // the current tile's)
+    u32x4_t ka[KS], va4[4], kb[KS], vb4[4];
+    if (wsub < n_tiles) load_tile(wsub, ka, va4);
+    for (int tile = wsub; tile < n_tiles; tile += 2 * wph) {
+      const int t1 = tile + wph;
+      load_tile(t1 < n_tiles ? t1 : tile, kb, vb4);
+      compute(tile, ka, va4);
+      if (t1 >= n_tiles) break;
+      const int t2 = t1 + wph;
+      load_tile(t2 < n_tiles ? t2 : t1, ka, va4);
+      compute(t1, kb, vb4);
     }
   }
   lsum += __shfl_xor(lsum, 16);
