@@ -143,7 +143,10 @@ template <int D, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
-  __shared__ int32_t ent_row[kMfmaEntChunk];
+  // per list entry: element offset of its first token's row (a multiple of
+  // Hkv*D >= 32) with the number of its tokens to attend (0..4) in the low
+  // bits; padded to whole tiles with empty entries
+  __shared__ int64_t ent_off[kMfmaEntChunk];
   constexpr int kStage = 4 * kMfmaTileTok * kVPitch;   // per-wave V tiles
   constexpr int kMerge = 4 * 16 * (D + 2) * 4;         // per-wave results
   __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
@@ -168,6 +171,9 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   const bf16_t* vg = static_cast<const bf16_t*>(a.v) + hk * D;
   const int64_t rstride = (int64_t)hkv * D;
   const int64_t own_row = a.pm.token_slot(seq, b_own * kBlock);  // always present
+  const int64_t own_off = own_row * rstride;
+  const int64_t k_ti = (c16 % 4) * rstride;  // K: token c16 % 4 of an entry
+  const int64_t v_ti = g * rstride;          // V: token g of an entry
 
   // this lane's B fragment of Q^T: head c16 of the group, dims 32s + 8g .. +8
   // at step s (K uses the same order, so one load instruction reads 64
@@ -189,12 +195,14 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
   for (int cb = e_beg; cb < e_end; cb += kMfmaEntChunk) {
     const int nloc = min(e_end, cb + kMfmaEntChunk) - cb;
     __syncthreads();
-    for (int i = threadIdx.x; i < nloc; i += blockDim.x) {
+    const int npad = (nloc + kMfmaTileEnt - 1) / kMfmaTileEnt * kMfmaTileEnt;
+    for (int i = threadIdx.x; i < npad; i += blockDim.x) {
       const int E = cb + i;
       const bool own = (E == n_list);
-      const int b = own ? b_own : (DENSE ? E : sel_row[E]);
-      const bool ok = own || (b >= 0 && b < b_own);
-      ent_row[i] = ok ? (int32_t)a.pm.token_slot(seq, b * kBlock) : -1;
+      const int b = i >= nloc ? -1 : (own ? b_own : (DENSE ? E : sel_row[E]));
+      const bool ok = i < nloc && (own || (b >= 0 && b < b_own));
+      ent_off[i] = ok ? (a.pm.token_slot(seq, b * kBlock) * rstride) | (own ? tail : kBlock)
+                      : own_row * rstride;
     }
     __syncthreads();
     const int n_tiles = (nloc + kMfmaTileEnt - 1) / kMfmaTileEnt;
@@ -211,20 +219,18 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
     auto load_tile = [&](int tile, u32x4_t (&kf)[KS], u32x4_t (&vf)[4]) {
       const int e0 = tile * kMfmaTileEnt;
       {
-        const int el = e0 + c16 / 4, ti = c16 % 4;
-        const int r0 = el < nloc ? ent_row[el] : -1;
-        const bool ok = r0 >= 0 && ti < ((cb + el == n_list) ? tail : kBlock);
-        const bf16_t* p = kg + (ok ? (int64_t)(r0 + ti) : own_row) * rstride + 8 * g;
+        const int64_t v = ent_off[e0 + c16 / 4];
+        const int64_t off = (c16 % 4) < (int)(v & 7) ? (v & ~7ll) + k_ti : own_off;
+        const bf16_t* p = kg + off + 8 * g;
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) kf[s2] = ld16(p + 32 * s2);
       }
       const int cv = c16 < D / 8 ? c16 : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tau = g + 4 * i, el = e0 + tau / 4, ti = tau % 4;
-        const int r0 = el < nloc ? ent_row[el] : -1;
-        const bool ok = r0 >= 0 && ti < ((cb + el == n_list) ? tail : kBlock);
-        vf[i] = ld16(vg + (ok ? (int64_t)(r0 + ti) : own_row) * rstride + 8 * cv);
+        const int64_t v = ent_off[e0 + i];
+        const int64_t off = g < (int)(v & 7) ? (v & ~7ll) + v_ti : own_off;
+        vf[i] = ld16(vg + off + 8 * cv);
       }
     };
     // one tile: S^T, online softmax, O^T update
@@ -242,9 +248,7 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
       float x[4];
       float mx = -INFINITY;
       {
-        const int el = e0 + g;
-        const int r0 = el < nloc ? ent_row[el] : -1;
-        const int nt = r0 < 0 ? 0 : ((cb + el == n_list) ? tail : kBlock);
+        const int nt = (int)(ent_off[e0 + g] & 7);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = r < nt ? sc[r] * sl2 : -INFINITY;

@@ -42,9 +42,16 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bfloat16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+// A column's reference maximum only moves when a score exceeds it by more
+// than this (log2 units); numerators stay below 2^kSlack and share the
+// reference with their sum, so the result does not depend on it.
+constexpr float kSlack = 8.0f;
 
 template <int D>
 struct FGeom {
@@ -226,9 +233,13 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, score(tt, i));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[c], mx);
+        const bool grow = mx > m[c] + kSlack;
+        const float m_new = grow ? mx : m[c];
+        corr[c] = (!grow || m[c] == -INFINITY) ? (grow ? 0.0f : 1.0f)
+                                                : __builtin_amdgcn_exp2f(m[c] - m_new);
+        rescale |= grow;
+        m[c] = m_new;
         const bool none = m_new == -INFINITY;  // nothing attended yet
-        corr[c] = none ? 1.0f : __builtin_amdgcn_exp2f(m[c] - m_new);
         float ps = 0.0f;
         uint32_t pw[8];
 #pragma unroll
@@ -241,8 +252,6 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
             pw[2 * tt + i / 2] = pack_bf16x2(p0, p1);
           }
         lp[c] = lp[c] * corr[c] + ps;
-        rescale |= corr[c] != 1.0f;
-        m[c] = m_new;
         // k-slots of step kk: tokens 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
