@@ -20,14 +20,15 @@
 // Exact top-k in four launches per batch of rows:
 //   P1  sampled groups only (every s-th): for each (query, lane) the largest
 //       key of the group -> the row's "union" of group maxima;
-//   P2  per row: tau = k-th largest union key.  Every union key is a key of
-//       the row and at least k keys are >= tau, so tau is at most the row's
-//       k-th largest key (a lower bound; keys 0 pad missing entries);
+//   P2  per row: tau = the k'-th largest union key, k' = ceil(1.5 k / s)
+//       (k' = k without sampling: then tau is a lower bound of the k-th
+//       key; with sampling about 1.5 k keys reach it);
 //   P3  all groups: keys >= tau (the survivors) appended per (row, split) in
 //       block order;
 //   P4  per row: survivors gathered in block order -> exact radix select and
 //       ordered emission (select.hpp); a row whose survivors overflowed its
-//       slots falls back to an exact select over recomputed keys.
+//       slots, or number fewer than k, falls back to an exact select over
+//       recomputed keys.
 #include <type_traits>
 
 #include "index.hpp"
@@ -324,7 +325,13 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
   if (threadIdx.x == 0) a.tile_stride[tile] = pass_stride(lo, a.top_k);
 }
 
-// P2: tau per row from its union of group maxima.
+// P2: tau per row from its union of group maxima: the k'-th largest union
+// key, k' = ceil(1.5 k / s) for sampling stride s (k' = k when every group
+// was sampled).  Each union key is a distinct key of the row, so at least
+// k' keys are >= tau; the unsampled groups hold about (s - 1) times as many
+// again, so about 1.5 k keys survive.  For s = 1 this is a guaranteed lower
+// bound of the k-th key; otherwise P4 checks that at least k keys survived
+// and falls back to an exact select when they did not.
 __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
   __shared__ uint32_t u[kPUnion];
   __shared__ SelShared sh;
@@ -334,13 +341,14 @@ __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
   const int s = a.row_stride[rl];
   const int n_groups = (n + kPGrp - 1) / kPGrp;
   const int un = min(kPUnion, ((n_groups + s - 1) / s) * 16);
+  const int kq = s == 1 ? a.top_k : max(1, min(a.top_k, (3 * a.top_k + 2 * s - 1) / (2 * s)));
   const uint32_t* src = a.uni + (int64_t)rl * kPUnion;
   for (int e = threadIdx.x; e < un; e += blockDim.x) u[e] = src[e];
   __syncthreads();
   uint32_t tau = 0u;
-  if (un >= a.top_k) {
+  if (un >= kq) {
     int r;
-    radix_kth(KeyArrayL{u}, un, a.top_k, sh, tau, r);
+    radix_kth(KeyArrayL{u}, un, kq, sh, tau, r);
   }
   if (threadIdx.x == 0) a.tau[rl] = tau;
 }
@@ -416,8 +424,8 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
     radix_kth(KeyArrayL{ck}, (int)m, a.top_k, sh, thr, r);
     emit_topk(KeyArrayL{ck}, IdArrayL{ci}, (int)m, thr, r, sel_row, a.top_k, sh);
   } else {
-    // survivors overflowed their slots (or fewer than k, which a valid tau
-    // excludes): exact select over every candidate
+    // survivors overflowed their slots, or the sampled threshold kept fewer
+    // than k: exact select over every candidate
     const PRecomputed<DI> get{&a, row, a.idx.seq_of(row)};
     uint32_t thr;
     int r;

@@ -178,6 +178,36 @@ def test_topk_all_scores_equal(gpu, fused, rows):
         assert np.all(sel[i, m:] == -1)
 
 
+def test_topk_sampled_threshold_short(gpu):
+    """Many rows (matrix-core indexer) at 131,072 candidates, where the
+    indexer samples every 8th group of 256 blocks for its threshold.  High
+    blocks are planted only in 6 sampled groups, one per column of 16: the
+    sampled threshold then admits only those 96 blocks, fewer than k, and
+    the rows must take the exact fallback.  Selection must still equal the
+    oracle's."""
+    _say("sampled threshold below k")
+    t = 131072 * 4
+    pos = [t] * 64
+    pb = Problem(MIXED.replace(n_ctx=t, n_needles=0, permute_pages=False), gpu,
+                 [0] * len(pos), pos)
+    wl = pb.wl
+    val = (3.0 * pb.cache.direction[0]).to(pb.cache.kidx.dtype)
+    for grp in range(0, 6 * 8, 8):          # sampled groups 0, 8, .., 40
+        for c in range(16):                 # one block per column
+            b = grp * 256 + 16 * c + c
+            for j in range(4):
+                tok = 4 * b + j
+                page = int(pb.cache.block_table[0, tok // wl.page_size])
+                pb.cache.kidx[page, tok % wl.page_size] = val
+    pb.pool_all()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, 512, pb.wl.scale)
+    st.select()
+    torch.cuda.synchronize()
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    for i in (0, 17, 63):
+        assert_sel_row(sel[i], int(n[i]), pb.oracle_select(i), 512)
+
+
 # ------------------------------------------------------------------ attention
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
