@@ -302,6 +302,42 @@ def _e2e(pb, rows_to_check=None, mode=None):
     return st, worst
 
 
+SHAPES = {
+    # name: (dtype, page_size, hq, hkv, d, hi, di)
+    "p16-h16/2-d128-i4x64": ("bf16", 16, 16, 2, 128, 4, 64),
+    "p256-h8/1-d64-i2x128": ("bf16", 256, 8, 1, 64, 2, 128),
+    "p64-h12/2-d128-i3x64": ("bf16", 64, 12, 2, 128, 3, 64),
+    "p32-h16/4-d64-i8x32": ("bf16", 32, 16, 4, 64, 8, 32),
+    "f32-p64-h8/2-d64-i4x64": ("f32", 64, 8, 2, 64, 4, 64),
+}
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+def test_e2e_shapes(gpu, shape, mode):
+    """End to end over the shapes the library accepts beyond the benchmark
+    configs: page sizes 16..256, GQA groups of 1..8 heads (6 included),
+    head_dim 64/128, 2..8 indexer heads of dim 32..128, float32.  Rows of two
+    sequences (permuted pages) at positions from 0 to past 5,000 blocks;
+    the prefill case uses 80 rows so that the matrix-core indexer runs where
+    the shape allows it."""
+    dt, page, hq, hkv, d, hi, di = SHAPES[shape]
+    _say(f"e2e shape {shape} {mode}")
+    wl = MIXED.replace(name=shape, dtype=dt, page_size=page, hq=hq, hkv=hkv, d=d, hi=hi,
+                       di=di, n_ctx=22000, n_seqs=2, n_needles=4, permute_pages=True,
+                       seed=91)
+    if mode == "decode":
+        pos = [21999, 5, 2051, 20000]
+        seq_id = [0, 1, 1, 1]
+    else:
+        pos = [int(x) for x in np.linspace(0, 21999, 60)] + list(range(2040, 2060))
+        seq_id = [i % 2 for i in range(len(pos))]
+    pb = Problem(wl, gpu, seq_id, pos)
+    pb.pool_all()
+    _, worst = _e2e(pb, mode=mode)
+    _say(f"  max err {worst:.3g}")
+
+
 @pytest.mark.parametrize("name", ["tiny_decode", "decode_8x32k", "decode_1m"])
 def test_e2e_decode_configs(gpu, name):
     _say(f"e2e {name}")
