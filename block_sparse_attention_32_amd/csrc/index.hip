@@ -333,6 +333,68 @@ __device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row, 
 // select.hpp picks the k best with ties to the lower id.
 constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
 
+// Survivors (key >= tau) of the published runs of a long row, placed in
+// ascending-id order into skey/sid.  Thread t owns union entries
+// [16t, 16t + 16): whole runs of JW entries (a run lists one wave's keys
+// best first).  A saturated run (sat_of != 0xff) counts its rescanned
+// survivors and records its first place in sat_off; its keys are placed
+// later.  Everything between the loads and the stores is in registers.
+template <int JW>
+__device__ void place_runs(const uint32_t* ukey, const int32_t* uid, int un, uint32_t tau,
+                           const uint8_t* sat_of, const uint32_t* sat_cnt, uint32_t* sat_off,
+                           uint32_t* skey, int32_t* sid, bool& fits, uint32_t& m_total,
+                           SelShared& sh) {
+  constexpr int E = kUnionCap / kSelThreads;
+  constexpr int R = E / JW;
+  const int e0 = (int)threadIdx.x * E;
+  uint32_t k[E];
+  int32_t id[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    k[i] = e0 + i < un ? ukey[e0 + i] : 0u;
+    id[i] = e0 + i < un ? uid[e0 + i] : 0;
+  }
+  uint32_t cnt[R];
+  int si[R];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    si[r] = e0 + r * JW < un ? (int)sat_of[e0 / JW + r] : 0xff;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < JW; ++j) c += (k[r * JW + j] >= tau && k[r * JW + j] != 0u) ? 1u : 0u;
+    cnt[r] = si[r] != 0xff ? sat_cnt[si[r]] : c;
+    mine += cnt[r];
+  }
+  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
+  fits = fits && m_total <= (uint32_t)kSelCap;
+  if (!fits) return;  // uniform: m_total is the workgroup total
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (si[r] != 0xff) {
+      sat_off[si[r]] = off;
+    } else {
+#pragma unroll
+      for (int i = 0; i < JW; ++i) {
+        const uint32_t ki = k[r * JW + i];
+        if (ki >= tau && ki != 0u) {
+          uint32_t rank = 0;
+#pragma unroll
+          for (int j = 0; j < JW; ++j) {
+            const uint32_t kj = k[r * JW + j];
+            rank += (kj >= tau && kj != 0u && id[r * JW + j] < id[r * JW + i]) ? 1u : 0u;
+          }
+          skey[off + rank] = ki;
+          sid[off + rank] = id[r * JW + i];
+        }
+      }
+    }
+    off += cnt[r];
+  }
+}
+
+
+
 // Exact top-k of n <= kDirectCap keys read from keys[0..n) (global memory
 // or LDS), every key held in registers.
 __device__ void select_direct(const uint32_t* keys, int n, int top_k, int32_t* sel_row,
@@ -484,60 +546,14 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
       sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
     __syncthreads();
   }
-  // runs (waves) owned by this thread: [w0, w1).  The survivors of an
-  // unsaturated run are its leading entries with key >= tau (a run lists
-  // its keys best first, key 0 = nothing left).
-  const int q = (nw + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(nw, (int)threadIdx.x * q), w1 = min(nw, w0 + q);
-  auto run_survivors = [&](int gw) {
-    int c2 = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxJw; ++j)
-      if (j < jw) {
-        const uint32_t k = ukey[gw * jw + j];
-        c2 += (k >= tau && k != 0u) ? 1 : 0;
-      }
-    return c2;
-  };
-  uint32_t mine = 0;
-#pragma unroll 1
-  for (int gw = w0; gw < w1; ++gw) {
-    const int si = sat_of[gw];
-    mine += (si != 0xff) ? sat_cnt[si] : (uint32_t)run_survivors(gw);
-  }
-  uint32_t m_total;
-  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
-  fits = fits && m_total <= (uint32_t)kSelCap;
-  if (fits) {
-#pragma unroll 1
-    for (int gw = w0; gw < w1; ++gw) {
-      const int si = sat_of[gw];
-      if (si != 0xff) {
-        sat_off[si] = off;
-        off += sat_cnt[si];
-        continue;
-      }
-      // the run's survivors, best first, go to ascending-id places
-      uint32_t rk[kMaxJw];
-      int32_t ri[kMaxJw];
-      int c2 = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxJw; ++j) {
-        rk[j] = j < jw ? ukey[gw * jw + j] : 0u;
-        ri[j] = j < jw ? uid[gw * jw + j] : 0;
-        c2 += (rk[j] >= tau && rk[j] != 0u) ? 1 : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxJw; ++i) {
-        if (i >= c2) break;
-        uint32_t rank = 0;
-#pragma unroll
-        for (int j = 0; j < kMaxJw; ++j) rank += (j < c2 && ri[j] < ri[i]) ? 1u : 0u;
-        skey[off + rank] = rk[i];
-        sid[off + rank] = ri[i];
-      }
-      off += (uint32_t)c2;
-    }
+  // survivors of the unsaturated runs placed, saturated runs' places reserved
+  uint32_t m_total = 0;
+  switch (jw) {
+    case 1: place_runs<1>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
+    case 2: place_runs<2>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
+    case 4: place_runs<4>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
+    case 8: place_runs<8>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
+    default: place_runs<16>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
   }
   __syncthreads();
   // survivors of saturated runs, in id order (whole workgroup per run)
