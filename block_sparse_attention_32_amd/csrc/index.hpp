@@ -83,6 +83,7 @@ constexpr int kPThreads = 512;    // threads of a scoring workgroup
 constexpr int kPGrp = 256;        // pooled keys staged per group
 constexpr int kPUnion = 4096;     // union entries (group maxima) per row
 constexpr int kPSurvCap = 8192;   // survivor slots per row, over all splits
+constexpr int kPSelCap = 8192;    // survivors a row's exact select stages in LDS
 constexpr int kPMaxStride = 8;    // largest group sampling stride of P1
 constexpr int kPMaxSplits = 16;   // block splits per tile
 constexpr int kPMinRows = 64;     // fused top-k of at least this many rows uses it
@@ -96,7 +97,7 @@ struct PIdxArgs {
   uint32_t* tau;             // [rows] lower bound of the k-th key (P2)
   int32_t* tile_stride;      // [tiles] sampling stride of P1
   int32_t* row_stride;       // [rows] stride used for each row's union
-  uint64_t* surv;            // [rows][splits][kPSurvCap / splits] (block << 32 | key)
+  uint64_t* surv;            // [rows][splits][kPSurvCap / splits] (block << 32 | score bits)
   uint32_t* surv_cnt;        // [rows][splits]
   int32_t* sel;
   int32_t* n_sel;

@@ -23,8 +23,8 @@
 //   P2  per row: tau = the k'-th largest union key, k' = ceil(1.5 k / s)
 //       (k' = k without sampling: then tau is a lower bound of the k-th
 //       key; with sampling about 1.5 k keys reach it);
-//   P3  all groups: keys >= tau (the survivors) appended per (row, split) in
-//       block order;
+//   P3  all groups: keys >= tau (the survivors; stored as block id and
+//       score bits) appended per (row, split) in block order;
 //   P4  per row: survivors gathered in block order -> exact radix select and
 //       ordered emission (select.hpp); a row whose survivors overflowed its
 //       slots, or number fewer than k, falls back to an exact select over
@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
                 if (sv && pos < (uint32_t)region) {
                   const int rl = tile * kPQT + w * (4 * AT) + at * 4 + g;
                   a.surv[((int64_t)rl * a.splits + split) * region + pos] =
-                      ((uint64_t)(uint32_t)b << 32) | ordered_key(sc);
+                      ((uint64_t)(uint32_t)b << 32) | __float_as_uint(sc);
                 }
                 run[at] += (uint32_t)__popcll(gm);
               }
@@ -382,8 +382,8 @@ struct IdArrayL {
 // P4: gather, exact select, ordered emission.
 template <int DI>
 __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
-  __shared__ uint32_t ck[kPSurvCap];
-  __shared__ int32_t ci[kPSurvCap];
+  __shared__ uint32_t ck[kPSelCap];
+  __shared__ int32_t ci[kPSelCap];
   __shared__ uint32_t offs[kPMaxSplits + 1];
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
       offs[sp] = o;
       o += c;
     }
-    offs[a.splits] = over ? 0xffffffffu : o;
+    offs[a.splits] = (over || o > (uint32_t)kPSelCap) ? 0xffffffffu : o;
   }
   __syncthreads();
   const uint32_t m = offs[a.splits];
@@ -413,8 +413,8 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
       const uint32_t cnt = ((sp + 1 < a.splits) ? offs[sp + 1] : m) - offs[sp];
       const uint64_t* src = a.surv + ((int64_t)rl * a.splits + sp) * region;
       for (uint32_t i = threadIdx.x; i < cnt; i += blockDim.x) {
-        const uint64_t v = src[i];
-        ck[offs[sp] + i] = (uint32_t)v;
+        const uint64_t v = src[i];  // (block << 32) | score bits
+        ck[offs[sp] + i] = ordered_key(__uint_as_float((uint32_t)v));
         ci[offs[sp] + i] = (int32_t)(v >> 32);
       }
     }
@@ -424,8 +424,8 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
     radix_kth(KeyArrayL{ck}, (int)m, a.top_k, sh, thr, r);
     emit_topk(KeyArrayL{ck}, IdArrayL{ci}, (int)m, thr, r, sel_row, a.top_k, sh);
   } else {
-    // survivors overflowed their slots, or the sampled threshold kept fewer
-    // than k: exact select over every candidate
+    // survivors overflowed their slots or the select's LDS, or the sampled
+    // threshold kept fewer than k: exact select over every candidate
     const PRecomputed<DI> get{&a, row, a.idx.seq_of(row)};
     uint32_t thr;
     int r;
