@@ -21,6 +21,8 @@
 //     16-token tiles, and V^T is read in that order)
 // Online softmax in log2 units; the sum of numerators is kept per lane
 // (four partial sums per column) and combined at the end.
+#include <type_traits>
+
 #include "attention.hpp"
 
 namespace qsa {
@@ -155,20 +157,33 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
       for (int n = 0; n < Gm::NDT; ++n) acc[c][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // staging: chunk ch = threadIdx.x + kFThreads i -> token ch / CPR, dims 8 (ch % CPR) ..
+    // staging.  K: chunk ch = threadIdx.x + kFThreads i -> token ch / CPR,
+    // dims 8 (ch % CPR) .. (a wave reads whole rows).  V: lane l of wave w
+    // -> token l, dims 8 (w + 8 i) .. , so that the transposed LDS writes of
+    // a wave go to 64 consecutive tokens of one dim row (no bank conflicts).
+    // A tile's token rows come from one page lookup when pages hold whole
+    // tiles, else one per token.
+    const bool page_tiles = a.pm.page_shift >= 6;
     u32x4_t pk[Gm::CPT], pv[Gm::CPT];
     auto fetch = [&](int t) {
+      const int j0 = t * kFTok;
+      const int64_t base = page_tiles ? a.pm.token_slot(seq, j0) : 0;
+      auto slot_of = [&](int j) {
+        return page_tiles ? base + (j - j0) : a.pm.token_slot(seq, j);
+      };
 #pragma unroll
       for (int i = 0; i < Gm::CPT; ++i) {
         const int ch = threadIdx.x + kFThreads * i;
-        const int j = t * kFTok + ch / Gm::CPR, part = ch % Gm::CPR;
+        const int j = j0 + ch / Gm::CPR, part = ch % Gm::CPR;
         pk[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (j < kv_end) pk[i] = *reinterpret_cast<const u32x4_t*>(kg + slot_of(j) * rstride + 8 * part);
+      }
+      const int jv = j0 + l;
+#pragma unroll
+      for (int i = 0; i < Gm::CPT; ++i) {
+        const int part = w + kFWaves * i;
         pv[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (j < kv_end) {
-          const int64_t slot = a.pm.token_slot(seq, j);
-          pk[i] = *reinterpret_cast<const u32x4_t*>(kg + slot * rstride + 8 * part);
-          pv[i] = *reinterpret_cast<const u32x4_t*>(vg + slot * rstride + 8 * part);
-        }
+        if (jv < kv_end) pv[i] = *reinterpret_cast<const u32x4_t*>(vg + slot_of(jv) * rstride + 8 * part);
       }
     };
     auto park = [&](unsigned char* buf) {
@@ -179,11 +194,23 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
         const int ch = threadIdx.x + kFThreads * i;
         const int jt = ch / Gm::CPR, part = ch % Gm::CPR;
         *reinterpret_cast<u32x4_t*>(ks + jt * Gm::KPITCH + part * 16) = pk[i];
-        const uint32_t wv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+      }
+      // adjacent lanes (tokens 2m, 2m+1) swap their rows and each writes
+      // 32-bit token pairs: the even lane for even dims, the odd lane for
+      // odd dims (byte permute of own and partner words)
+      const uint32_t psel = (l & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(vt + (8 * part + e) * Gm::VPITCH + jt * 2) =
-              (uint16_t)(wv[e / 2] >> (16 * (e % 2)));
+      for (int i = 0; i < Gm::CPT; ++i) {
+        const int part = w + kFWaves * i;
+        const uint32_t own[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+        unsigned char* col = vt + (8 * part + (l & 1)) * Gm::VPITCH + (l & ~1) * 2;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const uint32_t partner =
+              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own[k2], 0xB1, 0xF, 0xF, false);
+          *reinterpret_cast<uint32_t*>(col + 2 * k2 * Gm::VPITCH) =
+              __builtin_amdgcn_perm(partner, own[k2], psel);
+        }
       }
     };
 
@@ -219,44 +246,59 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
       u32x4_t pb[kFNC][2];
       bool rescale = false;
       float corr[kFNC];
+      // MASK: tiles reaching past the pass's smallest position mask slots
+      // past each column's position; the maximum is taken on raw scores
+      // (the scale is positive) and the scale folded into one fma per
+      // numerator
+      auto softmax = [&](auto mask_c) {
+        constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-      for (int c = 0; c < kFNC; ++c) {
-        // masked score of slot (tt, i): -inf past the column's position
-        auto score = [&](int tt, int i) {
-          const float v = sc[c][tt][i] * sl2;
-          return (need_mask && j0 + 16 * tt + 4 * g + i > cpos[c]) ? -INFINITY : v;
-        };
-        float mx = -INFINITY;
+        for (int c = 0; c < kFNC; ++c) {
+          auto masked = [&](int tt, int i) {
+            return MASK && j0 + 16 * tt + 4 * g + i > cpos[c];
+          };
+          float mr = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, score(tt, i));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool grow = mx > m[c] + kSlack;
-        const float m_new = grow ? mx : m[c];
-        corr[c] = (!grow || m[c] == -INFINITY) ? (grow ? 0.0f : 1.0f)
-                                                : __builtin_amdgcn_exp2f(m[c] - m_new);
-        rescale |= grow;
-        m[c] = m_new;
-        const bool none = m_new == -INFINITY;  // nothing attended yet
-        float ps = 0.0f;
-        uint32_t pw[8];
+            for (int i = 0; i < 4; ++i) mr = fmaxf(mr, masked(tt, i) ? -INFINITY : sc[c][tt][i]);
+          mr = fmaxf(mr, __shfl_xor(mr, 16));
+          mr = fmaxf(mr, __shfl_xor(mr, 32));
+          const float mx = mr * sl2;
+          const bool grow = mx > m[c] + kSlack;
+          const float m_new = grow ? mx : m[c];
+          corr[c] = (!grow || m[c] == -INFINITY) ? (grow ? 0.0f : 1.0f)
+                                                  : __builtin_amdgcn_exp2f(m[c] - m_new);
+          rescale |= grow;
+          m[c] = m_new;
+          // (without masking some score is finite, so m_new is)
+          const bool none = MASK && m_new == -INFINITY;
+          float ps = 0.0f;
+          uint32_t pw[8];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const float p0 = none ? 0.0f : __builtin_amdgcn_exp2f(score(tt, i) - m_new);
-            const float p1 = none ? 0.0f : __builtin_amdgcn_exp2f(score(tt, i + 1) - m_new);
-            ps += p0 + p1;
-            pw[2 * tt + i / 2] = pack_bf16x2(p0, p1);
-          }
-        lp[c] = lp[c] * corr[c] + ps;
-        // k-slots of step kk: tokens 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3
+            for (int i = 0; i < 4; i += 2) {
+              float p0 = __builtin_amdgcn_exp2f(fmaf(sc[c][tt][i], sl2, -m_new));
+              float p1 = __builtin_amdgcn_exp2f(fmaf(sc[c][tt][i + 1], sl2, -m_new));
+              if (MASK) {
+                p0 = (none || masked(tt, i)) ? 0.0f : p0;
+                p1 = (none || masked(tt, i + 1)) ? 0.0f : p1;
+              }
+              ps += p0 + p1;
+              pw[2 * tt + i / 2] = pack_bf16x2(p0, p1);
+            }
+          lp[c] = lp[c] * corr[c] + ps;
+          // k-slots of step kk: tokens 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          pb[c][kk] = u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
-      }
+          for (int kk = 0; kk < 2; ++kk)
+            pb[c][kk] = u32x4_t{pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
+        }
+      };
+      if (need_mask)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       if (__ballot(rescale) != 0ull) {
 #pragma unroll
         for (int c = 0; c < kFNC; ++c)
