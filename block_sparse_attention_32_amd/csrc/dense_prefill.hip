@@ -60,7 +60,7 @@ struct FGeom {
   static constexpr int KS = D / 32;               // k steps of Q.K
   static constexpr int NDT = D / 16;              // 16-dim tiles of the output
   static constexpr int KPITCH = D * 2 + 16;       // bytes per staged K row
-  static constexpr int VPITCH = kFTok * 2 + 16;   // bytes per staged V^T row (one dim)
+  static constexpr int VPITCH = kFTok * 2 + 8;    // bytes per staged V^T row (one dim)
   static constexpr int KBYTES = kFTok * KPITCH;
   static constexpr int BUF = KBYTES + D * VPITCH; // one stage (K then V^T)
   static constexpr int CPR = D / 8;               // 16-byte chunks per token row
