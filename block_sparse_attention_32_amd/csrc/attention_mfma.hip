@@ -140,7 +140,7 @@ __device__ void merge_splits(const AttnArgs& a, int row, bf16_t* orow) {
 }
 
 template <int D, bool DENSE, bool SPLIT>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
   // per list entry: element offset of its first token's row (a multiple of
