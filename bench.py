@@ -137,10 +137,12 @@ def _dense_time(fn, reps):
 # ------------------------------------------------------------------ prefill
 
 def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True,
-                dense_budget_s: float = 60.0):
+                dense_budget_s: float = 60.0, overlap: bool = False):
     """One step = the whole prefill of wl: every chunk of query rows in
     order (pool the chunk's new blocks -> fused scores + top-k -> per-row
-    sparse attention).  The existing context (if any) is pooled at set-up."""
+    sparse attention; with overlap the attention of chunk c runs on a second
+    stream beside the selection of chunk c+1).  The existing context (if any)
+    is pooled at set-up."""
     from block_sparse_attention_32_amd import pipeline as P
     log(f"[bench] drawing {wl.name} cache on {dev}")
     cache = W.make_cache(wl, device=dev)
@@ -158,12 +160,10 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
     if wl.n_ctx:
         P.pool_all(cv, 1, wl.n_ctx // 4, dev)               # set-up, untimed
 
+    sched = P.ChunkedPrefill(cv, [(c[0], c[1], c[2]) for c in chunks], overlap=overlap)
+
     def one(timer=None):
-        call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
-        for st, begin, nb, *_ in chunks:
-            call("pool", B.qsa_pool_blocks, cv, begin, nb)
-            call("topk", st.select)
-            call("attn", st.attend)
+        sched.run(timer.wrap if timer else None)
 
     wall, kern = _timed(one, steps, warmup)
     rows_total = sum(len(c[3]) for c in chunks)
@@ -295,6 +295,9 @@ def main():
     ap.add_argument("--workload", default="prefill_1m", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-GQA comparison")
+    ap.add_argument("--overlap", action="store_true",
+                    help="prefill: run each chunk's attention on a second stream, beside the "
+                         "next chunk's selection (per-kernel times then overlap)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -321,7 +324,8 @@ def main():
     if decode:
         wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=not args.no_dense)
     else:
-        wall, timer, work, ctx = run_prefill(wl, steps, warmup, dev, dense=not args.no_dense)
+        wall, timer, work, ctx = run_prefill(wl, steps, warmup, dev, dense=not args.no_dense,
+                                             overlap=args.overlap)
     kern_call = timer.avg_us()                      # per API call
     calls_per_step = ctx["launches"]
     kern = {k: v * calls_per_step for k, v in kern_call.items()}   # per step

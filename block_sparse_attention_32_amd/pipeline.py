@@ -75,3 +75,43 @@ def pool_all(cache: B.CacheView, n_seqs: int, n_blocks: int, device) -> None:
     """Pool blocks 0 .. n_blocks-1 of every sequence (cache set-up)."""
     begin = torch.zeros(n_seqs, dtype=torch.int32, device=device)
     B.qsa_pool_blocks(cache, begin, n_blocks)
+
+
+class ChunkedPrefill:
+    """A prefill in chunks of query rows, chunk by chunk in order.
+
+    chunks: list of (QsaStep, blk_begin, n_new_blocks): the chunk's rows and
+    the blocks its tokens complete (pooled before its selection).
+
+    With overlap=True the selections run on the caller's stream and the
+    attention calls on a second stream: the attention of chunk c waits
+    (HIP event) for the selection of chunk c only, so it runs while the
+    selection of chunk c+1 computes.  The two phases stress different units
+    (the indexer matrix cores and VALU, the attention the vector-memory
+    path), and nothing either writes is read by the other.  Results are the
+    same as with overlap=False; the caller's stream waits for the last
+    attention before returning.
+    """
+
+    def __init__(self, cache: B.CacheView, chunks, overlap: bool = True):
+        self.cache, self.chunks, self.overlap = cache, list(chunks), overlap
+        self.side = torch.cuda.Stream(device=cache.device) if overlap else None
+
+    def run(self, call=None):
+        """call(name, fn, *args): optional wrapper around each library call
+        (timing); it runs on the stream current at the call."""
+        call = call or (lambda name, fn, *a: fn(*a))
+        main = torch.cuda.current_stream()
+        for st, begin, nb in self.chunks:
+            call("pool", B.qsa_pool_blocks, self.cache, begin, nb)
+            call("topk", st.select)
+            if not self.overlap:
+                call("attn", st.attend)
+                continue
+            done = torch.cuda.Event()
+            done.record(main)
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(done)
+                call("attn", st.attend)
+        if self.overlap:
+            main.wait_stream(self.side)

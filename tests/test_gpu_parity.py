@@ -372,6 +372,47 @@ def test_e2e_prefill_1m_chunk(gpu, chunk):
     _e2e(pb, check)
 
 
+def test_chunked_prefill_overlap_matches_serial(gpu):
+    """The two-stream chunked prefill (each chunk's attention beside the next
+    chunk's selection) gives the serial schedule's results bit for bit, and
+    sampled rows match the oracle."""
+    _say("chunked prefill overlap")
+    wl = WL["prefill_8k_at_128k"].replace(n_ctx=20000, n_new=1536, chunk=512, n_needles=4)
+    cache = W.make_cache(wl, device=gpu)
+    cv = B.CacheView.from_cache(cache)
+    P.pool_all(cv, 1, wl.n_ctx // 4, gpu)
+    steps, rows = [], []
+    for ci in range(3):
+        seq_id, pos = W.prefill_rows(wl, ci)
+        qs = W.make_queries(wl, cache, seq_id, pos, device=gpu, seed=wl.seed + 7919 + ci)
+        qv = B.QueriesView(qs.seq_id, qs.pos, max(pos))
+        st = P.QsaStep(cv, qv, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "prefill")
+        b0 = pos[0] // 4
+        steps.append((st, torch.full((1,), b0, dtype=torch.int32, device=gpu),
+                      (pos[-1] + 1) // 4 - b0))
+        rows.append((qs, pos))
+    results = []
+    for overlap in (False, True):
+        for st, _, _ in steps:
+            st.sel.fill_(-7)
+            st.out.fill_(float("nan"))
+        P.ChunkedPrefill(cv, steps, overlap=overlap).run()
+        torch.cuda.synchronize()
+        results.append([(st.sel.clone(), st.n_sel.clone(), st.out.clone()) for st, _, _ in steps])
+    for (s0, n0, o0), (s1, n1, o1) in zip(*results):
+        assert torch.equal(s0, s1) and torch.equal(n0, n1) and torch.equal(o0, o1)
+    # the last chunk against the oracle on a few rows
+    qs, pos = rows[-1]
+    pb = Problem(wl, gpu, [0] * len(pos), pos)
+    pb.cache, pb.qs = cache, qs
+    _, sel, n = sel_rows(steps[-1][0].sel, steps[-1][0].n_sel)
+    got = f64(steps[-1][0].out)
+    for i in (0, 255, 511):
+        want_sel = pb.oracle_select(i)
+        assert_sel_row(sel[i], int(n[i]), want_sel, wl.top_k)
+        assert np.abs(got[i] - pb.oracle_attend(i, want_sel)).max() <= TOL[wl.dtype]
+
+
 def test_decode_with_boundary_margin(gpu):
     """Decode with a score gap of at least 2^-4 at the k-th boundary: blocks
     just below the boundary get their indexer keys halved (which halves
