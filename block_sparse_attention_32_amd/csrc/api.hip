@@ -188,6 +188,7 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
   a.pm = page_map(c);
   a.k = c->k;
   a.v = c->v;
+  a.n_slots = (int64_t)c->n_pages * c->page_size;
   a.hkv = c->n_kv_heads;
   a.hq = hq;
   a.q = q;

@@ -30,6 +30,7 @@ struct AttnArgs {
   float* part_acc;        // [T][n_splits][hq][D]
   float* part_ml;         // [T][n_splits][hq][2]
   uint32_t* cnt;          // [T]
+  int64_t n_slots;        // token rows of the K and V arrays (pages x page size)
 };
 
 // LDS layout of the generic kernel (byte offsets, each 16-byte aligned).
@@ -64,7 +65,6 @@ constexpr int kMfmaTileTok = 16;    // tokens per wave tile
 constexpr int kMfmaTileEnt = 4;     // token-list entries (blocks) per tile
 constexpr int kMfmaSplitEnt = 16;   // entries per split and KV head (split-K decode)
 constexpr int kMfmaEntChunk = 512;  // entries staged in LDS per pass
-constexpr int kVPitch = 272;        // LDS bytes per staged V row (256 + 16)
 
 bool attn_mfma_supported(int dtype, int hq, int hkv, int d);
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st);

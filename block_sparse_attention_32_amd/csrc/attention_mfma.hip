@@ -12,11 +12,15 @@
 //   O^T[D x 16 heads] += V^T[D x 16 tok] . P^T     v_mfma_f32_16x16x16_bf16
 //     B = the softmax numerators, used in the registers where S^T left
 //     them (lane group g holds tokens 4g..4g+3, which are its four
-//     k-slots); A = V^T read from an LDS copy of the tile's V rows.
+//     k-slots); A = V^T, read with ds_read_b64_tr_b16 from an LDS copy of
+//     the tile's V rows.  A product with a ones operand sums the
+//     numerators (the softmax denominator) on the matrix core as well.
 //
 // Workgroups: 4 waves per (row, split).  With n_splits > 1 (the SPLIT
 // instances) the split partials go to the workspace and the last split of
 // the row merges them.
+#include <type_traits>
+
 #include "attention.hpp"
 
 namespace qsa {
@@ -139,19 +143,38 @@ __device__ void merge_splits(const AttnArgs& a, int row, bf16_t* orow) {
   for (int j = 0; j < ND; ++j) o[j] = f32_to_bf16(O[j] * inv);
 }
 
-template <int D, bool DENSE, bool SPLIT>
+// K/V row offsets are kept as 32-bit byte offsets while both arrays are
+// smaller than this; larger caches take the WIDE instances, which keep row
+// indices and form 64-bit addresses.
+constexpr int64_t kNarrowCacheBytes = (1ll << 32) - (1ll << 16);
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+template <int D, bool DENSE, bool SPLIT, bool WIDE>
 __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
-  // per list entry: element offset of its first token's row (a multiple of
-  // Hkv*D >= 32) with the number of its tokens to attend (0..4) in the low
-  // bits; padded to whole tiles with empty entries
-  __shared__ int64_t ent_off[kMfmaEntChunk];
-  constexpr int kStage = 4 * kMfmaTileTok * kVPitch;   // per-wave V tiles
+  // LDS bytes per staged V row: 32 bytes more than the row, so that the 8
+  // rows one half-wave reads in a transposing load start 8 banks apart
+  constexpr int VP = 2 * D + 32;
+  // K rows are staged unpadded, 16-byte chunk c of tile row r at chunk
+  // position c ^ (r mod NCH): the 16 rows of one A-fragment read, all at
+  // the same chunk, then fall on distinct banks
+  constexpr int KP = 2 * D, NCH = D / 8;
+  constexpr int kStage = 4 * kMfmaTileTok * (VP + KP);  // per-wave K and V tiles
   constexpr int kMerge = 4 * 16 * (D + 2) * 4;         // per-wave results
+  // The token rows of the staged list, tile by tile: a tile is 4 entries
+  // (blocks) x 4 tokens, kept as [token j][entry i]; each value is the
+  // byte offset of the token's row in the K and V arrays (WIDE: its row
+  // index).  Tokens not to attend point at the row's own first token.
+  __shared__ __align__(16) uint32_t trow[kMfmaEntChunk * 4];
   __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
+  __shared__ int wcnt[4];
   __shared__ uint32_t flag;
-  const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
+  // the wave index is uniform: read it once so that what derives from it
+  // (the KV head, the wave's tiles, the cache base) stays scalar
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int l = lane_id(), g = l / 16, c16 = l % 16;
   const int hkv = a.hkv, hq = a.hq, G = hq / hkv;
   const int wph = 4 / hkv;  // waves per KV head
   const int hk = w % hkv, wsub = w / hkv;
@@ -167,17 +190,17 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
   const int e_end = min(n_entries, e_beg + a.eps);
   const int tail = (t % kBlock) + 1;  // tokens of the own block
 
-  const bf16_t* kg = static_cast<const bf16_t*>(a.k) + hk * D;
-  const bf16_t* vg = static_cast<const bf16_t*>(a.v) + hk * D;
-  const int64_t rstride = (int64_t)hkv * D;
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + hk * D * 2;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + hk * D * 2;
+  const int64_t rowbytes = (int64_t)hkv * D * 2;
   const int64_t own_row = a.pm.token_slot(seq, b_own * kBlock);  // always present
-  const int64_t own_off = own_row * rstride;
-  const int64_t k_ti = (c16 % 4) * rstride;  // K: token c16 % 4 of an entry
-  const int64_t v_ti = g * rstride;          // V: token g of an entry
+  const uint32_t own_t = WIDE ? (uint32_t)own_row : (uint32_t)(own_row * rowbytes);
+  const int cv = c16 < D / 8 ? c16 : 0;
+  const uint32_t lane_c = 16 * cv;  // 16-byte chunk cv of a K or V row
 
-  // this lane's B fragment of Q^T: head c16 of the group, dims 32s + 8g .. +8
-  // at step s (K uses the same order, so one load instruction reads 64
-  // contiguous bytes of each token row)
+  // this lane's B fragment of Q^T: head c16 of the group, dims 32 s + 8 g
+  // .. +8 at step s (K uses the same order, so one load instruction reads
+  // 64 contiguous bytes of each token row)
   u32x4_t qf[KS];
   {
     const bf16_t* qh = static_cast<const bf16_t*>(a.q) + ((int64_t)row * hq + hk * G + c16) * D;
@@ -185,133 +208,202 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
     for (int s = 0; s < KS; ++s)
       qf[s] = (c16 < G) ? ld16(qh + 32 * s + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  const float sl2 = a.scale * 1.4426950408889634f;  // scores in log2 units
-  float m = -INFINITY, lsum = 0.0f;
+  // Online softmax per head column.  Scores stay raw (q.k); the reference
+  // maximum m is kept raw and as m * scale * log2(e), and moves only when a
+  // score exceeds it by kSlack in log2 units (mlim, raw).
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const float slack_raw = kSlack / sl2;
+  float m_raw = -INFINITY, msl2 = -INFINITY, mlim = -INFINITY;
   f32x4_t acc[NDT];
 #pragma unroll
   for (int n = 0; n < NDT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  unsigned char* vs = lds + w * kMfmaTileTok * kVPitch;
+  f32x4_t lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};  // softmax denominator, via a ones operand
+  const u32x2_t ones = {0x3F803F80u, 0x3F803F80u};  // bfloat16 1.0 x 4
+  unsigned char* vs = lds + w * kMfmaTileTok * (VP + KP);
+  unsigned char* ks = vs + kMfmaTileTok * VP;
+  // transposing read of V^T (see the O^T step): the lane supplies the
+  // address of tile row 4g + c16/4, dims 16n + 4(c16 % 4) .. +4
+  const uint32_t tr_off = (4 * g + c16 / 4) * VP + 8 * (c16 % 4);
+  // K A-fragment reads: row c16, chunk 4s + g (dims 32s + 8g .. +8, the
+  // order of the Q fragments)
+  const uint32_t kr_off = c16 * KP;
 
   for (int cb = e_beg; cb < e_end; cb += kMfmaEntChunk) {
     const int nloc = min(e_end, cb + kMfmaEntChunk) - cb;
     __syncthreads();
-    const int npad = (nloc + kMfmaTileEnt - 1) / kMfmaTileEnt * kMfmaTileEnt;
-    for (int i = threadIdx.x; i < npad; i += blockDim.x) {
+    // Stage the valid entries of [cb, cb + nloc) at the front, in list
+    // order (a block-wide prefix count of the valid flags), so that every
+    // tile but the last holds four whole blocks.  The own block is the last
+    // entry of the list, hence the last valid entry of its chunk.
+    int nv = 0;
+    for (int i0 = 0; i0 < nloc; i0 += kAttnThreads) {
+      const int i = i0 + (int)threadIdx.x;
       const int E = cb + i;
       const bool own = (E == n_list);
       const int b = i >= nloc ? -1 : (own ? b_own : (DENSE ? E : sel_row[E]));
       const bool ok = i < nloc && (own || (b >= 0 && b < b_own));
-      ent_off[i] = ok ? (a.pm.token_slot(seq, b * kBlock) * rstride) | (own ? tail : kBlock)
-                      : own_row * rstride;
-    }
-    __syncthreads();
-    const int n_tiles = (nloc + kMfmaTileEnt - 1) / kMfmaTileEnt;
-    // A tile is 16 tokens (4 entries).  The K fragments (A operand: token
-    // c16, dims 32s + 8g) and the V rows (token g + 4i, 16-byte chunk
-    // c16) of the wave's next tile are loaded while the current one is
-    // computed.
-    //
-    // Loads are unconditional (straight-line code keeps the prefetch in
-    // flight): a token that is not attended -- past the own block's tail,
-    // or of an invalid list entry -- is read from the row's own first
-    // token instead, which is always in the cache; its score is masked to
-    // -inf and its numerator is 0, so it contributes nothing.
-    auto load_tile = [&](int tile, u32x4_t (&kf)[KS], u32x4_t (&vf)[4]) {
-      const int e0 = tile * kMfmaTileEnt;
-      {
-        const int64_t v = ent_off[e0 + c16 / 4];
-        const int64_t off = (c16 % 4) < (int)(v & 7) ? (v & ~7ll) + k_ti : own_off;
-        const bf16_t* p = kg + off + 8 * g;
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) kf[s2] = ld16(p + 32 * s2);
-      }
-      const int cv = c16 < D / 8 ? c16 : 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t v = ent_off[e0 + i];
-        const int64_t off = g < (int)(v & 7) ? (v & ~7ll) + v_ti : own_off;
-        vf[i] = ld16(vg + off + 8 * cv);
-      }
-    };
-    // one tile: S^T, online softmax, O^T update
-    auto compute = [&](int tile, const u32x4_t (&kf)[KS], const u32x4_t (&vf)[4]) {
-      const int e0 = tile * kMfmaTileEnt;
-      // S^T: lane holds tokens 4g + r (entry e0 + g) for head c16
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) sc = mfma16(kf[s2], qf[s2], sc);
-      if (c16 < D / 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4_t*>(vs + (g + 4 * i) * kVPitch + 16 * c16) = vf[i];
-      }
-      float x[4];
-      float mx = -INFINITY;
-      {
-        const int nt = (int)(ent_off[e0 + g] & 7);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = r < nt ? sc[r] * sl2 : -INFINITY;
-          x[r] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // move the reference maximum (and rescale) only when some column
-      // needs it
-      const bool grow = mx > m + kSlack;
-      if (__ballot(grow) != 0ull) {
-        const float m_new = grow ? mx : m;
-        const float corr = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-        lsum *= corr;
-#pragma unroll
-        for (int n = 0; n < NDT; ++n) acc[n] = acc[n] * corr;
-        m = m_new;
-      }
-      float p[4];
-      float psum = 0.0f;
+      const uint64_t bal = __ballot(ok);
+      if (l == 0) wcnt[w] = __popcll(bal);
+      __syncthreads();
+      int pos = nv + (int)lanes_below(bal), tot = nv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // m is -inf only while every score so far was masked (then x is too)
-        p[j] = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m);
-        psum += p[j];
+        const int c = wcnt[j];
+        pos += j < w ? c : 0;
+        tot += c;
       }
-      lsum += psum;
+      if (ok) {
+        const int64_t r0 = a.pm.token_slot(seq, b * kBlock);
+        const int nt = own ? tail : kBlock;
+        uint32_t* tp = trow + (pos / 4) * 16 + (pos % 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t r = j < nt ? r0 + j : own_row;
+          tp[4 * j] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+        }
+      }
+      nv = tot;
+      __syncthreads();
+    }
+    for (int i = nv + (int)threadIdx.x; i < ((nv + 3) & ~3); i += kAttnThreads) {
+      uint32_t* tp = trow + (i / 4) * 16 + (i % 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tp[4 * j] = own_t;
+    }
+    __syncthreads();
+    const int n_tiles = (nv + 3) / 4;
+    const int last = n_tiles - 1;
+    const bool own_here = n_list >= cb && n_list < cb + nloc;
+    // A tile is 16 tokens, tile row 4i + j = entry i, token j.  The K and
+    // V rows of the wave's next tile are loaded while the current one is
+    // computed, both the same way: load i reads entry i, lane group g its
+    // token g, lane c16 its 16-byte chunk, so that 16 lanes read a whole
+    // row (whole cache lines; the MFMA operand order, 64 bytes of 16 rows
+    // per load, costs the vector cache about twice as much).  Every load
+    // reads a row present in the cache (masked tokens read the own block's
+    // first token).
+    auto load_tile = [&](int tile, u32x4_t (&kf)[4], u32x4_t (&vf)[4]) {
+      const u32x4_t tv = *reinterpret_cast<const u32x4_t*>(trow + tile * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (WIDE) {
+          const int64_t o = (int64_t)tv[i] * rowbytes + lane_c;
+          kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
+          vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
+        } else {
+          const uint32_t o = tv[i] + lane_c;
+          kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
+          vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
+        }
+      }
+    };
+    // one tile: S^T, online softmax, O^T update.  Only the last tile of
+    // the chunk can hold tokens not to attend (the own block's tail, the
+    // padding), so only it masks.
+    auto compute = [&](auto masked, int tile, const u32x4_t (&kf)[4], const u32x4_t (&vf)[4]) {
+      constexpr bool MASK = decltype(masked)::value;
+      // K and V rows to LDS (row 4i + g)
+      if (c16 < D / 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + g;
+          *reinterpret_cast<u32x4_t*>(ks + r * KP + 16 * (cv ^ (r % NCH))) = kf[i];
+          *reinterpret_cast<u32x4_t*>(vs + (4 * i + g) * VP + 16 * c16) = vf[i];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // S^T: lane holds tile tokens 4g + r (entry g, token r) for head c16
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const u32x4_t kfr = *reinterpret_cast<const u32x4_t*>(
+            ks + kr_off + 16 * ((4 * s2 + g) ^ (c16 % NCH)));
+        sc = mfma16(kfr, qf[s2], sc);
+      }
+      float x[4];
+      if constexpr (MASK) {
+        const int pos = tile * 4 + g;
+        const int nt = pos < nv - 1 ? kBlock : (pos == nv - 1 ? (own_here ? tail : kBlock) : 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = r < nt ? sc[r] : -INFINITY;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = sc[r];
+      }
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__ballot(mx > mlim) != 0ull) {
+        // the column's maximum over the four lane groups (rows 16 apart,
+        // then 32 apart)
+        float cm = mx;
+        {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm),
+                                                          false, false);
+          cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm),
+                                                          false, false);
+          cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        if (cm > mlim) {
+          const float msl2_new = cm * sl2;
+          const float corr = __builtin_amdgcn_exp2f(msl2 - msl2_new);  // 0 while msl2 = -inf
+          lacc = lacc * corr;
+#pragma unroll
+          for (int n = 0; n < NDT; ++n) acc[n] = acc[n] * corr;
+          m_raw = cm;
+          msl2 = msl2_new;
+          mlim = m_raw + slack_raw;
+        }
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(x[r], sl2, -msl2));
       const u32x2_t pb = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      // O^T += V^T . P^T; k-slot i of lane group g is token 4g + i
+      // O^T += V^T . P^T.  A lane's k-slots j are tile tokens 4g + j
+      // (where S^T left them); the transposing LDS read gives lane (g, c16)
+      // V[4g + j][16n + c16], j = 0..3.
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {
-        const unsigned char* col = vs + 2 * (16 * n + c16);
-        uint32_t h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          h[j] = *reinterpret_cast<const uint16_t*>(col + (4 * g + j) * kVPitch);
-        const u32x2_t va = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        acc[n] = mfma16k16(va, pb, acc[n]);
+        const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vs + tr_off + 32 * n));
+        acc[n] = mfma16k16(__builtin_bit_cast(u32x2_t, v4), pb, acc[n]);
       }
+      lacc = mfma16k16(ones, pb, lacc);
       __builtin_amdgcn_wave_barrier();
     };
-    // two register sets alternate: the loads of the wave's next tile go to
-    // the set not being computed (the last tile reloads itself, so every
-    // step issues the same loads and the wait before a product covers only
-    // the current tile's)
-    u32x4_t ka[KS], va4[4], kb[KS], vb4[4];
-    if (wsub < n_tiles) load_tile(wsub, ka, va4);
-    for (int tile = wsub; tile < n_tiles; tile += 2 * wph) {
-      const int t1 = tile + wph;
-      load_tile(t1 < n_tiles ? t1 : tile, kb, vb4);
-      compute(tile, ka, va4);
-      if (t1 >= n_tiles) break;
-      const int t2 = t1 + wph;
-      load_tile(t2 < n_tiles ? t2 : t1, ka, va4);
-      compute(t1, kb, vb4);
+    // The wave's tiles are wsub + q * wph, q < nmine; the last tile of the
+    // chunk (masked) is its owner's last.  Two register sets alternate: the
+    // loads of the next tile go to the set not being computed (past the end
+    // a wave reloads its last tile, so every step issues the same loads and
+    // the wait before a product covers only the current tile's).
+    const int nmine = wsub < n_tiles ? (last - wsub) / wph + 1 : 0;
+    const bool has_last = nmine > 0 && wsub + (nmine - 1) * wph == last;
+    const int nclean = nmine - (has_last ? 1 : 0);
+    auto T = [&](int q) { return wsub + min(q, nmine - 1) * wph; };
+    u32x4_t kA[4], vA[4], kB[4], vB[4];
+    if (nmine > 0) {
+      load_tile(T(0), kA, vA);
+      int q = 0;
+      for (; q + 2 <= nclean; q += 2) {
+        load_tile(T(q + 1), kB, vB);
+        compute(std::false_type{}, T(q), kA, vA);
+        load_tile(T(q + 2), kA, vA);
+        compute(std::false_type{}, T(q + 1), kB, vB);
+      }
+      if (q < nclean) {  // one clean tile left (in A), then perhaps the last (B)
+        load_tile(T(q + 1), kB, vB);
+        compute(std::false_type{}, T(q), kA, vA);
+        if (has_last) compute(std::true_type{}, T(q + 1), kB, vB);
+      } else if (has_last) {
+        compute(std::true_type{}, T(q), kA, vA);
+      }
     }
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const float lsum = lacc[0];  // every row of the ones product is the column sum
   __syncthreads();
   // per-wave results to LDS: [wave][head][D + 2] (acc, then m, l)
   float* mrg = reinterpret_cast<float*>(lds);
@@ -322,7 +414,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[16 * n + 4 * g + i] = acc[n][i];
     if (g == 0) {
-      o[D] = m;
+      o[D] = msl2;
       o[D + 1] = lsum;
     }
   }
@@ -373,21 +465,25 @@ bool attn_mfma_supported(int dtype, int hq, int hkv, int d) {
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st) {
   dim3 grid((unsigned)a.n_splits, (unsigned)n_rows);
   const bool split = a.n_splits > 1;
-#define QSA_ATTN_LAUNCH(DD, DN, SP) \
-  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP>), grid, dim3(256), 0, st, a)
+  const bool wide = a.n_slots * a.hkv * d * 2 > kNarrowCacheBytes;
+#define QSA_ATTN_LAUNCH(DD, DN, SP, WD) \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD>), grid, dim3(256), 0, st, a)
+#define QSA_ATTN_LAUNCH_W(DD, DN, SP) \
+  if (wide) QSA_ATTN_LAUNCH(DD, DN, SP, true); else QSA_ATTN_LAUNCH(DD, DN, SP, false)
   if (d == 128) {
     if (dense) {
-      if (split) QSA_ATTN_LAUNCH(128, true, true); else QSA_ATTN_LAUNCH(128, true, false);
+      if (split) { QSA_ATTN_LAUNCH_W(128, true, true); } else { QSA_ATTN_LAUNCH_W(128, true, false); }
     } else {
-      if (split) QSA_ATTN_LAUNCH(128, false, true); else QSA_ATTN_LAUNCH(128, false, false);
+      if (split) { QSA_ATTN_LAUNCH_W(128, false, true); } else { QSA_ATTN_LAUNCH_W(128, false, false); }
     }
   } else {
     if (dense) {
-      if (split) QSA_ATTN_LAUNCH(64, true, true); else QSA_ATTN_LAUNCH(64, true, false);
+      if (split) { QSA_ATTN_LAUNCH_W(64, true, true); } else { QSA_ATTN_LAUNCH_W(64, true, false); }
     } else {
-      if (split) QSA_ATTN_LAUNCH(64, false, true); else QSA_ATTN_LAUNCH(64, false, false);
+      if (split) { QSA_ATTN_LAUNCH_W(64, false, true); } else { QSA_ATTN_LAUNCH_W(64, false, false); }
     }
   }
+#undef QSA_ATTN_LAUNCH_W
 #undef QSA_ATTN_LAUNCH
 }
 

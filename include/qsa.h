@@ -162,7 +162,8 @@ qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
  *   out[i][hq] = sum_{j in S_i} softmax_j(scale * q[i][hq] . K[j][hk]) V[j][hk]
  * accumulated in float32 and rounded to nearest-even in the cache dtype.
  * q, out: [T][n_q_heads][D] in the cache dtype; sel/n_sel as written by
- * qsa_topk_blocks (row stride top_k).
+ * qsa_topk_blocks (row stride top_k).  Ids outside [0, pos[i]/4) among
+ * the first n_sel[i] entries are skipped.
  * qsa_attn_decode splits each row's token set across workgroups (for few
  * rows); qsa_attn_prefill gives each row its own workgroup (for many rows).
  * Both compute the same result. */

@@ -243,6 +243,82 @@ def test_attention_given_selection(gpu, case, mode):
         assert err <= TOL[wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
 
 
+def _run_attention(pb, cv, sel, n_sel, mode):
+    wl = pb.wl
+    out = torch.full_like(pb.qs.q, float("nan"))
+    op = B.QSA_OP_ATTN_DECODE if mode == "decode" else B.QSA_OP_ATTN_PREFILL
+    ws = B.workspace(op, cv, pb.rows, wl.hq, wl.top_k)
+    fn = B.qsa_attn_decode if mode == "decode" else B.qsa_attn_prefill
+    fn(cv, pb.rows, pb.qs.q, sel.to(pb.device), n_sel.to(pb.device), wl.top_k, wl.scale, out,
+       ws)
+    torch.cuda.synchronize()
+    return f64(out)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_attention_skips_invalid_entries(gpu, mode):
+    """Block ids outside [0, pos/4) inside a row's n_sel entries (negative,
+    the own block, later blocks) are skipped; the other entries are attended
+    as given."""
+    _say(f"attention invalid entries {mode}")
+    pb = Problem(MIXED, gpu, [0] * len(MIXED_POS), MIXED_POS)
+    wl = pb.wl
+    T = len(pb.pos_list)
+    rng = np.random.default_rng(5)
+    sel = torch.full((T, wl.top_k), -1, dtype=torch.int32)
+    n_sel = torch.zeros(T, dtype=torch.int32)
+    kept = []
+    for i in range(T):
+        s = pb.oracle_select(i).astype(np.int64)
+        b_own = pb.pos_list[i] // 4
+        bad = [-1, -7, b_own, b_own + 3, 1 << 30]
+        drop = rng.choice(len(s), size=min(len(s), int(rng.integers(0, 9))), replace=False)
+        k = np.delete(s, drop)
+        lst = list(k)
+        for _ in range(min(int(rng.integers(1, 9)), wl.top_k - len(k))):
+            lst.insert(int(rng.integers(0, len(lst) + 1)), int(rng.choice(bad)))
+        sel[i, : len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        n_sel[i] = len(lst)
+        kept.append(k)
+    got = _run_attention(pb, pb.cv, sel, n_sel, mode)
+    for i in range(T):
+        err = np.abs(got[i] - pb.oracle_attend(i, kept[i])).max()
+        assert err <= TOL[wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
+
+
+def test_attention_cache_over_4gib(gpu):
+    """K and V arrays over 4 GiB each (rows addressed with 64-bit offsets):
+    the sequence's pages sit at the top of the arrays."""
+    _say("attention cache over 4 GiB")
+    pos = [5, 2051, 32771, 59999]
+    pb = Problem(MIXED, gpu, [0] * len(pos), pos)
+    wl, c = pb.wl, pb.cache
+    page_bytes = wl.page_size * wl.hkv * wl.d * c.k.element_size()
+    n_big = (1 << 32) // page_bytes + c.n_pages + 16
+    off = n_big - c.n_pages
+    kb = torch.empty((n_big,) + tuple(c.k.shape[1:]), dtype=c.k.dtype, device=gpu)
+    vb = torch.empty_like(kb)
+    kb[off:] = c.k
+    vb[off:] = c.v
+    cv = B.CacheView(kb, vb, c.kidx, c.kbar, (c.block_table + off).contiguous(), c.seq_len,
+                     wl.total_len)
+    assert kb.numel() * kb.element_size() > (1 << 32)
+    T = len(pos)
+    sel = torch.full((T, wl.top_k), -1, dtype=torch.int32)
+    n_sel = torch.zeros(T, dtype=torch.int32)
+    sels = [pb.oracle_select(i) for i in range(T)]
+    for i, s in enumerate(sels):
+        sel[i, : len(s)] = torch.from_numpy(s.astype(np.int32))
+        n_sel[i] = len(s)
+    for mode in ("decode", "prefill"):
+        got = _run_attention(pb, cv, sel, n_sel, mode)
+        for i in range(T):
+            err = np.abs(got[i] - pb.oracle_attend(i, sels[i])).max()
+            assert err <= TOL[wl.dtype], f"{mode} row {i} t={pos[i]} err={err}"
+    del kb, vb, cv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
 def test_dense_attention(gpu, mode):
     _say(f"dense {mode}")
