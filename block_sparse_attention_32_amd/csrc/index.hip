@@ -270,6 +270,10 @@ struct KeyArray {  // keys in LDS or global memory
   const uint32_t* k;
   __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
 };
+struct ScoreKeys {  // keys of caller scores
+  const float* s;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return score_key(s[e]); }
+};
 struct IdArray {
   const int32_t* id;
   __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
@@ -395,14 +399,27 @@ __device__ void place_runs(const uint32_t* ukey, const int32_t* uid, int un, uin
 
 
 
-// Exact top-k of n <= kDirectCap keys read from keys[0..n) (global memory
-// or LDS), every key held in registers.
-__device__ void select_direct(const uint32_t* keys, int n, int top_k, int32_t* sel_row,
-                              int32_t* n_sel, int row, SelShared& sh) {
+// Exact top-k of a row of n <= kDirectCap candidates whose keys get(e)
+// returns: thread t holds keys t * EPT .. t * EPT + EPT - 1 in registers
+// (all of its loads in flight at once), then a register radix select and
+// ordered emission.  Kept out of line: it runs once per row.
+template <class Get>
+__device__ __noinline__ void select_direct(Get get, int n, int top_k, int32_t* sel_row,
+                                           int32_t* n_sel, int row, SelShared& sh) {
+  constexpr int EPT = kDirectCap / kSelThreads;
+  const int base = (int)threadIdx.x * EPT;
+  uint32_t key[EPT];
+  int32_t id[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    key[i] = get(min(base + i, n - 1));
+    id[i] = base + i;
+  }
   uint32_t thr;
   int r;
-  radix_kth(KeyArray{keys}, n, top_k, sh, thr, r);
-  emit_topk(KeyArray{keys}, SelfId{}, n, thr, r, sel_row, top_k, sh);
+  bool resolved;
+  radix_kth_regs<EPT>(key, n, top_k, sh, thr, r, resolved);
+  emit_regs<EPT>(key, id, n, thr, r, sel_row, top_k, sh);
   if (threadIdx.x == 0) n_sel[row] = top_k;
 }
 
@@ -428,9 +445,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
   if (direct && given) {  // every score is stored already: one workgroup
     if (c != 0) return;
-    for (int e = threadIdx.x; e < p.n; e += blockDim.x) dkeys[e] = score_key(given[e]);
-    __syncthreads();
-    select_direct(dkeys, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(ScoreKeys{given}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
     return;
   }
   if (c >= p.W) return;
@@ -478,9 +493,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   }
   if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
   if (direct) {
-    for (int e = threadIdx.x; e < p.n; e += blockDim.x) dkeys[e] = ws_row[e];
-    __syncthreads();
-    select_direct(dkeys, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(KeyArray{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
     return;
   }
 
