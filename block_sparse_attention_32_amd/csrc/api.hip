@@ -133,10 +133,10 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
   p.tile = p.mfma ? kMfmaTileTok : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
   const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
   if (split && p.mfma) {
-    // kMfmaSplitEnt entries per KV head and split (two tiles per wave at
-    // two waves per KV head); grow the split when rows x splits would
-    // exceed kMaxSplitWgs
-    const int wph = 4 / c->n_kv_heads;
+    // split workgroups have 8 waves, wph of them per KV head, and each
+    // wave gets two 4-entry tiles (kMfmaSplitEnt = 16 entries per wave
+    // pair); grow the split when rows x splits would exceed kMaxSplitWgs
+    const int wph = 8 / c->n_kv_heads;
     int eps = kMfmaSplitEnt * wph / 2;
     while ((int64_t)rows * ((entries + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
     p.eps = eps;

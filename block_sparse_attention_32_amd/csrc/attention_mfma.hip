@@ -60,14 +60,16 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 constexpr float kSlack = 8.0f;
 
 // Split partials of a row, [split][head] x (D floats of unnormalised acc,
-// then (m in log2 units, l)), are written and merged by 256 threads that
-// each own one head and D/16 contiguous dims of it (hq <= 16).
-template <int D>
+// then (m in log2 units, l)), are written and merged by the NT threads of a
+// workgroup, each owning one head and D/(NT/16) contiguous dims of it
+// (hq <= 16).
+template <int D, int NT>
 struct MergeLane {
-  static constexpr int ND = D / 16;  // dims per thread
+  static constexpr int LPH = NT / 16;  // threads per head
+  static constexpr int ND = D / LPH;   // dims per thread
   int h, d0;
   bool on;
-  __device__ MergeLane(int hq) : h(threadIdx.x / 16), d0((threadIdx.x % 16) * ND), on(h < hq) {}
+  __device__ MergeLane(int hq) : h(threadIdx.x / LPH), d0((threadIdx.x % LPH) * ND), on(h < hq) {}
 };
 
 __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
@@ -76,17 +78,17 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
 __device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
-constexpr int kMergeBatch = 8;  // splits whose partials are in flight together
-
 // Merge of a row's split partials, run by the last split workgroup after its
 // acquire.  Each thread keeps a running (M, L, O[ND]) for its head and dims;
 // the partials of the next kMergeBatch splits are loaded while the current
 // batch is folded in.
-template <int D>
+template <int D, int NT>
 __device__ void merge_splits(const AttnArgs& a, int row, bf16_t* orow) {
-  constexpr int ND = MergeLane<D>::ND;
+  constexpr int ND = MergeLane<D, NT>::ND;
   constexpr int NV = ND / 2;  // 8-byte loads per split
-  const MergeLane<D> ml(a.hq);
+  // splits whose partials are in flight together
+  constexpr int kMergeBatch = ND >= 4 ? 64 / ND : 16;
+  const MergeLane<D, NT> ml(a.hq);
   if (!ml.on) return;
   const int S = a.n_splits, hq = a.hq;
   const int64_t rb = (int64_t)row * S * hq;
@@ -150,8 +152,15 @@ constexpr int64_t kNarrowCacheBytes = (1ll << 32) - (1ll << 16);
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
+// Waves per workgroup: 4, or 8 for the split instances (few rows: twice the
+// entries per split, half the partials to merge).
+template <bool SPLIT>
+constexpr int attn_waves() { return SPLIT ? 8 : 4; }
+
 template <int D, bool DENSE, bool SPLIT, bool WIDE>
-__global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
+    attn_mfma_kernel(AttnArgs a) {
+  constexpr int NW = attn_waves<SPLIT>(), NT = NW * kWave;
   constexpr int NDT = D / 16;  // 16-wide d tiles of the output
   constexpr int KS = D / 32;   // 32-wide k steps of Q.K
   // LDS bytes per staged V row: 32 bytes more than the row, so that the 8
@@ -161,22 +170,22 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
   // position c ^ (r mod NCH): the 16 rows of one A-fragment read, all at
   // the same chunk, then fall on distinct banks
   constexpr int KP = 2 * D, NCH = D / 8;
-  constexpr int kStage = 4 * kMfmaTileTok * (VP + KP);  // per-wave K and V tiles
-  constexpr int kMerge = 4 * 16 * (D + 2) * 4;         // per-wave results
+  constexpr int kStage = NW * kMfmaTileTok * (VP + KP);  // per-wave K and V tiles
+  constexpr int kMerge = NW * 16 * (D + 2) * 4;         // per-wave results
   // The token rows of the staged list, tile by tile: a tile is 4 entries
   // (blocks) x 4 tokens, kept as [token j][entry i]; each value is the
   // byte offset of the token's row in the K and V arrays (WIDE: its row
   // index).  Tokens not to attend point at the row's own first token.
   __shared__ __align__(16) uint32_t trow[kMfmaEntChunk * 4];
   __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
-  __shared__ int wcnt[4];
+  __shared__ int wcnt[NW];
   __shared__ uint32_t flag;
   // the wave index is uniform: read it once so that what derives from it
   // (the KV head, the wave's tiles, the cache base) stays scalar
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int l = lane_id(), g = l / 16, c16 = l % 16;
   const int hkv = a.hkv, hq = a.hq, G = hq / hkv;
-  const int wph = 4 / hkv;  // waves per KV head
+  const int wph = NW / hkv;  // waves per KV head
   const int hk = w % hkv, wsub = w / hkv;
   const int row = blockIdx.y, split = blockIdx.x;
 
@@ -236,7 +245,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
     // tile but the last holds four whole blocks.  The own block is the last
     // entry of the list, hence the last valid entry of its chunk.
     int nv = 0;
-    for (int i0 = 0; i0 < nloc; i0 += kAttnThreads) {
+    for (int i0 = 0; i0 < nloc; i0 += NT) {
       const int i = i0 + (int)threadIdx.x;
       const int E = cb + i;
       const bool own = (E == n_list);
@@ -247,7 +256,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
       __syncthreads();
       int pos = nv + (int)lanes_below(bal), tot = nv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NW; ++j) {
         const int c = wcnt[j];
         pos += j < w ? c : 0;
         tot += c;
@@ -265,7 +274,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
       nv = tot;
       __syncthreads();
     }
-    for (int i = nv + (int)threadIdx.x; i < ((nv + 3) & ~3); i += kAttnThreads) {
+    for (int i = nv + (int)threadIdx.x; i < ((nv + 3) & ~3); i += NT) {
       uint32_t* tp = trow + (i / 4) * 16 + (i % 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) tp[4 * j] = own_t;
@@ -420,9 +429,9 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
   }
   __syncthreads();
   bf16_t* orow = static_cast<bf16_t*>(a.out) + (int64_t)row * hq * D;
-  // combine the waves of each KV head: thread = (head, D/16 dims)
-  const MergeLane<D> lane(hq);
-  constexpr int ND = MergeLane<D>::ND;
+  // combine the waves of each KV head: thread = (head, its dims)
+  const MergeLane<D, NT> lane(hq);
+  constexpr int ND = MergeLane<D, NT>::ND;
   if (lane.on) {
     const int hk_ = lane.h / G, hh = lane.h % G;
     float M = -INFINITY;
@@ -453,7 +462,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 2 : 3) attn_mfma_kernel(AttnArgs 
   }
   if constexpr (SPLIT) {
     if (!arrive_last(a.cnt + row, (uint32_t)a.n_splits, &flag)) return;
-    merge_splits<D>(a, row, orow);
+    merge_splits<D, NT>(a, row, orow);
   }
 }
 
@@ -467,7 +476,8 @@ void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStr
   const bool split = a.n_splits > 1;
   const bool wide = a.n_slots * a.hkv * d * 2 > kNarrowCacheBytes;
 #define QSA_ATTN_LAUNCH(DD, DN, SP, WD) \
-  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD>), grid, dim3(256), 0, st, a)
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD>), grid, dim3(attn_waves<SP>() * 64), 0, \
+                     st, a)
 #define QSA_ATTN_LAUNCH_W(DD, DN, SP) \
   if (wide) QSA_ATTN_LAUNCH(DD, DN, SP, true); else QSA_ATTN_LAUNCH(DD, DN, SP, false)
   if (d == 128) {
