@@ -108,6 +108,54 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
     return wall, kern, work, ctx
 
 
+def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
+    """One multi-token decode step: pool the newest complete block -> fused
+    scores and exact top-k for each sequence's first draft row -> split-K
+    sparse attention of every draft row over that selection plus its own
+    recent tokens."""
+    from block_sparse_attention_32_amd import pipeline as P
+    log(f"[bench] drawing {wl.name} cache on {dev}")
+    cache = W.make_cache(wl, device=dev)
+    seq_id, pos, sel_of = W.mtp_rows(wl)
+    qs = W.make_queries(wl, cache, seq_id, pos, device=dev)
+    cv = B.CacheView.from_cache(cache)
+    rows = B.QueriesView(qs.seq_id, qs.pos, max(pos))
+    n_blocks = wl.total_len // 4
+    P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
+    sel_of_t = torch.tensor(sel_of, dtype=torch.int32, device=dev)
+    step = P.MtpStep(cv, rows, qs.q, qs.q_idx, qs.w, sel_of_t, wl.n_seqs, wl.top_k, wl.scale)
+    newest = torch.full((wl.n_seqs,), n_blocks - 1, dtype=torch.int32, device=dev)
+
+    def one(timer=None):
+        call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
+        call("pool", B.qsa_pool_blocks, cv, newest, 1)
+        call("topk", step.select)
+        call("attn", step.attend)
+
+    wall, kern = _timed(one, steps, warmup)
+    n_sel = step.n_sel.cpu().numpy()
+    n_tok = int(sum(4 * int(n_sel[s]) + p - 4 * (pos[s] // 4) + 1 for s, p in zip(sel_of, pos)))
+    cand = sum(pos[s] // 4 for s in range(wl.n_seqs))
+    esz = 2 if wl.dtype == "bf16" else 4
+    work = {
+        "topk": {"bytes": cand * wl.di * esz, "bound": "hbm", "kernel": "topk_kernel",
+                 "files": ("index.hip", "index.hpp", "select.hpp", "common.hpp")},
+        "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm",
+                 "kernel": "attn_mfma_kernel",
+                 "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
+        "pool": {"bytes": wl.n_seqs * 5 * wl.di * esz, "bound": "hbm", "kernel": "pool_kernel",
+                 "files": ("index.hip", "index.hpp", "common.hpp")},
+    }
+    dense_ms = None
+    if dense:
+        ds = P.DenseStep(cv, rows, qs.q, wl.scale, "decode")
+        dense_ms = _dense_time(ds.run, max(5, steps // 4))
+    ctx = {"rows": rows.n_rows, "cache": cache, "qs": qs, "pos": pos, "sel_of": sel_of,
+           "launches": 1, "dense_ms": dense_ms,
+           "dense_note": "split-K flash-decode of every draft row over all its tokens"}
+    return wall, kern, work, ctx
+
+
 def _timed(one, steps, warmup):
     for _ in range(warmup):
         one()
@@ -233,6 +281,8 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
                        kidx.double().cpu().numpy(), None]
         return seqs[s]
 
+    if wl.mode == "mtp":
+        return cpu_baseline_mtp(wl, ctx, seq, budget_s)
     if wl.mode == "decode":
         qs, pos = ctx["qs"], ctx["pos"]
         rows = [(s, t, qs.q[i], qs.q_idx[i], qs.w[i]) for i, (s, t) in
@@ -285,6 +335,39 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
                       "; numpy float64 single-threaded"}
 
 
+def cpu_baseline_mtp(wl, ctx, seq, budget_s):
+    """Oracle of a multi-token decode step: one selection per sequence, then
+    every draft row attends it plus its own recent tokens; repeated steps."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    qs, pos, sel_of = ctx["qs"], ctx["pos"], ctx["sel_of"]
+    seq_ids = qs.seq_id.cpu().tolist()
+    q = qs.q.double().cpu().numpy()
+    qi = qs.q_idx.double().cpu().numpy()
+    w = qs.w.double().cpu().numpy()
+    for s in set(seq_ids):
+        e = seq(s)
+        if e[3] is None:
+            e[3] = O.pool_blocks(e[2], wl.dtype)        # set-up, untimed
+    done, el = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while el < budget_s:
+            sels = {}
+            for i, s in enumerate(seq_ids):
+                k, v, _, kbar = seq(s)
+                r = sel_of[i]
+                if r not in sels:
+                    sels[r] = O.qsa_select_row(kbar, qi[r], w[r], pos[r], wl.top_k)
+                O.attend(q[i], k, v, O.token_set_shared(sels[r], pos[r], pos[i]), wl.scale)
+                done += 1
+            el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} draft rows of {wl.name} ({done // len(seq_ids)} repeated steps: "
+                      f"select once per sequence, attend every row; {el:.1f} s); numpy float64 "
+                      "single-threaded"}
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -311,7 +394,7 @@ def main():
     B.lib()  # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
-    decode = wl.mode == "decode"
+    decode = wl.mode in ("decode", "mtp")
     steps = args.steps if args.steps is not None else (200 if decode else 3)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 1)
     if args.copy_calibration:
@@ -321,7 +404,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if decode:
+    if wl.mode == "mtp":
+        wall, timer, work, ctx = run_mtp(wl, steps, warmup, dev, dense=not args.no_dense)
+    elif decode:
         wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=not args.no_dense)
     else:
         wall, timer, work, ctx = run_prefill(wl, steps, warmup, dev, dense=not args.no_dense,

@@ -20,13 +20,15 @@ QSA_BLOCK = 4
 QSA_MAX_TOPK = 512
 QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_TOPK, QSA_OP_ATTN_DECODE, QSA_OP_ATTN_PREFILL = 0, 1, 2
-QSA_OP_DENSE_DECODE, QSA_OP_DENSE_PREFILL = 3, 4
+QSA_OP_DENSE_DECODE, QSA_OP_DENSE_PREFILL, QSA_OP_ATTN_DECODE_SHARED = 3, 4, 5
+QSA_MAX_SHARED_LAG = 60
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error"}
 
 SYMBOLS = (
     "qsa_pool_blocks", "qsa_index_scores", "qsa_topk_blocks", "qsa_attn_decode",
-    "qsa_attn_prefill", "qsa_dense_attn_decode", "qsa_dense_attn_prefill",
+    "qsa_attn_decode_shared", "qsa_attn_prefill", "qsa_dense_attn_decode",
+    "qsa_dense_attn_prefill",
     "qsa_workspace_size", "qsa_status_string", "qsa_version",
 )
 
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "qsa_index_scores": [P, P, P, P, I32, P, I64, P],
             "qsa_topk_blocks": [P, P, P, I64, P, P, I32, I32, P, P, P, SZ, P],
             "qsa_attn_decode": [P, P, P, I32, P, P, I32, F, P, P, SZ, P],
+            "qsa_attn_decode_shared": [P, P, P, I32, P, P, P, I32, F, P, P, SZ, P],
             "qsa_attn_prefill": [P, P, P, I32, P, P, I32, F, P, P, SZ, P],
             "qsa_dense_attn_decode": [P, P, P, I32, F, P, P, SZ, P],
             "qsa_dense_attn_prefill": [P, P, P, I32, F, P, P, SZ, P],
@@ -242,6 +245,20 @@ def _attn(name, cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream):
 
 def qsa_attn_decode(cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream=None):
     _attn("qsa_attn_decode", cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream)
+
+
+def qsa_attn_decode_shared(cache, queries, q, sel, n_sel, sel_of, top_k, scale, out, ws,
+                           stream=None):
+    """Decode rows reusing the selection of row sel_of[i] (draft tokens of a
+    multi-token step): see qsa_attn_decode_shared in include/qsa.h."""
+    _check(q, "q", cache.dtype, cache.device)
+    _check(out, "out", cache.dtype, cache.device)
+    for t, n in ((sel, "sel"), (n_sel, "n_sel"), (sel_of, "sel_of")):
+        _check(t, n, torch.int32, cache.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("qsa_attn_decode_shared", cache.ref, queries.ref, _ptr(q), int(q.shape[1]), _ptr(sel),
+          _ptr(n_sel), _ptr(sel_of), int(top_k), ctypes.c_float(scale), _ptr(out), _ptr(ws),
+          wsb, _stream(stream))
 
 
 def qsa_attn_prefill(cache, queries, q, sel, n_sel, top_k, scale, out, ws=None, stream=None):

@@ -127,8 +127,12 @@ struct AttnPlan {
 AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, int top_k) {
   AttnPlan p;
   const bool dense = (op == QSA_OP_DENSE_DECODE || op == QSA_OP_DENSE_PREFILL);
-  const bool split = (op == QSA_OP_ATTN_DECODE || op == QSA_OP_DENSE_DECODE);
-  const int entries = (dense ? qm->max_pos / QSA_BLOCK : top_k) + 1;
+  const bool split = (op == QSA_OP_ATTN_DECODE || op == QSA_OP_DENSE_DECODE ||
+                     op == QSA_OP_ATTN_DECODE_SHARED);
+  // a row reusing another row's selection also attends up to kMaxBridge
+  // whole blocks before its own
+  const int entries = (dense ? qm->max_pos / QSA_BLOCK : top_k) + 1 +
+                      (op == QSA_OP_ATTN_DECODE_SHARED ? kMaxBridge : 0);
   p.mfma = attn_mfma_supported(c->dtype, hq, c->n_kv_heads, c->head_dim) ? 1 : 0;
   p.tile = p.mfma ? kMfmaTileTok : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
   const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
@@ -167,7 +171,7 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
 qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, const void* q,
                             int32_t hq, const int32_t* sel, const int32_t* n_sel,
                             int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, const int32_t* sel_of = nullptr) {
   qsa_status st = check_cache(c);
   if (st != QSA_OK) return st;
   if ((st = check_queries(c, qm)) != QSA_OK) return st;
@@ -176,6 +180,7 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
   if (hq * c->head_dim > kMaxOutPerThread * kAttnThreads) return QSA_ERR_UNSUPPORTED;
   if (!dense && (top_k < 1 || top_k > QSA_MAX_TOPK)) return QSA_ERR_INVALID_ARG;
   if (!dense && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
+  if (op == QSA_OP_ATTN_DECODE_SHARED && sel_of == nullptr) return QSA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || scale != scale) return QSA_ERR_INVALID_ARG;
   if (qm->n_rows > 0 && (q == nullptr || out == nullptr)) return QSA_ERR_INVALID_ARG;
   if (c->k == nullptr || c->v == nullptr) return QSA_ERR_INVALID_ARG;
@@ -199,6 +204,8 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
   a.max_pos = qm->max_pos;
   a.sel = sel;
   a.n_sel = n_sel;
+  a.sel_of = sel_of;
+  a.n_rows = qm->n_rows;
   a.top_k = top_k;
   a.scale = scale;
   a.n_splits = p.splits;
@@ -366,6 +373,14 @@ qsa_status qsa_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void
                           out, ws, ws_bytes, stream);
 }
 
+qsa_status qsa_attn_decode_shared(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                                  int32_t n_q_heads, const int32_t* sel, const int32_t* n_sel,
+                                  const int32_t* sel_of, int32_t top_k, float scale, void* out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return attention_common(QSA_OP_ATTN_DECODE_SHARED, c, qm, q, n_q_heads, sel, n_sel, top_k,
+                          scale, out, ws, ws_bytes, stream, sel_of);
+}
+
 qsa_status qsa_attn_prefill(const qsa_cache* c, const qsa_queries* qm, const void* q,
                             int32_t n_q_heads, const int32_t* sel, const int32_t* n_sel,
                             int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
@@ -398,6 +413,7 @@ size_t qsa_workspace_size(int32_t op, const qsa_cache* c, const qsa_queries* qm,
       return a > b ? a : b;
     }
     case QSA_OP_ATTN_DECODE:
+    case QSA_OP_ATTN_DECODE_SHARED:
     case QSA_OP_ATTN_PREFILL:
     case QSA_OP_DENSE_DECODE:
     case QSA_OP_DENSE_PREFILL:

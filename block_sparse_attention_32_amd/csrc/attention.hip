@@ -43,11 +43,11 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
 
   const int seq = min(max(a.seq_id[row], 0), a.n_seqs - 1);
   const int t = min(max(a.pos[row], 0), a.max_pos);
-  const int b_own = t / kBlock;
-  // selected ids outside [0, b_own) are skipped, n_sel is clamped to [0, top_k]
-  const int n_list = DENSE ? b_own : min(max(a.n_sel[row], 0), a.top_k);
-  const int n_entries = n_list + 1;
-  const int* sel_row = DENSE ? nullptr : a.sel + (int64_t)row * a.top_k;
+  // n_sel is clamped to [0, top_k]; selected ids the row may not attend are
+  // skipped
+  const RowList rl(a, row, t, DENSE);
+  const int b_own = rl.b_own;
+  const int n_entries = rl.e_own + 1;
   const int e_beg = split * a.eps;
   const int e_end = min(n_entries, e_beg + a.eps);
 
@@ -73,10 +73,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
       const int e = e0 + j / kBlock, i = j % kBlock;
       int64_t r = -1;
       if (e < e_end) {
-        const bool own = (e == n_list);
-        const int b = own ? b_own : (DENSE ? e : sel_row[e]);
+        const bool own = (e == rl.e_own);
+        bool ok = true;
+        const int b = own ? b_own : rl.block(e, DENSE, ok);
         const int ntok = own ? (t % kBlock) + 1 : kBlock;
-        const bool ok = own || (b >= 0 && b < b_own);
         if (ok && i < ntok) r = a.pm.token_slot(seq, b * kBlock + i);
       }
       trow[j] = r;

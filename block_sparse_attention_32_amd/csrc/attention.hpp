@@ -31,6 +31,44 @@ struct AttnArgs {
   float* part_ml;         // [T][n_splits][hq][2]
   uint32_t* cnt;          // [T]
   int64_t n_slots;        // token rows of the K and V arrays (pages x page size)
+  const int32_t* sel_of;  // [T] or null: row i reuses the selection of row sel_of[i]
+  int n_rows;             // T
+};
+
+// A row reusing another row's selection attends at most this many whole
+// blocks between that row's own block and its own (QSA_MAX_SHARED_LAG).
+constexpr int kMaxBridge = (QSA_MAX_SHARED_LAG + QSA_BLOCK - 1) / QSA_BLOCK;
+
+// The block list of one row: n_list selected entries, then n_bridge whole
+// blocks b_sel .. b_own - 1, then the own block (the last entry).  Selected
+// ids outside [0, b_sel) are skipped.
+struct RowList {
+  int b_own, b_sel, n_list, n_bridge, e_own;
+  const int32_t* sel;
+  __device__ __forceinline__ RowList(const AttnArgs& a, int row, int t, bool dense) {
+    b_own = t / QSA_BLOCK;
+    int rs = row;
+    b_sel = b_own;
+    if (!dense && a.sel_of != nullptr) {
+      rs = min(max(a.sel_of[row], 0), a.n_rows - 1);
+      const int ts = min(max(a.pos[rs], 0), a.max_pos);
+      b_sel = max(min(ts / QSA_BLOCK, b_own), b_own - kMaxBridge);
+    }
+    n_list = dense ? b_own : min(max(a.n_sel[rs], 0), a.top_k);
+    n_bridge = b_own - b_sel;
+    e_own = n_list + n_bridge;
+    sel = dense ? nullptr : a.sel + (int64_t)rs * a.top_k;
+  }
+  // block of entry e (< e_own) and whether it is attended
+  __device__ __forceinline__ int block(int e, bool dense, bool& ok) const {
+    if (e >= n_list) {
+      ok = true;
+      return b_sel + (e - n_list);
+    }
+    const int b = dense ? e : sel[e];
+    ok = b >= 0 && b < b_sel;
+    return b;
+  }
 };
 
 // LDS layout of the generic kernel (byte offsets, each 16-byte aligned).

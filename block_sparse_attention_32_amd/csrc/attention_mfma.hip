@@ -191,10 +191,9 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
 
   const int seq = min(max(a.seq_id[row], 0), a.n_seqs - 1);
   const int t = min(max(a.pos[row], 0), a.max_pos);
-  const int b_own = t / kBlock;
-  const int n_list = DENSE ? b_own : min(max(a.n_sel[row], 0), a.top_k);
-  const int n_entries = n_list + 1;
-  const int* sel_row = DENSE ? nullptr : a.sel + (int64_t)row * a.top_k;
+  const RowList rl(a, row, t, DENSE);
+  const int b_own = rl.b_own;
+  const int n_entries = rl.e_own + 1;
   const int e_beg = split * a.eps;
   const int e_end = min(n_entries, e_beg + a.eps);
   const int tail = (t % kBlock) + 1;  // tokens of the own block
@@ -248,9 +247,10 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     for (int i0 = 0; i0 < nloc; i0 += NT) {
       const int i = i0 + (int)threadIdx.x;
       const int E = cb + i;
-      const bool own = (E == n_list);
-      const int b = i >= nloc ? -1 : (own ? b_own : (DENSE ? E : sel_row[E]));
-      const bool ok = i < nloc && (own || (b >= 0 && b < b_own));
+      const bool own = (E == rl.e_own);
+      bool ok = i < nloc;
+      int b = b_own;
+      if (ok && !own) b = rl.block(E, DENSE, ok);
       const uint64_t bal = __ballot(ok);
       if (l == 0) wcnt[w] = __popcll(bal);
       __syncthreads();
@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     __syncthreads();
     const int n_tiles = (nv + 3) / 4;
     const int last = n_tiles - 1;
-    const bool own_here = n_list >= cb && n_list < cb + nloc;
+    const bool own_here = rl.e_own >= cb && rl.e_own < cb + nloc;
     // A tile is 16 tokens, tile row 4i + j = entry i, token j.  The K and
     // V rows of the wave's next tile are loaded while the current one is
     // computed, both the same way: load i reads entry i, lane group g its

@@ -55,6 +55,39 @@ class QsaStep:
         return self.sel, self.n_sel, self.out
 
 
+class MtpStep:
+    """A multi-token decode step (draft tokens of speculative decoding): the
+    selection is made for rows 0 .. n_sel_rows - 1 only (each sequence's
+    first draft row) and every row attends the selection of row sel_of[i]
+    plus its own recent tokens (qsa_attn_decode_shared)."""
+
+    def __init__(self, cache: B.CacheView, rows: B.QueriesView, q, q_idx, w, sel_of,
+                 n_sel_rows: int, top_k: int, scale: float):
+        self.cache, self.rows, self.q = cache, rows, q
+        self.top_k, self.scale, self.n = int(top_k), float(scale), int(n_sel_rows)
+        dev = cache.device
+        t = rows.n_rows
+        n = self.n
+        self.sel_of = sel_of
+        self.q_idx, self.w = q_idx[:n], w[:n]
+        self.sel = torch.full((t, self.top_k), -1, dtype=torch.int32, device=dev)
+        self.n_sel = torch.zeros((t,), dtype=torch.int32, device=dev)
+        seq_id, pos = rows.tensors
+        self.sel_rows = B.QueriesView(seq_id[:n], pos[:n], rows.s.max_pos)
+        self.out = torch.empty_like(q)
+        self.ws_topk = B.workspace(B.QSA_OP_TOPK, cache, self.sel_rows, 0, self.top_k)
+        self.ws_attn = B.workspace(B.QSA_OP_ATTN_DECODE_SHARED, cache, rows, q.shape[1],
+                                   self.top_k)
+
+    def select(self):
+        B.qsa_topk_blocks(self.cache, self.sel_rows, self.top_k, self.sel[: self.n],
+                          self.n_sel[: self.n], self.ws_topk, q_idx=self.q_idx, w=self.w)
+
+    def attend(self):
+        B.qsa_attn_decode_shared(self.cache, self.rows, self.q, self.sel, self.n_sel,
+                                 self.sel_of, self.top_k, self.scale, self.out, self.ws_attn)
+
+
 class DenseStep:
     """Dense causal GQA attention of the same rows (comparison baseline)."""
 

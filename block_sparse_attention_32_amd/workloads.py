@@ -36,7 +36,7 @@ BLOCK_TOKENS = 4  # micro-block length used to place needles
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str               # "decode" or "prefill"
+    mode: str               # "decode", "prefill" or "mtp" (multi-token decode)
     dtype: str              # "f32" or "bf16"
     n_seqs: int
     n_ctx: int              # tokens already cached before this step's rows
@@ -74,7 +74,8 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads the method is measured on.
+# The workloads the method is measured on (mtp4_1m: four draft tokens of a
+# multi-token decode step at 1M context sharing one selection).
 WORKLOADS = {
     "tiny_decode": Workload(
         name="tiny_decode", mode="decode", dtype="f32", n_seqs=1, n_ctx=64,
@@ -88,6 +89,10 @@ WORKLOADS = {
         name="decode_1m", mode="decode", dtype="bf16", n_seqs=1,
         n_ctx=1048576, n_new=1, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
         needle_depths=(0.0, 0.25, 0.5, 0.75, 0.99), seed=1003),
+    "mtp4_1m": Workload(
+        name="mtp4_1m", mode="mtp", dtype="bf16", n_seqs=1,
+        n_ctx=1048576, n_new=4, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
+        needle_depths=(0.0, 0.25, 0.5, 0.75, 0.99), seed=1006),
     "prefill_8k_at_128k": Workload(
         name="prefill_8k_at_128k", mode="prefill", dtype="bf16", n_seqs=1,
         n_ctx=131072, n_new=8192, hq=16, hkv=2, d=128, hi=4, di=64,
@@ -161,6 +166,8 @@ def make_cache(wl: Workload, device="cpu", seed: int | None = None) -> Cache:
     # existing context) or of the whole sequence (full prefill)
     if wl.mode == "decode":
         n_blocks_visible = (wl.total_len - 1) // BLOCK_TOKENS
+    elif wl.mode == "mtp":  # the candidates of the draft rows' shared selection
+        n_blocks_visible = wl.n_ctx // BLOCK_TOKENS
     elif wl.n_ctx > 0:
         n_blocks_visible = wl.n_ctx // BLOCK_TOKENS
     else:
@@ -239,7 +246,26 @@ def prefill_rows(wl: Workload, chunk_index: int = 0):
     return [0] * len(pos), pos
 
 
+def mtp_rows(wl: Workload):
+    """(seq_id, pos, sel_of) of a multi-token decode step: the n_new draft
+    tokens of every sequence (positions n_ctx .. n_ctx + n_new - 1).  The
+    first draft row of each sequence comes first (rows 0 .. n_seqs - 1): the
+    selection is made for it, and every draft row of the sequence reuses it
+    (sel_of = the sequence's first row)."""
+    seq_id = list(range(wl.n_seqs))
+    pos = [wl.n_ctx] * wl.n_seqs
+    sel_of = list(range(wl.n_seqs))
+    for s in range(wl.n_seqs):
+        for j in range(1, wl.n_new):
+            seq_id.append(s)
+            pos.append(wl.n_ctx + j)
+            sel_of.append(s)
+    return seq_id, pos, sel_of
+
+
 def step_rows(wl: Workload, chunk_index: int = 0):
+    if wl.mode == "mtp":
+        return mtp_rows(wl)[:2]
     return decode_rows(wl) if wl.mode == "decode" else prefill_rows(wl, chunk_index)
 
 

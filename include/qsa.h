@@ -66,6 +66,7 @@ extern "C" {
 #define QSA_BLOCK 4        /* tokens per micro-block */
 #define QSA_MAX_TOPK 512   /* largest supported top_k (the pages' budget) */
 #define QSA_MAX_BLOCKS (1 << 20) /* candidate blocks per query (4M tokens) */
+#define QSA_MAX_SHARED_LAG 60    /* qsa_attn_decode_shared: pos[i] - pos[sel_of[i]] */
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -82,7 +83,8 @@ typedef enum qsa_op {
   QSA_OP_ATTN_DECODE = 1,
   QSA_OP_ATTN_PREFILL = 2,
   QSA_OP_DENSE_DECODE = 3,
-  QSA_OP_DENSE_PREFILL = 4
+  QSA_OP_DENSE_PREFILL = 4,
+  QSA_OP_ATTN_DECODE_SHARED = 5
 } qsa_op;
 
 /* Paged cache shared by K, V, the indexer keys and the pooled block keys.
@@ -177,6 +179,25 @@ qsa_status qsa_attn_prefill(const qsa_cache *c, const qsa_queries *qm,
                             const int32_t *sel, const int32_t *n_sel,
                             int32_t top_k, float scale, void *out, void *ws,
                             size_t ws_bytes, void *stream);
+
+/* Multi-token decode with one selection reused across draft positions
+ * (keieiax.jp glossary, FAQ on whether the selection is shared across
+ * layers: multi-token prediction may reuse the top index across its
+ * speculative steps).  Row i attends the selection made for row
+ * s = sel_of[i] (a row of the same call, same sequence, at position
+ * pos[s] <= pos[i] <= pos[s] + QSA_MAX_SHARED_LAG), and everything from the
+ * start of that row's own block up to its own position:
+ *   S_i = {4b .. 4b+3 : b in sel[s][0 .. n_sel[s]-1], b < pos[s]/4}
+ *         U {4*(pos[s]/4) .. pos[i]}
+ * sel_of[i] = i gives exactly qsa_attn_decode's result.  sel_of: [T] device
+ * int32; rows outside the limits above are clamped to them (their result
+ * is unspecified).  ws: qsa_workspace_size(QSA_OP_ATTN_DECODE_SHARED, ...). */
+qsa_status qsa_attn_decode_shared(const qsa_cache *c, const qsa_queries *qm,
+                                  const void *q, int32_t n_q_heads,
+                                  const int32_t *sel, const int32_t *n_sel,
+                                  const int32_t *sel_of, int32_t top_k,
+                                  float scale, void *out, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* Comparison baseline (glossary: dense GQA attention kernels): causal
  * attention of every row over all tokens 0..pos[i] of its sequence, same

@@ -195,6 +195,22 @@ def token_set(sel: np.ndarray, t: int) -> np.ndarray:
     return np.asarray(toks, dtype=np.int64)
 
 
+def token_set_shared(sel: np.ndarray, t_sel: int, t: int) -> np.ndarray:
+    """Tokens attended at position t >= t_sel by a query that reuses the
+    selection made for the query at t_sel (multi-token prediction reusing
+    the top index across speculative steps: [QSA glossary], FAQ on whether
+    the selection is shared across layers).
+
+    Reading: the reused selection stands for the context before t_sel's own
+    block; every token from the start of that block up to t is attended
+    (the tail grows with the drafted tokens).  For t == t_sel this is
+    token_set(sel, t).
+    """
+    toks = [BLOCK * int(b) + i for b in sel for i in range(BLOCK)]
+    toks += list(range(BLOCK * own_block(t_sel), t + 1))
+    return np.asarray(toks, dtype=np.int64)
+
+
 # --------------------------------------------------------------------------
 # step 6: attention over the token set
 # --------------------------------------------------------------------------

@@ -58,6 +58,8 @@ def test_workspace_sizes(libqsa):
     assert ws(B.QSA_OP_ATTN_PREFILL, R(c), R(q), 16, 512) == 0   # one workgroup per row
     assert ws(B.QSA_OP_DENSE_PREFILL, R(c), R(q), 16, 0) == 0
     assert ws(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 512) == ws(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 512)
+    # rows reusing a selection also attend the bridge blocks: never less
+    assert ws(B.QSA_OP_ATTN_DECODE_SHARED, R(c), R(q), 16, 512) >= ws(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 512)
     assert ws(99, R(c), R(q), 16, 512) == 0
     assert ws(B.QSA_OP_TOPK, None, R(q), 0, 512) == 0
     # bigger problems never need less
@@ -110,6 +112,11 @@ def test_call_validation(libqsa):
     assert ad(R(c), R(q), 8, 16, 8, 8, 512, f(0.1), 8, 8, wd - 1, None) == -3
     assert ad(R(c), R(q), 8, 64, 8, 8, 512, f(0.1), 8, 8, wd, None) == -2       # Hq*D > 4096
     assert L.qsa_dense_attn_decode(R(c), R(q), 8, 16, f(0.1), 8, None, 0, None) == -3
+    wsh = L.qsa_workspace_size(B.QSA_OP_ATTN_DECODE_SHARED, R(c), R(q), 16, 512)
+    sh = L.qsa_attn_decode_shared
+    assert sh(R(c), R(q), 8, 16, 8, 8, None, 512, f(0.1), 8, 8, wsh, None) == -1   # no sel_of
+    assert sh(R(c), R(q), 8, 16, 8, 8, 8, 512, f(0.1), 8, 8, wsh - 1, None) == -3
+    assert sh(R(c), R(q), 8, 16, 8, 8, 8, 0, f(0.1), 8, 8, wsh, None) == -1       # top_k 0
     # zero rows: valid and a no-op
     z = _rows(n_rows=0, seq_id=None, pos=None)
     assert L.qsa_attn_prefill(R(c), R(z), None, 16, 8, 8, 512, f(0.1), None, None, 0, None) == 0

@@ -286,6 +286,59 @@ def test_attention_skips_invalid_entries(gpu, mode):
         assert err <= TOL[wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
 
 
+# draft groups (selection position, lags of the rows reusing it); lag 0 is
+# the row the selection was made for
+SHARED_GROUPS = {
+    "tiny": [(20, [0, 1, 2, 3]), (50, [0, 5, 13])],
+    "mixed": [(2047, [0, 1, 2, 3]), (2050, [0, 1, 2, 3]), (32766, [0, 2, 4, 9]),
+              (40000, [0, 60]), (40003, [0, 57, 60]), (59940, [0, 60])],
+}
+
+
+@pytest.mark.parametrize("case", ["tiny", "mixed"])
+def test_attention_decode_shared_selection(gpu, case):
+    """Draft rows of a multi-token decode step reuse their group's selection
+    and attend everything from the selection row's own block on; compared
+    with the oracle's token_set_shared.  Rows that are not selection rows
+    carry a poisoned selection of their own, which must not be read."""
+    _say(f"attention shared selection {case}")
+    pos, sel_of = [], []
+    for t_s, lags in SHARED_GROUPS[case]:
+        first = len(pos)
+        for lag in lags:
+            pos.append(t_s + lag)
+            sel_of.append(first)
+    wl0 = WL["tiny_decode"] if case == "tiny" else MIXED
+    pb = Problem(wl0, gpu, [0] * len(pos), pos)
+    wl = pb.wl
+    T = len(pos)
+    sel = torch.full((T, wl.top_k), -1, dtype=torch.int32)
+    n_sel = torch.full((T,), wl.top_k, dtype=torch.int32)   # poison for non-selection rows
+    sels = {}
+    for i in range(T):
+        if sel_of[i] == i:
+            s_ = pb.oracle_select(i)
+            sels[i] = s_
+            sel[i, : len(s_)] = torch.from_numpy(s_.astype(np.int32))
+            n_sel[i] = len(s_)
+        else:
+            sel[i] = torch.arange(wl.top_k, dtype=torch.int32)  # must not be used
+    out = torch.full_like(pb.qs.q, float("nan"))
+    ws = B.workspace(B.QSA_OP_ATTN_DECODE_SHARED, pb.cv, pb.rows, wl.hq, wl.top_k)
+    B.qsa_attn_decode_shared(pb.cv, pb.rows, pb.qs.q, sel.to(gpu), n_sel.to(gpu),
+                             torch.tensor(sel_of, dtype=torch.int32, device=gpu), wl.top_k,
+                             wl.scale, out, ws)
+    torch.cuda.synchronize()
+    got = f64(out)
+    for i in range(T):
+        s_ = sel_of[i]
+        toks = O.token_set_shared(sels[s_], pos[s_], pos[i])
+        k, v = pb.token_kv(0, toks)
+        want = O.attend(f64(pb.qs.q[i]), k, v, np.arange(len(toks)), wl.scale)
+        err = np.abs(got[i] - want).max()
+        assert err <= TOL[wl.dtype], f"row {i} t={pos[i]} (selection at {pos[s_]}) err={err}"
+
+
 def test_attention_cache_over_4gib(gpu):
     """K and V arrays over 4 GiB each (rows addressed with 64-bit offsets):
     the sequence's pages sit at the top of the arrays."""
@@ -425,6 +478,37 @@ def test_e2e_decode_configs(gpu, name):
     _, sel, n = sel_rows(st.sel, st.n_sel)
     for i, s in enumerate(pb.seq_id_list):
         assert set(pb.cache.needles[s]) <= set(sel[i, : n[i]].tolist())
+
+
+@pytest.mark.parametrize("n_ctx", [60000, 1048576], ids=["60k", "1m"])
+def test_e2e_mtp_step(gpu, n_ctx):
+    """A whole multi-token decode step (the mtp workload recipe): pooling,
+    the fused top-k of each sequence's first draft row (bit-exact), then
+    every draft row over that selection plus its recent tokens."""
+    wl = WL["mtp4_1m"].replace(n_ctx=n_ctx, n_seqs=2 if n_ctx < 100000 else 1, n_new=4)
+    _say(f"e2e mtp {wl.name} n_ctx={n_ctx} seqs={wl.n_seqs}")
+    seq_id, pos, sel_of = W.mtp_rows(wl)
+    pb = Problem(wl, gpu, seq_id, pos)
+    pb.pool_all()
+    st = P.MtpStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w,
+                   torch.tensor(sel_of, dtype=torch.int32, device=gpu), wl.n_seqs, wl.top_k,
+                   wl.scale)
+    st.select()
+    st.attend()
+    torch.cuda.synchronize()
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    got = f64(st.out)
+    sels = {}
+    for r in range(wl.n_seqs):
+        sels[r] = pb.oracle_select(r)
+        assert_sel_row(sel[r], int(n[r]), sels[r], wl.top_k)
+    for i in range(len(pos)):
+        r = sel_of[i]
+        toks = O.token_set_shared(sels[r], pos[r], pos[i])
+        k, v = pb.token_kv(seq_id[i], toks)
+        want = O.attend(f64(pb.qs.q[i]), k, v, np.arange(len(toks)), wl.scale)
+        err = np.abs(got[i] - want).max()
+        assert err <= TOL[wl.dtype], f"row {i} t={pos[i]} err={err}"
 
 
 def test_e2e_prefill_8k_at_128k(gpu):

@@ -24,6 +24,10 @@ MUTATIONS = {
                       "order = np.lexsort((ids, scores))"),
     "own_block_cut": ("toks += list(range(BLOCK * own_block(t), t + 1))",
                       "toks += list(range(BLOCK * own_block(t), t))"),
+    "shared_tail_from_own_block": ("range(BLOCK * own_block(t_sel), t + 1)",
+                                   "range(BLOCK * own_block(t), t + 1)"),
+    "shared_tail_cut": ("range(BLOCK * own_block(t_sel), t + 1)",
+                        "range(BLOCK * own_block(t_sel), t)"),
     "own_block_competes": ("return own_block(t)\n", "return own_block(t) + 1\n"),
     "gqa_interleaved": ("return hq // (n_q_heads // n_kv_heads)",
                         "return hq % n_kv_heads"),

@@ -215,6 +215,39 @@ def test_token_set_closed_form():
     assert O.token_set(np.array([1]), 11).tolist() == [4, 5, 6, 7, 8, 9, 10, 11]
 
 
+def test_token_set_shared_closed_form():
+    """A query reusing the selection made 4 positions earlier: the reused
+    blocks, then everything from the earlier query's own block on."""
+    assert O.token_set_shared(np.array([0, 2]), 13, 17).tolist() == \
+        [0, 1, 2, 3, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17]
+    assert O.token_set_shared(np.array([], dtype=np.int64), 3, 5).tolist() == [0, 1, 2, 3, 4, 5]
+    # the drafted tokens cross into the next block: 8..9 join the tail
+    assert O.token_set_shared(np.array([0]), 6, 9).tolist() == list(range(10))
+
+
+@pytest.mark.parametrize("t_sel", [0, 5, 13, 40])
+def test_token_set_shared_reduces_to_token_set(t_sel):
+    rng = np.random.default_rng(t_sel)
+    n = t_sel // 4
+    sel = np.sort(rng.choice(n, size=min(n, 3), replace=False)) if n else np.array([], np.int64)
+    assert O.token_set_shared(sel, t_sel, t_sel).tolist() == O.token_set(sel, t_sel).tolist()
+
+
+@pytest.mark.parametrize("t_sel,t", [(13, 13), (13, 16), (13, 19), (6, 30), (0, 3)])
+def test_shared_selection_covering_context_is_dense(t_sel, t):
+    """When the reused selection holds every block before t_sel's own block,
+    a later draft position attends its whole causal prefix: the result is
+    dense causal attention (pinned to torch SDPA above)."""
+    rng = np.random.default_rng(t)
+    k = rng.standard_normal((t + 1, 2, 8))
+    v = rng.standard_normal((t + 1, 2, 8))
+    q = rng.standard_normal((4, 8))
+    sel = np.arange(t_sel // 4)
+    got = O.attend(q, k, v, O.token_set_shared(sel, t_sel, t), 0.3)
+    want = O.dense_causal(q[None], k, v, np.array([t]), 0.3)[0]
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- attention
 
 def _sdpa(q, k, v, mask, scale):
