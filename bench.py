@@ -104,7 +104,8 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
         ds = P.DenseStep(cv, rows, qs.q, wl.scale, "decode")
         dense_ms = _dense_time(ds.run, max(5, steps // 4))
     ctx = {"rows": rows.n_rows, "cache": cache, "qs": qs, "pos": pos, "launches": 1,
-           "dense_ms": dense_ms, "dense_note": "split-K flash-decode over all tokens"}
+           "dense_ms": dense_ms, "dense_note": "split-K flash-decode over all tokens",
+           "step": step}
     return wall, kern, work, ctx
 
 
@@ -151,7 +152,7 @@ def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
         ds = P.DenseStep(cv, rows, qs.q, wl.scale, "decode")
         dense_ms = _dense_time(ds.run, max(5, steps // 4))
     ctx = {"rows": rows.n_rows, "cache": cache, "qs": qs, "pos": pos, "sel_of": sel_of,
-           "launches": 1, "dense_ms": dense_ms,
+           "launches": 1, "dense_ms": dense_ms, "step": step,
            "dense_note": "split-K flash-decode of every draft row over all its tokens"}
     return wall, kern, work, ctx
 
@@ -261,6 +262,42 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
     ctx.update(dense_ms=dense_ms, dense_note=note,
                dense_tflops=sum(dense_flop) / (dense_ms * 1e-3) / 1e12)
     return wall, kern, work, ctx
+
+
+# ------------------------------------------------------------------ memory
+
+def memory_report(wl, ctx, dev):
+    """Device memory of the mask-free hand-off against a materialised kq_mask
+    for the largest call of the step (the last prefill chunk, or the decode
+    rows): the selection and the workspaces the library needs (sel, n_sel,
+    top-k and attention workspaces) versus a float16 [rows x keys] mask of
+    the same rows, which is allocated and filled here so that its footprint
+    is measured (free device memory before and after), not just computed."""
+    if wl.mode == "prefill":
+        st, pos = ctx["chunks"][-1][0], ctx["chunks"][-1][3]
+    else:
+        st, pos = ctx["step"], ctx["pos"]
+    rows, keys = len(pos), max(pos) + 1
+    free_bytes = sum(t.numel() * t.element_size()
+                     for t in (st.sel, st.n_sel, st.ws_topk, st.ws_attn))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free0 = torch.cuda.mem_get_info(dev)[0]
+    mask = torch.empty((rows, keys), dtype=torch.float16, device=dev)
+    mask.fill_(float("-inf"))
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info(dev)[0]
+    del mask
+    torch.cuda.empty_cache()
+    need = rows * keys * 2
+    seen = int(free0 - free1)
+    return {"rows": rows, "keys": keys, "kq_mask_bytes": need,
+            # below the allocator's granularity the free-memory reading does not move
+            "kq_mask_measured_bytes": seen if seen >= need // 2 else None,
+            "mask_free_bytes": int(free_bytes),
+            "how": "float16 [rows x keys] mask allocated and filled (measured as the drop in "
+                   "free device memory); mask-free = sel + n_sel + top-k and attention "
+                   "workspaces of the same call"}
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -381,6 +418,8 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="prefill: run each chunk's attention on a second stream, beside the "
                          "next chunk's selection (per-kernel times then overlap)")
+    ap.add_argument("--no-memory", action="store_true",
+                    help="skip the mask-free vs materialised-kq_mask memory measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -458,6 +497,8 @@ def main():
                             "how": ctx.get("dense_note", "")}
         if "dense_tflops" in ctx:
             out["dense_gqa"]["achieved_tflops"] = round(ctx["dense_tflops"], 1)
+    if not args.no_memory:
+        out["memory"] = memory_report(wl, ctx, dev)
     out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ctx)
     print(json.dumps(out), flush=True)
 
