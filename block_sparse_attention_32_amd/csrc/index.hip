@@ -180,7 +180,7 @@ __device__ __forceinline__ void load_row_query(typename RowQuery<T, DI, HI>::typ
 // workgroup into keys[] (ordered keys; blocks >= n get key 0).  All of a
 // thread's loads of a pass are issued before any is used.
 template <typename T, int DI, int HI>
-__device__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
+__device__ __forceinline__ void chunk_scores(const IdxArgs& a, int seq, int n, int c0,
                              const typename RowQuery<T, DI, HI>::type& iq, int32_t* pages,
                              uint32_t* keys) {
   constexpr bool kBf = std::is_same<T, bf16_t>::value;
@@ -286,18 +286,25 @@ template <typename T, int DI>
 struct RowKeys {
   const float* given;
   const uint32_t* stored;
-  const TopkArgs* t;
-  int row, seq;
+  const T* kbar;
+  const T* qrow;     // the row's q_idx, [hi][DI]
+  const float* wrow; // the row's head weights
+  int hi, seq;
+  PageMap pm;
+  __device__ __forceinline__ RowKeys(const float* g, const uint32_t* st, const TopkArgs& t, int row,
+                                     int sq)
+      : given(g), stored(st), kbar(static_cast<const T*>(t.idx.kbar)),
+        qrow(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI),
+        wrow(t.idx.w + (int64_t)row * t.idx.hi), hi(t.idx.hi), seq(sq), pm(t.idx.pm) {}
   __device__ __forceinline__ uint32_t operator()(int e) const {
     if (given != nullptr) return score_key(given[e]);
     if (stored != nullptr) return stored[e];
-    const T* p = static_cast<const T*>(t->idx.kbar) + t->idx.pm.block_slot(seq, e) * DI;
-    const T* qrow = static_cast<const T*>(t->idx.q_idx) + (int64_t)row * t->idx.hi * DI;
+    const T* p = kbar + pm.block_slot(seq, e) * DI;
     float s = 0.0f;
-    for (int h = 0; h < t->idx.hi; ++h) {
+    for (int h = 0; h < hi; ++h) {
       float d = 0.0f;
       for (int c = 0; c < DI; ++c) d = fmaf(to_f32(qrow[h * DI + c]), to_f32(p[c]), d);
-      s = fmaf(t->idx.w[(int64_t)row * t->idx.hi + h], fmaxf(d, 0.0f), s);
+      s = fmaf(wrow[h], fmaxf(d, 0.0f), s);
     }
     return score_key(s);
   }
@@ -311,7 +318,7 @@ __device__ __forceinline__ void write_all(int32_t* sel_row, int32_t* n_sel, int 
 
 // Exact selection over every candidate of a row straight from a key source.
 template <class Get>
-__device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row, int32_t* n_sel,
+__device__ __noinline__ void select_full(Get get, int n, int top_k, int32_t* sel_row, int32_t* n_sel,
                             int row, SelShared& sh) {
   uint32_t thr;
   int r;
@@ -337,67 +344,150 @@ __device__ void select_full(const Get& get, int n, int top_k, int32_t* sel_row, 
 // select.hpp picks the k best with ties to the lower id.
 constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
 
-// Survivors (key >= tau) of the published runs of a long row, placed in
-// ascending-id order into skey/sid.  Thread t owns union entries
-// [16t, 16t + 16): whole runs of JW entries (a run lists one wave's keys
-// best first).  A saturated run (sat_of != 0xff) counts its rescanned
-// survivors and records its first place in sat_off; its keys are placed
-// later.  Everything between the loads and the stores is in registers.
-template <int JW>
-__device__ void place_runs(const uint32_t* ukey, const int32_t* uid, int un, uint32_t tau,
-                           const uint8_t* sat_of, const uint32_t* sat_cnt, uint32_t* sat_off,
-                           uint32_t* skey, int32_t* sid, bool& fits, uint32_t& m_total,
-                           SelShared& sh) {
+// LDS of the tail of a long row.
+struct LongShared {
+  uint32_t skey[kSelCap];  // survivors, in ascending id order
+  int32_t sid[kSelCap];
+  int32_t sat_w[kMaxSat];  // saturated runs
+  uint32_t sat_cnt[kMaxSat], sat_off[kMaxSat];
+  uint32_t n_sat;
+};
+
+// Tail of a long row (the last chunk to finish), JW keys per published run.
+// Thread t holds union entries [E t, E t + E) -- whole runs, E = kUnionCap /
+// 256 -- in registers, loaded at once.  tau = the k-th largest union key
+// (low bits past two radix digits cleared); a run whose last published key
+// reaches tau is saturated and rescanned from the key source; the other
+// runs' survivors (key >= tau) are placed in id order straight from the
+// registers, each run's entries ranked by id (a run lists one wave's keys
+// best first).  Then the exact select among the survivors.
+template <int JW, class Src>
+__device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, int nw, int n,
+                                          int top_k, int32_t* sel_row, int32_t* n_sel, int row,
+                                          LongShared& ls, SelShared& sh) {
   constexpr int E = kUnionCap / kSelThreads;
   constexpr int R = E / JW;
+  const int un = nw * JW;
   const int e0 = (int)threadIdx.x * E;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t k[E];
   int32_t id[E];
+  {
+    uint64_t v[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    k[i] = e0 + i < un ? ukey[e0 + i] : 0u;
-    id[i] = e0 + i < un ? uid[e0 + i] : 0;
+    for (int i = 0; i < E; ++i) v[i] = e0 + i < un ? tops[e0 + i] : 0ull;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      k[i] = (uint32_t)v[i];
+      id[i] = (int32_t)(v[i] >> 32);
+    }
   }
-  uint32_t cnt[R];
+  if (threadIdx.x == 0) ls.n_sat = 0u;
+  uint32_t tau;
+  {
+    int r;
+    bool resolved;
+    radix_kth_regs<E>(k, un, top_k, sh, tau, r, resolved, 2);
+  }
+  // saturated runs (index into sat_w, or 0xff)
   int si[R];
-  uint32_t mine = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    si[r] = e0 + r * JW < un ? (int)sat_of[e0 / JW + r] : 0xff;
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < JW; ++j) c += (k[r * JW + j] >= tau && k[r * JW + j] != 0u) ? 1u : 0u;
-    cnt[r] = si[r] != 0xff ? sat_cnt[si[r]] : c;
-    mine += cnt[r];
-  }
-  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
-  fits = fits && m_total <= (uint32_t)kSelCap;
-  if (!fits) return;  // uniform: m_total is the workgroup total
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (si[r] != 0xff) {
-      sat_off[si[r]] = off;
-    } else {
-#pragma unroll
-      for (int i = 0; i < JW; ++i) {
-        const uint32_t ki = k[r * JW + i];
-        if (ki >= tau && ki != 0u) {
-          uint32_t rank = 0;
-#pragma unroll
-          for (int j = 0; j < JW; ++j) {
-            const uint32_t kj = k[r * JW + j];
-            rank += (kj >= tau && kj != 0u && id[r * JW + j] < id[r * JW + i]) ? 1u : 0u;
-          }
-          skey[off + rank] = ki;
-          sid[off + rank] = id[r * JW + i];
-        }
+  for (int rr = 0; rr < R; ++rr) {
+    si[rr] = 0xff;
+    const uint32_t last = k[rr * JW + JW - 1];
+    if (e0 + rr * JW < un && last >= tau && last != 0u) {
+      const uint32_t sidx = atomicAdd(&ls.n_sat, 1u);
+      if (sidx < (uint32_t)kMaxSat) {
+        ls.sat_w[sidx] = e0 / JW + rr;
+        si[rr] = (int)sidx;
       }
     }
-    off += cnt[r];
+  }
+  __syncthreads();
+  const int ns = (int)ls.n_sat;
+  bool fits = ns <= kMaxSat;
+  // survivor counts of saturated runs (whole workgroup, one run at a time)
+#pragma unroll 1
+  for (int i = 0; fits && i < ns; ++i) {
+    const int e = ls.sat_w[i] * 256 + (int)threadIdx.x;
+    const bool hit = e < n && src(e) >= tau;
+    const uint32_t cw = (uint32_t)__popcll(ballot(hit));
+    if (lane == 0) sh.wcnt[1][wave] = cw;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      ls.sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
+    __syncthreads();
+  }
+  // survivors of the unsaturated runs placed, saturated runs' places reserved
+  uint32_t cnt[R], mine = 0;
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < JW; ++j) c += (k[rr * JW + j] >= tau && k[rr * JW + j] != 0u) ? 1u : 0u;
+    cnt[rr] = si[rr] != 0xff ? ls.sat_cnt[si[rr]] : c;
+    mine += cnt[rr];
+  }
+  uint32_t m_total;
+  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
+  fits = fits && m_total <= (uint32_t)kSelCap;
+  if (fits) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      if (si[rr] != 0xff) {
+        ls.sat_off[si[rr]] = off;
+      } else {
+#pragma unroll
+        for (int i = 0; i < JW; ++i) {
+          const uint32_t ki = k[rr * JW + i];
+          if (ki >= tau && ki != 0u) {
+            uint32_t rank = 0;
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+              const uint32_t kj = k[rr * JW + j];
+              rank += (kj >= tau && kj != 0u && id[rr * JW + j] < id[rr * JW + i]) ? 1u : 0u;
+            }
+            ls.skey[off + rank] = ki;
+            ls.sid[off + rank] = id[rr * JW + i];
+          }
+        }
+      }
+      off += cnt[rr];
+    }
+  }
+  __syncthreads();
+  // survivors of saturated runs, in id order (whole workgroup per run)
+#pragma unroll 1
+  for (int i = 0; fits && i < ns; ++i) {
+    const int e = ls.sat_w[i] * 256 + (int)threadIdx.x;
+    const uint32_t kk = e < n ? src(e) : 0u;
+    const bool hit = e < n && kk >= tau;
+    const uint64_t m = ballot(hit);
+    if (lane == 0) sh.wcnt[1][wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t base = ls.sat_off[i];
+    for (int w2 = 0; w2 < wave; ++w2) base += sh.wcnt[1][w2];
+    if (hit) {
+      ls.skey[base + lanes_below(m)] = kk;
+      ls.sid[base + lanes_below(m)] = e;
+    }
+    __syncthreads();
+  }
+  if (fits && m_total == (uint32_t)top_k) {
+    // exactly k survivors: all of them, already in id order
+    for (int j = threadIdx.x; j < top_k; j += kSelThreads) sel_row[j] = ls.sid[j];
+    if (threadIdx.x == 0) n_sel[row] = top_k;
+  } else if (fits) {
+    uint32_t thr;
+    int r;
+    radix_kth(KeyArray{ls.skey}, (int)m_total, top_k, sh, thr, r);
+    emit_topk(KeyArray{ls.skey}, IdArray{ls.sid}, (int)m_total, thr, r, sel_row, top_k, sh);
+    if (threadIdx.x == 0) n_sel[row] = top_k;
+  } else {
+    // rare: too many survivors (heavy ties): exact select over every key
+    select_full(src, n, top_k, sel_row, n_sel, row, sh);
   }
 }
-
-
 
 // Exact top-k of a row of n <= kDirectCap candidates whose keys get(e)
 // returns: thread t holds keys t * EPT .. t * EPT + EPT - 1 in registers
@@ -427,13 +517,9 @@ template <typename T, int DI, int HI>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   __shared__ uint32_t keys[kChunk];
   __shared__ int32_t pages[kChunk];
-  __shared__ uint32_t dkeys[kDirectCap];
-  __shared__ uint32_t skey[kSelCap];
-  __shared__ int32_t sid[kSelCap];
-  __shared__ int32_t sat_w[kMaxSat];
-  __shared__ uint32_t sat_cnt[kMaxSat], sat_off[kMaxSat];
+  __shared__ LongShared ls;
   __shared__ SelShared sh;
-  __shared__ uint32_t flag, n_sat;
+  __shared__ uint32_t flag;
   const int rl = blockIdx.y, row = t.row0 + rl, c = blockIdx.x;
   const RowPlan p(t, row);
   int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
@@ -497,108 +583,15 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
     return;
   }
 
-  // ---- last chunk of a long row.  This code runs once per row on one CU,
-  // so it is kept compact (rolled loops over LDS data): its instructions
-  // are fetched cold.
-  const RowKeys<T, DI> src{given, keep ? ws_row : nullptr, &t, row, p.seq};
-  const int jw = p.jw, nw = p.W * kSelWaves, un = nw * jw;
-  uint32_t* ukey = dkeys;                                   // [kUnionCap]
-  int32_t* uid = reinterpret_cast<int32_t*>(dkeys + kUnionCap);  // [kUnionCap]
-  // per run: index into sat_w of a saturated run, else 0xff (nw <= kUnionCap
-  // bytes fit in the chunk's key buffer, no longer needed)
-  uint8_t* sat_of = reinterpret_cast<uint8_t*>(keys);
-  {
-    constexpr int UPT = kUnionCap / kSelThreads;
-    uint64_t v[UPT];  // all loads in flight before any is used
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int e = threadIdx.x + kSelThreads * i;
-      v[i] = e < un ? tops[e] : 0ull;
-    }
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int e = threadIdx.x + kSelThreads * i;
-      if (e < un) {
-        ukey[e] = (uint32_t)v[i];
-        uid[e] = (int32_t)(v[i] >> 32);
-      }
-    }
-  }
-  for (int gw = threadIdx.x; gw < nw; gw += kSelThreads) sat_of[gw] = 0xff;
-  if (threadIdx.x == 0) n_sat = 0u;
-  __syncthreads();
-  // tau: the k-th largest published key, low bits past two digits cleared
-  uint32_t tau;
-  {
-    int r;
-    radix_kth(KeyArray{ukey}, un, t.top_k, sh, tau, r, 2);
-  }
-  // a run whose last published key still reaches tau is saturated
-  for (int gw = threadIdx.x; gw < nw; gw += kSelThreads) {
-    const uint32_t last = ukey[gw * jw + jw - 1];
-    if (last >= tau && last != 0u) {
-      const uint32_t sidx = atomicAdd(&n_sat, 1u);
-      if (sidx < (uint32_t)kMaxSat) {
-        sat_w[sidx] = gw;
-        sat_of[gw] = (uint8_t)sidx;
-      }
-    }
-  }
-  __syncthreads();
-  const int ns = (int)n_sat;
-  bool fits = ns <= kMaxSat;
-  // survivor counts of saturated runs (whole workgroup, one run at a time)
-#pragma unroll 1
-  for (int i = 0; fits && i < ns; ++i) {
-    const int e = sat_w[i] * 256 + (int)threadIdx.x;
-    const bool hit = e < p.n && src(e) >= tau;
-    const uint32_t cw = (uint32_t)__popcll(ballot(hit));
-    if (lane == 0) sh.wcnt[1][wave] = cw;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
-    __syncthreads();
-  }
-  // survivors of the unsaturated runs placed, saturated runs' places reserved
-  uint32_t m_total = 0;
-  switch (jw) {
-    case 1: place_runs<1>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
-    case 2: place_runs<2>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
-    case 4: place_runs<4>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
-    case 8: place_runs<8>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
-    default: place_runs<16>(ukey, uid, un, tau, sat_of, sat_cnt, sat_off, skey, sid, fits, m_total, sh); break;
-  }
-  __syncthreads();
-  // survivors of saturated runs, in id order (whole workgroup per run)
-#pragma unroll 1
-  for (int i = 0; fits && i < ns; ++i) {
-    const int e = sat_w[i] * 256 + (int)threadIdx.x;
-    const uint32_t k = e < p.n ? src(e) : 0u;
-    const bool hit = e < p.n && k >= tau;
-    const uint64_t m = ballot(hit);
-    if (lane == 0) sh.wcnt[1][wave] = (uint32_t)__popcll(m);
-    __syncthreads();
-    uint32_t base = sat_off[i];
-    for (int w2 = 0; w2 < wave; ++w2) base += sh.wcnt[1][w2];
-    if (hit) {
-      skey[base + lanes_below(m)] = k;
-      sid[base + lanes_below(m)] = e;
-    }
-    __syncthreads();
-  }
-  if (fits && m_total == (uint32_t)t.top_k) {
-    // exactly k survivors: all of them, already in id order
-    for (int j = threadIdx.x; j < t.top_k; j += kSelThreads) sel_row[j] = sid[j];
-    if (threadIdx.x == 0) t.n_sel[row] = t.top_k;
-  } else if (fits) {
-    uint32_t thr;
-    int r;
-    radix_kth(KeyArray{skey}, (int)m_total, t.top_k, sh, thr, r);
-    emit_topk(KeyArray{skey}, IdArray{sid}, (int)m_total, thr, r, sel_row, t.top_k, sh);
-    if (threadIdx.x == 0) t.n_sel[row] = t.top_k;
-  } else {
-    // rare: too many survivors (heavy ties): exact select over every key
-    select_full(src, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+  // ---- last chunk of a long row
+  const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+  const int nw = p.W * kSelWaves;
+  switch (p.jw) {
+    case 1: long_tail<1>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 2: long_tail<2>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 4: long_tail<4>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 8: long_tail<8>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    default: long_tail<16>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
   }
 }
 
