@@ -132,11 +132,6 @@ __device__ __forceinline__ uint32_t ordered_key(float s) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-struct KeyArrayL {
-  const uint32_t* k;
-  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
-};
-
 }  // namespace
 
 // Inverse of ordered_key: the float whose key is k (k >= 1).
@@ -333,7 +328,6 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
 // bound of the k-th key; otherwise P4 checks that at least k keys survived
 // and falls back to an exact select when they did not.
 __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
-  __shared__ uint32_t u[kPUnion];
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
   const int n = a.idx.pos_of(row) / kBlock;
@@ -342,13 +336,22 @@ __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
   const int n_groups = (n + kPGrp - 1) / kPGrp;
   const int un = min(kPUnion, ((n_groups + s - 1) / s) * 16);
   const int kq = s == 1 ? a.top_k : max(1, min(a.top_k, (3 * a.top_k + 2 * s - 1) / (2 * s)));
-  const uint32_t* src = a.uni + (int64_t)rl * kPUnion;
-  for (int e = threadIdx.x; e < un; e += blockDim.x) u[e] = src[e];
-  __syncthreads();
   uint32_t tau = 0u;
   if (un >= kq) {
+    // thread t holds union entries [EPT t, EPT t + EPT), loaded at once
+    constexpr int EPT = kPUnion / 256;
+    const u32x4_t* src =
+        reinterpret_cast<const u32x4_t*>(a.uni + (int64_t)rl * kPUnion) + threadIdx.x * (EPT / 4);
+    uint32_t key[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const u32x4_t v = src[j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * j + c] = v[c];
+    }
     int r;
-    radix_kth(KeyArrayL{u}, un, kq, sh, tau, r);
+    bool resolved;
+    radix_kth_regs<EPT>(key, un, kq, sh, tau, r, resolved);
   }
   if (threadIdx.x == 0) a.tau[rl] = tau;
 }
@@ -374,16 +377,9 @@ struct PRecomputed {
 struct IdSelf {
   __device__ __forceinline__ int32_t operator()(int e) const { return e; }
 };
-struct IdArrayL {
-  const int32_t* id;
-  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
-};
-
 // P4: gather, exact select, ordered emission.
 template <int DI>
 __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
-  __shared__ uint32_t ck[kPSelCap];
-  __shared__ int32_t ci[kPSelCap];
   __shared__ uint32_t offs[kPMaxSplits + 1];
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
@@ -409,20 +405,43 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
   __syncthreads();
   const uint32_t m = offs[a.splits];
   if (m != 0xffffffffu && m >= (uint32_t)a.top_k) {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const uint32_t cnt = ((sp + 1 < a.splits) ? offs[sp + 1] : m) - offs[sp];
-      const uint64_t* src = a.surv + ((int64_t)rl * a.splits + sp) * region;
-      for (uint32_t i = threadIdx.x; i < cnt; i += blockDim.x) {
-        const uint64_t v = src[i];  // (block << 32) | score bits
-        ck[offs[sp] + i] = ordered_key(__uint_as_float((uint32_t)v));
-        ci[offs[sp] + i] = (int32_t)(v >> 32);
+    // survivor j of the row (splits in order, each in block order) is
+    // entry j - offs[sp] of split sp's region, offs[sp] <= j < offs[sp + 1].
+    // Thread t holds survivors [EPT t, EPT t + EPT) in registers (loads all
+    // in flight), then the register radix select and ordered emission.
+    constexpr int EPT = kPSelCap / 256;
+    const uint64_t* rs = a.surv + (int64_t)rl * a.splits * region;
+    const int base = (int)threadIdx.x * EPT;
+    int sp = 0;
+    while (sp + 1 < a.splits && offs[sp + 1] <= (uint32_t)base) ++sp;
+    uint32_t start = offs[sp];
+    uint32_t next = sp + 1 < a.splits ? offs[sp + 1] : m;
+    uint64_t v[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const uint32_t jj = (uint32_t)(base + i);
+      if (jj < m) {
+        while (jj >= next) {  // the next split (empty splits are skipped)
+          ++sp;
+          start = next;
+          next = sp + 1 < a.splits ? offs[sp + 1] : m;
+        }
+        v[i] = rs[sp * region + (jj - start)];  // (block << 32) | score bits
       }
     }
-    __syncthreads();
+    uint32_t key[EPT];
+    int32_t id[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const bool ok = (uint32_t)(base + i) < m;
+      key[i] = ok ? ordered_key(__uint_as_float((uint32_t)v[i])) : 0u;
+      id[i] = ok ? (int32_t)(v[i] >> 32) : 0;
+    }
     uint32_t thr;
     int r;
-    radix_kth(KeyArrayL{ck}, (int)m, a.top_k, sh, thr, r);
-    emit_topk(KeyArrayL{ck}, IdArrayL{ci}, (int)m, thr, r, sel_row, a.top_k, sh);
+    bool resolved;
+    radix_kth_regs<EPT>(key, (int)m, a.top_k, sh, thr, r, resolved);
+    emit_regs<EPT>(key, id, (int)m, thr, r, sel_row, a.top_k, sh);
   } else {
     // survivors overflowed their slots or the select's LDS, or the sampled
     // threshold kept fewer than k: exact select over every candidate
