@@ -157,6 +157,36 @@ def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
     return wall, kern, work, ctx
 
 
+def run_project(wl: W.Workload, steps: int, warmup: int, dev):
+    """One step = the indexer projections of one prefill chunk of rows:
+    q_idx, w and the rows' indexer keys (into the paged cache) from hidden
+    states of size wl.hidden."""
+    log(f"[bench] drawing {wl.name} on {dev}")
+    cache = W.make_cache(wl, device=dev)
+    seq_id, pos = W.prefill_rows(wl, 0)
+    pj = W.make_projection(wl, len(pos), wl.hidden, device=dev)
+    cv = B.CacheView.from_cache(cache)
+    rows = B.QueriesView(torch.tensor(seq_id, dtype=torch.int32, device=dev),
+                         torch.tensor(pos, dtype=torch.int32, device=dev), max(pos))
+    q_idx = torch.empty((len(pos), wl.hi, wl.di), dtype=wl.torch_dtype, device=dev)
+    w = torch.empty((len(pos), wl.hi), dtype=torch.float32, device=dev)
+
+    def one(timer=None):
+        call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
+        call("project", B.qsa_index_project, cv, rows, pj.x, pj.wq, pj.wk, pj.ww, q_idx, w)
+
+    wall, kern = _timed(one, steps, warmup)
+    t, h = len(pos), wl.hidden
+    n = wl.hi * wl.di + wl.di + wl.hi
+    esz = 2
+    work = {"project": {"bytes": t * h * esz + n * h * esz + t * (wl.hi * wl.di + wl.di) * esz
+                                 + t * wl.hi * 4,
+                        "flops": 2 * t * h * n, "bound": "hbm", "kernel": "project_kernel",
+                        "files": ("project.hip", "project.hpp", "common.hpp")}}
+    ctx = {"rows": t, "cache": cache, "pos": pos, "proj": pj, "launches": 1, "dense_ms": None}
+    return wall, kern, work, ctx
+
+
 def _timed(one, steps, warmup):
     for _ in range(warmup):
         one()
@@ -320,6 +350,8 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
 
     if wl.mode == "mtp":
         return cpu_baseline_mtp(wl, ctx, seq, budget_s)
+    if wl.mode == "project":
+        return cpu_baseline_project(wl, ctx, budget_s)
     if wl.mode == "decode":
         qs, pos = ctx["qs"], ctx["pos"]
         rows = [(s, t, qs.q[i], qs.q_idx[i], qs.w[i]) for i, (s, t) in
@@ -370,6 +402,28 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
                          f"extrapolated as pooling + rows x mean row time"
                          if wl.mode != "decode" else "") +
                       "; numpy float64 single-threaded"}
+
+
+def cpu_baseline_project(wl, ctx, budget_s):
+    """Oracle of the projections (numpy float64 matrix products, one thread)
+    on batches of the same rows, scaled to rows/s."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    pj = ctx["proj"]
+    x = pj.x.double().cpu().numpy()
+    wq, wk, ww = (t.double().cpu().numpy() for t in (pj.wq, pj.wk, pj.ww))
+    batch = 256
+    done, el = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while el < budget_s:
+            i = done % (x.shape[0] - batch)
+            O.index_project(x[i:i + batch], wq, wk, ww, wl.hi, wl.dtype)
+            done += batch
+            el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows of {wl.name} in batches of {batch} ({el:.1f} s); numpy "
+                      "float64 single-threaded"}
 
 
 def cpu_baseline_mtp(wl, ctx, seq, budget_s):
@@ -434,8 +488,9 @@ def main():
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
     decode = wl.mode in ("decode", "mtp")
-    steps = args.steps if args.steps is not None else (200 if decode else 3)
-    warmup = args.warmup if args.warmup is not None else (20 if decode else 1)
+    short = decode or wl.mode == "project"  # microsecond steps: many of them
+    steps = args.steps if args.steps is not None else (200 if short else 3)
+    warmup = args.warmup if args.warmup is not None else (20 if short else 1)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -443,7 +498,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if wl.mode == "mtp":
+    if wl.mode == "project":
+        wall, timer, work, ctx = run_project(wl, steps, warmup, dev)
+    elif wl.mode == "mtp":
         wall, timer, work, ctx = run_mtp(wl, steps, warmup, dev, dense=not args.no_dense)
     elif decode:
         wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=not args.no_dense)
@@ -483,7 +540,15 @@ def main():
         "roofline": roof,
         "kernels_us_per_step": {k: round(v, 2) for k, v in kern.items()},
     }
-    if not decode:
+    if wl.mode == "project":
+        pw = work["project"]
+        t_us = kern["project"]
+        out["projection_mfma"] = {"flops_per_step": pw["flops"],
+                                  "achieved_tflops": round(pw["flops"] / (t_us * 1e-6) / 1e12, 1),
+                                  "peak_tflops": BF16_PEAK_TFLOPS,
+                                  "frac": round(pw["flops"] / (t_us * 1e-6) / 1e12
+                                                / BF16_PEAK_TFLOPS, 4)}
+    elif not decode:
         tk = work["topk"]
         t_us = kern["topk"]
         out["indexer_mfma"] = {"kernels": tk["kernel"], "flops_per_step": tk["flops"],
@@ -497,7 +562,7 @@ def main():
                             "how": ctx.get("dense_note", "")}
         if "dense_tflops" in ctx:
             out["dense_gqa"]["achieved_tflops"] = round(ctx["dense_tflops"], 1)
-    if not args.no_memory:
+    if not args.no_memory and wl.mode != "project":
         out["memory"] = memory_report(wl, ctx, dev)
     out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ctx)
     print(json.dumps(out), flush=True)

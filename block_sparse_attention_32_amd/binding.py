@@ -26,7 +26,8 @@ QSA_MAX_SHARED_LAG = 60
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error"}
 
 SYMBOLS = (
-    "qsa_pool_blocks", "qsa_index_scores", "qsa_topk_blocks", "qsa_attn_decode",
+    "qsa_pool_blocks", "qsa_index_project", "qsa_index_scores", "qsa_topk_blocks",
+    "qsa_attn_decode",
     "qsa_attn_decode_shared", "qsa_attn_prefill", "qsa_dense_attn_decode",
     "qsa_dense_attn_prefill",
     "qsa_workspace_size", "qsa_status_string", "qsa_version",
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "qsa_pool_blocks": [P, P, I32, P],
             "qsa_index_scores": [P, P, P, P, I32, P, I64, P],
+            "qsa_index_project": [P, P, P, I32, P, P, P, I32, P, P, P, P],
             "qsa_topk_blocks": [P, P, P, I64, P, P, I32, I32, P, P, P, SZ, P],
             "qsa_attn_decode": [P, P, P, I32, P, P, I32, F, P, P, SZ, P],
             "qsa_attn_decode_shared": [P, P, P, I32, P, P, P, I32, F, P, P, SZ, P],
@@ -241,6 +243,20 @@ def _attn(name, cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream):
         _check(n_sel, "n_sel", torch.int32, cache.device)
         _call(name, cache.ref, queries.ref, _ptr(q), int(q.shape[1]), _ptr(sel), _ptr(n_sel),
               int(top_k), ctypes.c_float(scale), _ptr(out), _ptr(ws), wsb, _stream(stream))
+
+
+def qsa_index_project(cache, queries, x, wq, wk, ww, q_idx, w, kidx_out=None, stream=None):
+    """Indexer projections of the rows' hidden states x [T, H]: q_idx [T, Hi,
+    Di], w [T, Hi] float32, and each row's indexer key written into kidx_out
+    (default: the cache's kidx).  Weights [out, H], bfloat16."""
+    for t, n in ((x, "x"), (wq, "wq"), (wk, "wk"), (ww, "ww"), (q_idx, "q_idx")):
+        _check(t, n, cache.dtype, cache.device)
+    _check(w, "w", torch.float32, cache.device)
+    kidx_out = cache.tensors[2] if kidx_out is None else kidx_out
+    _check(kidx_out, "kidx_out", cache.dtype, cache.device)
+    _call("qsa_index_project", cache.ref, queries.ref, _ptr(x), int(x.shape[1]), _ptr(wq),
+          _ptr(wk), _ptr(ww), int(ww.shape[0]), _ptr(q_idx), _ptr(kidx_out), _ptr(w),
+          _stream(stream))
 
 
 def qsa_attn_decode(cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream=None):

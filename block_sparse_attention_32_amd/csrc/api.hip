@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "attention.hpp"
+#include "project.hpp"
 #include "index.hpp"
 
 using namespace qsa;
@@ -371,6 +372,42 @@ qsa_status qsa_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void
                            void* stream) {
   return attention_common(QSA_OP_ATTN_DECODE, c, qm, q, n_q_heads, sel, n_sel, top_k, scale,
                           out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_index_project(const qsa_cache* c, const qsa_queries* qm, const void* x,
+                             int32_t h_dim, const void* wq, const void* wk, const void* ww,
+                             int32_t n_idx_heads, void* q_idx, void* kidx_out, float* w,
+                             void* stream) {
+  qsa_status st = check_cache(c);
+  if (st != QSA_OK) return st;
+  if ((st = check_queries(c, qm)) != QSA_OK) return st;
+  if (c->dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
+  if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
+  if (h_dim < 1 || h_dim % kProjKStep != 0) return QSA_ERR_INVALID_ARG;
+  if (qm->n_rows == 0) return QSA_OK;
+  if (x == nullptr || wq == nullptr || wk == nullptr || ww == nullptr || q_idx == nullptr ||
+      kidx_out == nullptr || w == nullptr)
+    return QSA_ERR_INVALID_ARG;
+  ProjArgs a;
+  a.pm = page_map(c);
+  a.x = static_cast<const bf16_t*>(x);
+  a.wq = static_cast<const bf16_t*>(wq);
+  a.wk = static_cast<const bf16_t*>(wk);
+  a.ww = static_cast<const bf16_t*>(ww);
+  a.h = h_dim;
+  a.nq = n_idx_heads * c->idx_dim;
+  a.nk = c->idx_dim;
+  a.n = a.nq + a.nk + n_idx_heads;
+  a.rows = qm->n_rows;
+  a.seq_id = qm->seq_id;
+  a.pos = qm->pos;
+  a.n_seqs = c->n_seqs;
+  a.max_pos = qm->max_pos;
+  a.q_idx = static_cast<bf16_t*>(q_idx);
+  a.kidx = static_cast<bf16_t*>(kidx_out);
+  a.w = w;
+  run_project(a, as_stream(stream));
+  return launched();
 }
 
 qsa_status qsa_attn_decode_shared(const qsa_cache* c, const qsa_queries* qm, const void* q,

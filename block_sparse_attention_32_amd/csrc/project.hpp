@@ -1,0 +1,36 @@
+// Argument block of the indexer projections (project.hip).
+#pragma once
+
+#include "common.hpp"
+
+namespace qsa {
+
+struct ProjArgs {
+  PageMap pm;
+  const bf16_t* x;       // [T][h]
+  const bf16_t* wq;      // [nq][h]
+  const bf16_t* wk;      // [nk][h]
+  const bf16_t* ww;      // [n - nq - nk][h]
+  int h, nq, nk, n;      // hidden size; Hi*Di; Di; Hi*Di + Di + Hi
+  int rows;              // T
+  const int32_t* seq_id;
+  const int32_t* pos;
+  int n_seqs, max_pos;
+  bf16_t* q_idx;         // [T][nq]
+  bf16_t* kidx;          // paged cache rows [slot][nk]
+  float* w;              // [T][Hi]
+  __device__ __forceinline__ int seq_of(int row) const {
+    const int s = seq_id[row];
+    return s < 0 ? 0 : (s >= n_seqs ? n_seqs - 1 : s);
+  }
+  __device__ __forceinline__ int pos_of(int row) const {
+    const int t = pos[row];
+    return t < 0 ? 0 : (t > max_pos ? max_pos : t);
+  }
+};
+
+constexpr int kProjKStep = 64;  // the hidden size must be a multiple of this
+
+void run_project(const ProjArgs& a, hipStream_t st);
+
+}  // namespace qsa

@@ -36,7 +36,8 @@ BLOCK_TOKENS = 4  # micro-block length used to place needles
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str               # "decode", "prefill" or "mtp" (multi-token decode)
+    mode: str               # "decode", "prefill", "mtp" (multi-token decode) or
+                            # "project" (the indexer projections alone)
     dtype: str              # "f32" or "bf16"
     n_seqs: int
     n_ctx: int              # tokens already cached before this step's rows
@@ -52,6 +53,7 @@ class Workload:
     needle_depths: tuple = ()  # fractions of the candidate range (decode)
     permute_pages: bool = False
     chunk: int = 0          # prefill chunk length; 0 = all rows in one step
+    hidden: int = 0         # hidden size of the indexer projections ("project")
     seed: int = 0
 
     @property
@@ -93,6 +95,10 @@ WORKLOADS = {
         name="mtp4_1m", mode="mtp", dtype="bf16", n_seqs=1,
         n_ctx=1048576, n_new=4, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
         needle_depths=(0.0, 0.25, 0.5, 0.75, 0.99), seed=1006),
+    "project_32k": Workload(
+        name="project_32k", mode="project", dtype="bf16", n_seqs=1, n_ctx=0,
+        n_new=32768, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512, hidden=2048,
+        seed=1007),
     "prefill_8k_at_128k": Workload(
         name="prefill_8k_at_128k", mode="prefill", dtype="bf16", n_seqs=1,
         n_ctx=131072, n_new=8192, hq=16, hkv=2, d=128, hi=4, di=64,
@@ -263,9 +269,42 @@ def mtp_rows(wl: Workload):
     return seq_id, pos, sel_of
 
 
+@dataclass
+class Projection:
+    """Hidden states and indexer projection weights (one row per output)."""
+    x: torch.Tensor    # [T, H]
+    wq: torch.Tensor   # [Hi * Di, H]
+    wk: torch.Tensor   # [Di, H]
+    ww: torch.Tensor   # [Hi, H]
+
+
+def make_projection(wl: Workload, rows: int, hidden: int, device="cpu", grid: bool = False,
+                    seed: int | None = None) -> Projection:
+    """Draw hidden states and projection weights.  grid=False: x ~ N(0, 1),
+    weights ~ N(0, 1) / sqrt(H).  grid=True: x = round(8 N(0,1)) / 8 clipped
+    to [-4, 4] and weights multiples of 1/16 in [-1, 1]; then every product
+    is a multiple of 2^-7 of magnitude at most 4, and every sum of up to
+    2^14 of them is exact in float32.  Draw order: x, wq, wk, ww."""
+    g = _gen(device, (wl.seed + 104729) if seed is None else seed)
+    dt = wl.torch_dtype
+
+    def w_(n):
+        r = torch.randn((n, hidden), generator=g, device=device)
+        if grid:
+            return torch.clamp(torch.round(r * 8.0) / 16.0, -1.0, 1.0).to(dt)
+        return (r / hidden ** 0.5).to(dt)
+
+    x = torch.randn((rows, hidden), generator=g, device=device)
+    x = grid8(x) if grid else x
+    return Projection(x=x.to(dt).contiguous(), wq=w_(wl.hi * wl.di).contiguous(),
+                      wk=w_(wl.di).contiguous(), ww=w_(wl.hi).contiguous())
+
+
 def step_rows(wl: Workload, chunk_index: int = 0):
     if wl.mode == "mtp":
         return mtp_rows(wl)[:2]
+    if wl.mode == "project":
+        return prefill_rows(wl, chunk_index)
     return decode_rows(wl) if wl.mode == "decode" else prefill_rows(wl, chunk_index)
 
 

@@ -180,6 +180,24 @@ qsa_status qsa_attn_prefill(const qsa_cache *c, const qsa_queries *qm,
                             int32_t top_k, float scale, void *out, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* Indexer projections (the input side of the learned indexer the
+ * keieiax.jp glossary describes in section 4トークンずつまとめて; the pages
+ * print no projection, so these are plain linear maps, no bias).  For every
+ * row i (token pos[i] of sequence seq_id[i]) with hidden state x[i]:
+ *   q_idx[i][h][d] = bf(sum_c x[i][c] * wq[h*Di + d][c])
+ *   kidx_out[token pos[i] of seq_id[i]][d] = bf(sum_c x[i][c] * wk[d][c])
+ *   w[i][h] = sum_c x[i][c] * ww[h][c]                       (float32)
+ * bf = round to nearest-even bfloat16 of the float32 sum.  x: [T][h_dim];
+ * wq: [Hi*Di][h_dim]; wk: [Di][h_dim]; ww: [Hi][h_dim] (each output's
+ * weights contiguous); q_idx: [T][Hi][Di]; kidx_out: the paged layout of
+ * qsa_cache.kidx (normally that buffer); w: [T][Hi].  bfloat16 caches only;
+ * h_dim a positive multiple of 64; 1 <= n_idx_heads <= 8. */
+qsa_status qsa_index_project(const qsa_cache *c, const qsa_queries *qm,
+                             const void *x, int32_t h_dim, const void *wq,
+                             const void *wk, const void *ww,
+                             int32_t n_idx_heads, void *q_idx, void *kidx_out,
+                             float *w, void *stream);
+
 /* Multi-token decode with one selection reused across draft positions
  * (keieiax.jp glossary, FAQ on whether the selection is shared across
  * layers: multi-token prediction may reuse the top index across its

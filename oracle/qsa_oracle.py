@@ -212,6 +212,29 @@ def token_set_shared(sel: np.ndarray, t_sel: int, t: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# before step 1: the indexer's input projections
+# --------------------------------------------------------------------------
+
+def index_project(x: np.ndarray, wq: np.ndarray, wk: np.ndarray, ww: np.ndarray,
+                  n_heads: int, dtype: str):
+    """The learned indexer's inputs from hidden states ([QSA glossary],
+    section 4トークンずつまとめて: the indexer is learned and light; the pages
+    print no projection, so these are plain linear maps).
+
+    x [T, H]; wq [Hi*Di, H], wk [Di, H], ww [Hi, H] (one row per output).
+    Returns q_idx [T, Hi, Di] and kidx [T, Di] rounded to the storage dtype,
+    and w [T, Hi] rounded to float32.  Each output is the dot product of the
+    token's hidden state with one weight row (a matrix product, computed in
+    float64).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    q = round_to_storage(x @ np.asarray(wq, dtype=np.float64).T, dtype)
+    k = round_to_storage(x @ np.asarray(wk, dtype=np.float64).T, dtype)
+    w = round_to_f32(x @ np.asarray(ww, dtype=np.float64).T)
+    return q.reshape(x.shape[0], n_heads, -1), k, w
+
+
+# --------------------------------------------------------------------------
 # step 6: attention over the token set
 # --------------------------------------------------------------------------
 

@@ -208,6 +208,67 @@ def test_topk_sampled_threshold_short(gpu):
         assert_sel_row(sel[i], int(n[i]), pb.oracle_select(i), 512)
 
 
+# ------------------------------------------------------------------ projections
+
+def _project(gpu, hi, di, hidden, rows, grid, seed):
+    wl = WL["project_32k"].replace(hi=hi, di=di, n_new=max(2 * rows, 256), permute_pages=True,
+                                   seed=seed)
+    cache = W.make_cache(wl, device=gpu)
+    rng = np.random.default_rng(seed)
+    pos = sorted(rng.choice(wl.total_len, size=rows, replace=False).tolist())
+    seq_id = [0] * rows
+    pj = W.make_projection(wl, rows, hidden, device=gpu, grid=grid)
+    cv = B.CacheView.from_cache(cache)
+    rv = B.QueriesView(torch.tensor(seq_id, dtype=torch.int32, device=gpu),
+                       torch.tensor(pos, dtype=torch.int32, device=gpu), max(pos))
+    before = cache.kidx.clone()
+    q_idx = torch.full((rows, hi, di), float("nan"), dtype=torch.bfloat16, device=gpu)
+    w = torch.full((rows, hi), float("nan"), dtype=torch.float32, device=gpu)
+    B.qsa_index_project(cv, rv, pj.x, pj.wq, pj.wk, pj.ww, q_idx, w)
+    torch.cuda.synchronize()
+    q, k, wo = O.index_project(f64(pj.x), f64(pj.wq), f64(pj.wk), f64(pj.ww), hi, "bf16")
+    tok = torch.tensor(pos, dtype=torch.long, device=gpu)
+    pages = cache.block_table[0].long()[tok // wl.page_size]
+    got_k = f64(cache.kidx[pages, tok % wl.page_size])
+    # every other slot of the cache is untouched
+    written = torch.zeros(cache.kidx.shape[:2], dtype=torch.bool, device=gpu)
+    written[pages, tok % wl.page_size] = True
+    assert torch.equal(cache.kidx[~written], before[~written])
+    return f64(q_idx), got_k, f64(w), q, k, wo, pj
+
+
+@pytest.mark.parametrize("hi,di,hidden,rows", [(4, 64, 512, 200), (2, 128, 256, 77),
+                                               (4, 64, 2048, 130), (1, 16, 64, 5)])
+def test_index_project_grid_bit_exact(gpu, hi, di, hidden, rows):
+    """Indexer projections on grid inputs (every float32 sum exact): q_idx,
+    the keys written into the paged cache and w equal the oracle bit for
+    bit; ragged row counts, two column blocks when Hi*Di + Di + Hi > 336."""
+    _say(f"projections grid hi={hi} di={di} H={hidden} rows={rows}")
+    gq, gk, gw, q, k, wo, _ = _project(gpu, hi, di, hidden, rows, True, 31 + rows)
+    assert np.array_equal(gq, q), np.abs(gq - q).max()
+    assert np.array_equal(gk, k), np.abs(gk - k).max()
+    assert np.array_equal(gw, wo), np.abs(gw - wo).max()
+
+
+def test_index_project_gaussian_within_rounding(gpu):
+    """Gaussian inputs at the bench shape (H 2048).  A float32 sum of n
+    products errs by at most n * 2^-24 * sum|x_c w_c| (standard bound), and
+    each side rounds to bfloat16 once (half a unit each): the outputs agree
+    within one unit plus that bound, and almost all agree exactly."""
+    _say("projections gaussian")
+    H = 2048
+    gq, gk, gw, q, k, wo, pj = _project(gpu, 4, 64, H, 300, False, 5)
+    ax = np.abs(f64(pj.x))
+    gam = H * 2.0 ** -24
+    for g_, o_, wt in ((gq, q, pj.wq), (gk, k, pj.wk)):
+        bound_acc = gam * (ax @ np.abs(f64(wt)).T).reshape(o_.shape)
+        ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(o_), 1e-30))).astype(int) - 7)
+        assert np.all(np.abs(g_ - o_) <= ulp + bound_acc), np.abs(g_ - o_).max()
+        assert np.mean(g_ != o_) < 0.01
+    assert np.all(np.abs(gw - wo) <= gam * (ax @ np.abs(f64(pj.ww)).T) + 2.0 ** -24 * np.abs(wo))
+
+
+# ------------------------------------------------------------------ attention
 # ------------------------------------------------------------------ attention
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])

@@ -28,6 +28,10 @@ MUTATIONS = {
                                    "range(BLOCK * own_block(t), t + 1)"),
     "shared_tail_cut": ("range(BLOCK * own_block(t_sel), t + 1)",
                         "range(BLOCK * own_block(t_sel), t)"),
+    "project_head_order": ("return q.reshape(x.shape[0], n_heads, -1), k, w",
+                           "return q.reshape(x.shape[0], -1, n_heads).transpose(0, 2, 1), k, w"),
+    "project_key_from_query_weights": ("k = round_to_storage(x @ np.asarray(wk, dtype=np.float64).T, dtype)",
+                                       "k = round_to_storage(x @ np.asarray(wq, dtype=np.float64)[: len(wk)].T, dtype)"),
     "own_block_competes": ("return own_block(t)\n", "return own_block(t) + 1\n"),
     "gqa_interleaved": ("return hq // (n_q_heads // n_kv_heads)",
                         "return hq % n_kv_heads"),

@@ -248,6 +248,45 @@ def test_shared_selection_covering_context_is_dense(t_sel, t):
     assert np.allclose(got, want, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- projections
+
+def test_index_project_one_hot_states_read_weight_columns():
+    """A one-hot hidden state picks column c of every weight matrix: q_idx,
+    kidx and w are those columns (rounded), laid out head by head."""
+    rng = np.random.default_rng(11)
+    h, hi, di = 12, 3, 4
+    wq = rng.integers(-40, 40, (hi * di, h)) / 16.0
+    wk = rng.integers(-40, 40, (di, h)) / 16.0
+    ww = rng.standard_normal((hi, h))
+    x = np.eye(h)[[5, 0, 11]]
+    q, k, w = O.index_project(x, wq, wk, ww, hi, "bf16")
+    for t, c in enumerate([5, 0, 11]):
+        for head in range(hi):
+            assert q[t, head].tolist() == wq[head * di:(head + 1) * di, c].tolist()
+        assert k[t].tolist() == wk[:, c].tolist()
+        assert w[t].tolist() == O.round_to_f32(ww[:, c]).tolist()
+
+
+def test_index_project_hand_example():
+    # x = (1, 2), wq rows (1, 0), (0, 1), (1, 1), (2, -1) -> heads [[1, 2], [3, 0]]
+    x = np.array([[1.0, 2.0]])
+    wq = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [2.0, -1.0]])
+    wk = np.array([[0.5, 0.25], [-1.0, 1.0]])
+    ww = np.array([[0.1, 0.2]])
+    q, k, w = O.index_project(x, wq, wk, ww, 2, "f32")
+    assert q.tolist() == [[[1.0, 2.0], [3.0, 0.0]]]
+    assert k.tolist() == [[1.0, 1.0]]
+    assert w.tolist() == [[float(np.float32(0.5))]]
+
+
+def test_index_project_rounds_bf16():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1
+    x = np.array([[1.0, 2.0 ** -8]])
+    wq = np.array([[1.0, 1.0]])
+    q, k, _ = O.index_project(x, wq, wq, wq, 1, "bf16")
+    assert q[0, 0, 0] == 1.0 and k[0, 0] == 1.0
+
+
 # ---------------------------------------------------------------- attention
 
 def _sdpa(q, k, v, mask, scale):
