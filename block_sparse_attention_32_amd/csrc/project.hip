@@ -13,10 +13,12 @@
 // cache.
 //
 // One contraction Y[T x N] = X[T x H] . W^T, W the N = Hi*Di + Di + Hi
-// weight rows stacked (Wq, Wk, Ww), on v_mfma_f32_16x16x32_bf16: a
-// workgroup of 4 waves owns 64 rows x up to 336 columns; each wave 16 rows
-// (A fragments straight from x) against all the columns, whose 64-wide K
-// slices are staged in LDS by whole 128-byte rows and shared by the waves.
+// weight rows stacked (Wq, Wk, Ww), on v_mfma_f32_16x16x32_bf16.  A
+// workgroup of 8 waves owns 128 rows x up to 336 columns: 64-wide K slices
+// of its rows of X and of the weight rows are staged in LDS by whole
+// 128-byte rows (double-buffered: the next slice's loads are in flight
+// while the current one is multiplied); wave (wm, wn) computes 64 rows x
+// 5 or 6 column tiles, reading both operands from LDS.
 #include "project.hpp"
 
 namespace qsa {
@@ -32,82 +34,109 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int kPM = 64;                 // rows per workgroup
+constexpr int kPM = 128;                // rows per workgroup
 constexpr int kPNT = 21;                // 16-column tiles per workgroup
 constexpr int kPN = kPNT * 16;          // columns per workgroup
 constexpr int kPK = 64;                 // K slice staged at once
-constexpr int kPPitch = kPK * 2 + 16;   // LDS bytes per staged weight row
+constexpr int kPPitch = kPK * 2 + 16;   // LDS bytes per staged row
+constexpr int kPRowsL = kPM + kPN;      // staged rows per slice (X rows, then W rows)
+constexpr int kPBuf = kPRowsL * kPPitch;
+constexpr int kPThr = 512;
+constexpr int kPChunks = kPRowsL * (kPK / 8);  // 16-byte pieces per slice
+constexpr int kPPer = (kPChunks + kPThr - 1) / kPThr;
+constexpr int kPMaxNt = 6;              // column tiles of a wave
 
 }  // namespace
 
-__global__ void __launch_bounds__(256) project_kernel(ProjArgs a) {
-  __shared__ __align__(16) unsigned char ws[kPN * kPPitch];
+__global__ void __launch_bounds__(kPThr) project_kernel(ProjArgs a) {
+  __shared__ __align__(16) unsigned char lds[2 * kPBuf];  // two slices
   const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
-  const int m0 = blockIdx.x * kPM + w * 16;
+  const int wm = w / 4, wn = w % 4;
+  const int mt0 = blockIdx.x * kPM;
   const int n0 = blockIdx.y * kPN;
   const int H = a.h;
-  // this lane's A row (rows past T reload the last row; their results are
-  // not stored)
-  const bf16_t* xr = a.x + (int64_t)min(m0 + c16, a.rows - 1) * H + 8 * g;
-  f32x4_t acc[kPNT];
-#pragma unroll
-  for (int nt = 0; nt < kPNT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // weight row n of the stacked [Wq; Wk; Ww], or null past N
-  auto wrow = [&](int n) -> const bf16_t* {
+  // this wave's column tiles: 6, 5, 5, 5 of the 21
+  const int nt0 = wn == 0 ? 0 : 1 + 5 * wn, ntc = wn == 0 ? 6 : 5;
+  // source of staged row r: X rows (past T: the last row, never stored),
+  // then weight rows of the stacked [Wq; Wk; Ww] (past N: none)
+  auto src_row = [&](int r) -> const bf16_t* {
+    if (r < kPM) return a.x + (int64_t)min(mt0 + r, a.rows - 1) * H;
+    const int n = n0 + r - kPM;
     if (n < a.nq) return a.wq + (int64_t)n * H;
     if (n < a.nq + a.nk) return a.wk + (int64_t)(n - a.nq) * H;
     if (n < a.n) return a.ww + (int64_t)(n - a.nq - a.nk) * H;
     return nullptr;
   };
-  constexpr int kChunks = kPN * (kPK / 8);                    // 16-byte pieces per slice
-  constexpr int kPer = (kChunks + 255) / 256;
-  for (int k0 = 0; k0 < H; k0 += kPK) {
-    u32x4_t xa[2];
+  u32x4_t st[kPPer];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) xa[s] = *reinterpret_cast<const u32x4_t*>(xr + k0 + 32 * s);
-    u32x4_t wv[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int ci = (int)threadIdx.x + 256 * j;
-      const bf16_t* p = ci < kChunks ? wrow(n0 + ci / 8) : nullptr;
-      wv[j] = p ? *reinterpret_cast<const u32x4_t*>(p + k0 + 8 * (ci % 8))
+    for (int j = 0; j < kPPer; ++j) {
+      const int ci = (int)threadIdx.x + kPThr * j;
+      const bf16_t* p = ci < kPChunks ? src_row(ci / 8) : nullptr;
+      st[j] = p ? *reinterpret_cast<const u32x4_t*>(p + k0 + 8 * (ci % 8))
                 : u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();  // the previous slice's reads are done
+  };
+  auto store = [&](unsigned char* buf) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int ci = (int)threadIdx.x + 256 * j;
-      if (ci < kChunks)
-        *reinterpret_cast<u32x4_t*>(ws + (ci / 8) * kPPitch + 16 * (ci % 8)) = wv[j];
+    for (int j = 0; j < kPPer; ++j) {
+      const int ci = (int)threadIdx.x + kPThr * j;
+      if (ci < kPChunks)
+        *reinterpret_cast<u32x4_t*>(buf + (ci / 8) * kPPitch + 16 * (ci % 8)) = st[j];
     }
-    __syncthreads();
+  };
+  f32x4_t acc[4][kPMaxNt];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kPMaxNt; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nslice = H / kPK;
+  load(0);
+  store(lds);
+  __syncthreads();
+  for (int ks = 0; ks < nslice; ++ks) {
+    unsigned char* cur = lds + (ks & 1) * kPBuf;
+    if (ks + 1 < nslice) load((ks + 1) * kPK);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      u32x4_t af[4];
 #pragma unroll
-      for (int nt = 0; nt < kPNT; ++nt) {
-        const u32x4_t b =
-            *reinterpret_cast<const u32x4_t*>(ws + (nt * 16 + c16) * kPPitch + 64 * s + 16 * g);
-        acc[nt] = mfma_bf16(xa[s], b, acc[nt]);
+      for (int mt = 0; mt < 4; ++mt)
+        af[mt] = *reinterpret_cast<const u32x4_t*>(cur + (64 * wm + 16 * mt + c16) * kPPitch +
+                                                   64 * s + 16 * g);
+#pragma unroll
+      for (int nt = 0; nt < kPMaxNt; ++nt) {
+        if (nt < ntc) {  // uniform
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(
+              cur + (kPM + 16 * (nt0 + nt) + c16) * kPPitch + 64 * s + 16 * g);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16(af[mt], b, acc[mt][nt]);
+        }
       }
     }
+    if (ks + 1 < nslice) store(lds + ((ks + 1) & 1) * kPBuf);
+    __syncthreads();
   }
-  // lane holds rows m0 + 4g + i of column n0 + 16 nt + c16
+  // lane holds rows 4g + i of each row tile, column c16 of each column tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + 4 * g + i;
-    if (row >= a.rows) continue;
-    const int seq = a.seq_of(row), t = a.pos_of(row);
-    const int64_t slot = a.pm.token_slot(seq, t);
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < kPNT; ++nt) {
-      const int n = n0 + 16 * nt + c16;
-      const float y = acc[nt][i];
-      if (n < a.nq) {
-        a.q_idx[(int64_t)row * a.nq + n] = f32_to_bf16(y);
-      } else if (n < a.nq + a.nk) {
-        a.kidx[slot * a.nk + (n - a.nq)] = f32_to_bf16(y);
-      } else if (n < a.n) {
-        a.w[(int64_t)row * (a.n - a.nq - a.nk) + (n - a.nq - a.nk)] = y;
+    for (int i = 0; i < 4; ++i) {
+      const int row = mt0 + 64 * wm + 16 * mt + 4 * g + i;
+      if (row >= a.rows) continue;
+      const int64_t slot = a.pm.token_slot(a.seq_of(row), a.pos_of(row));
+#pragma unroll
+      for (int nt = 0; nt < kPMaxNt; ++nt) {
+        const int n = n0 + 16 * (nt0 + nt) + c16;
+        if (nt >= ntc) continue;
+        const float y = acc[mt][nt][i];
+        if (n < a.nq) {
+          a.q_idx[(int64_t)row * a.nq + n] = f32_to_bf16(y);
+        } else if (n < a.nq + a.nk) {
+          a.kidx[slot * a.nk + (n - a.nq)] = f32_to_bf16(y);
+        } else if (n < a.n) {
+          a.w[(int64_t)row * (a.n - a.nq - a.nk) + (n - a.nq - a.nk)] = y;
+        }
       }
     }
   }
@@ -115,7 +144,7 @@ __global__ void __launch_bounds__(256) project_kernel(ProjArgs a) {
 
 void run_project(const ProjArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.rows + kPM - 1) / kPM), (unsigned)((a.n + kPN - 1) / kPN));
-  hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(project_kernel, grid, dim3(kPThr), 0, st, a);
 }
 
 }  // namespace qsa
