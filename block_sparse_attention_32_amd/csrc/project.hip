@@ -16,9 +16,12 @@
 // weight rows stacked (Wq, Wk, Ww), on v_mfma_f32_16x16x32_bf16.  A
 // workgroup of 8 waves owns 128 rows x up to 336 columns: 64-wide K slices
 // of its rows of X and of the weight rows are staged in LDS by whole
-// 128-byte rows (double-buffered: the next slice's loads are in flight
-// while the current one is multiplied); wave (wm, wn) computes 64 rows x
-// 5 or 6 column tiles, reading both operands from LDS.
+// 128-byte rows, double-buffered, with the loads of the slice after next
+// in flight while the current one is multiplied (one slice of products
+// does not cover a memory round trip; the loads are unconditional -- past
+// the end they reload the last slice -- so that each wait covers only the
+// older slice); wave (wm, wn) computes 64 rows x 5 or 6 column tiles,
+// reading both operands from LDS.
 #include "project.hpp"
 
 namespace qsa {
@@ -67,22 +70,30 @@ __global__ void __launch_bounds__(kPThr) project_kernel(ProjArgs a) {
     if (n < a.n) return a.ww + (int64_t)(n - a.nq - a.nk) * H;
     return nullptr;
   };
-  u32x4_t st[kPPer];
-  auto load = [&](int k0) {
+  // the thread's staged pieces: source rows (fixed across slices) and
+  // their LDS places
+  // (pieces past the slice or of rows past N read x's first row and store
+  // nothing or zeros: every load is unconditional)
+  const bf16_t* sp[kPPer];
+  uint32_t live = 0u;  // bit j: the piece's row has data
 #pragma unroll
-    for (int j = 0; j < kPPer; ++j) {
-      const int ci = (int)threadIdx.x + kPThr * j;
-      const bf16_t* p = ci < kPChunks ? src_row(ci / 8) : nullptr;
-      st[j] = p ? *reinterpret_cast<const u32x4_t*>(p + k0 + 8 * (ci % 8))
-                : u32x4_t{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < kPPer; ++j) {
+    const int ci = (int)threadIdx.x + kPThr * j;
+    const bf16_t* p = ci < kPChunks ? src_row(ci / 8) : nullptr;
+    sp[j] = p ? p + 8 * (ci % 8) : a.x;
+    live |= p ? (1u << j) : 0u;
+  }
+  auto load = [&](int k0, u32x4_t (&st)[kPPer]) {
+#pragma unroll
+    for (int j = 0; j < kPPer; ++j) st[j] = *reinterpret_cast<const u32x4_t*>(sp[j] + k0);
   };
-  auto store = [&](unsigned char* buf) {
+  auto store = [&](unsigned char* buf, const u32x4_t (&st)[kPPer]) {
 #pragma unroll
     for (int j = 0; j < kPPer; ++j) {
       const int ci = (int)threadIdx.x + kPThr * j;
       if (ci < kPChunks)
-        *reinterpret_cast<u32x4_t*>(buf + (ci / 8) * kPPitch + 16 * (ci % 8)) = st[j];
+        *reinterpret_cast<u32x4_t*>(buf + (ci / 8) * kPPitch + 16 * (ci % 8)) =
+            (live >> j) & 1u ? st[j] : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
   f32x4_t acc[4][kPMaxNt];
@@ -91,12 +102,7 @@ __global__ void __launch_bounds__(kPThr) project_kernel(ProjArgs a) {
 #pragma unroll
     for (int nt = 0; nt < kPMaxNt; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nslice = H / kPK;
-  load(0);
-  store(lds);
-  __syncthreads();
-  for (int ks = 0; ks < nslice; ++ks) {
-    unsigned char* cur = lds + (ks & 1) * kPBuf;
-    if (ks + 1 < nslice) load((ks + 1) * kPK);
+  auto compute = [&](const unsigned char* cur) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4_t af[4];
@@ -114,8 +120,25 @@ __global__ void __launch_bounds__(kPThr) project_kernel(ProjArgs a) {
         }
       }
     }
-    if (ks + 1 < nslice) store(lds + ((ks + 1) & 1) * kPBuf);
+  };
+  // slice ks is in LDS buffer ks % 2; register sets rA / rB alternate
+  // holding the next slice (loaded a whole step earlier) and the one after
+  u32x4_t rA[kPPer], rB[kPPer];
+  // one step: issue the loads of slice ks + 2, multiply slice ks, store
+  // slice ks + 1 (the other register set) into the other buffer
+  auto step = [&](int ks, const u32x4_t (&rnext)[kPPer], u32x4_t (&rafter)[kPPer]) {
+    load(min(ks + 2, nslice - 1) * kPK, rafter);
+    compute(lds + (ks & 1) * kPBuf);
+    store(lds + ((ks + 1) & 1) * kPBuf, rnext);
     __syncthreads();
+  };
+  load(0, rA);
+  load(min(1, nslice - 1) * kPK, rB);
+  store(lds, rA);
+  __syncthreads();
+  for (int ks = 0; ks < nslice; ks += 2) {
+    step(ks, rB, rA);  // slice ks + 1 is in rB; slice ks + 2 goes to rA
+    if (ks + 1 < nslice) step(ks + 1, rA, rB);
   }
   // lane holds rows 4g + i of each row tile, column c16 of each column tile
 #pragma unroll
