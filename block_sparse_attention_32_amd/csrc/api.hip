@@ -143,6 +143,11 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
     // pair); grow the split when rows x splits would exceed kMaxSplitWgs
     const int wph = 8 / c->n_kv_heads;
     int eps = kMfmaSplitEnt * wph / 2;
+    // a row's last split merges up to 16 partials in one round trip: when a
+    // few more entries per split (at most a quarter) bring the count to 16,
+    // take them
+    const int e16 = ((entries + 15) / 16 + 3) / 4 * 4;
+    if ((entries + eps - 1) / eps > 16 && e16 * 4 <= eps * 5) eps = e16;
     while ((int64_t)rows * ((entries + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
     p.eps = eps;
     p.splits = (entries + eps - 1) / eps;
