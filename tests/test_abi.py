@@ -117,6 +117,15 @@ def test_call_validation(libqsa):
     assert sh(R(c), R(q), 8, 16, 8, 8, None, 512, f(0.1), 8, 8, wsh, None) == -1   # no sel_of
     assert sh(R(c), R(q), 8, 16, 8, 8, 8, 512, f(0.1), 8, 8, wsh - 1, None) == -3
     assert sh(R(c), R(q), 8, 16, 8, 8, 8, 0, f(0.1), 8, 8, wsh, None) == -1       # top_k 0
+    # indexer projections
+    pj = L.qsa_index_project
+    assert pj(R(c), R(q), 8, 100, 8, 8, 8, 4, 8, 8, 8, None) == -1        # h_dim % 64
+    assert pj(R(c), R(q), 8, 0, 8, 8, 8, 4, 8, 8, 8, None) == -1
+    assert pj(R(c), R(q), 8, 2048, 8, 8, 8, 0, 8, 8, 8, None) == -1       # no heads
+    assert pj(R(c), R(q), 8, 2048, 8, 8, 8, 9, 8, 8, 8, None) == -1       # > 8 heads
+    assert pj(R(c), R(q), None, 2048, 8, 8, 8, 4, 8, 8, 8, None) == -1    # no x
+    assert pj(R(c), R(q), 8, 2048, 8, 8, 8, 4, 8, None, 8, None) == -1    # no kidx_out
+    assert pj(R(_cache(dtype=0)), R(q), 8, 2048, 8, 8, 8, 4, 8, 8, 8, None) == -2  # f32
     # zero rows: valid and a no-op
     z = _rows(n_rows=0, seq_id=None, pos=None)
     assert L.qsa_attn_prefill(R(c), R(z), None, 16, 8, 8, 512, f(0.1), None, None, 0, None) == 0
