@@ -44,7 +44,13 @@ points are resolved as follows (each is also listed in the design notes):
   kept ids are reported in ascending order;
 * one selection per query token, shared by all query heads; query head hq
   uses KV head hq // (Hq // Hkv);
-* attention is softmax(scale * q . k) over the token set, in float64.
+* attention is softmax(scale * q . k) over the token set, in float64;
+* the block size is a parameter (default 4).  Block size 1 is the
+  token-granular selection the pages contrast QSA with ([PR #30965 digest],
+  paragraph on Raschka's explanation: DeepSeek Sparse Attention picks single
+  tokens where QSA picks 4-token blocks; paragraph on the trade-offs: the
+  block index is the coarser one).  The budget stays 2,048 tokens, so
+  top_k = 2048 / block; a block of one token pools to its own key.
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 (closed forms, invariants, brute force and library routines).  Absolute
@@ -61,6 +67,7 @@ import numpy as np
 BLOCK = 4
 # At most 512 blocks = 2,048 tokens per query ([QSA glossary] public setting).
 TOP_K_BLOCKS = 512
+BUDGET_TOKENS = BLOCK * TOP_K_BLOCKS
 
 
 # --------------------------------------------------------------------------
@@ -112,24 +119,24 @@ def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def pool_blocks(kidx: np.ndarray, dtype: str, b_begin: int = 0,
-                b_end: int | None = None) -> np.ndarray:
+                b_end: int | None = None, block: int = BLOCK) -> np.ndarray:
     """Pooled indexer keys of complete blocks b_begin .. b_end-1.
 
     kidx: [L, Di] float64 values of one sequence's indexer keys.
-    Returns [b_end - b_begin, Di]: the mean of the 4 keys of each block,
-    rounded to the storage dtype.  Only complete blocks exist: b_end defaults
-    to L // 4 and may not exceed it.
+    Returns [b_end - b_begin, Di]: the mean of the `block` keys of each
+    block, rounded to the storage dtype.  Only complete blocks exist: b_end
+    defaults to L // block and may not exceed it.
     """
     kidx = np.asarray(kidx, dtype=np.float64)
-    n_complete = kidx.shape[0] // BLOCK
+    n_complete = kidx.shape[0] // block
     if b_end is None:
         b_end = n_complete
     if not (0 <= b_begin <= b_end <= n_complete):
         raise ValueError("block range outside the complete blocks")
     out = np.empty((b_end - b_begin, kidx.shape[1]), dtype=np.float64)
     for b in range(b_begin, b_end):
-        rows = kidx[BLOCK * b: BLOCK * b + BLOCK]
-        out[b - b_begin] = rows.sum(axis=0) / BLOCK
+        rows = kidx[block * b: block * b + block]
+        out[b - b_begin] = rows.sum(axis=0) / block
     return round_to_storage(out, dtype)
 
 
@@ -137,14 +144,14 @@ def pool_blocks(kidx: np.ndarray, dtype: str, b_begin: int = 0,
 # step 2: candidates (causal block limit) and the own (tail) block
 # --------------------------------------------------------------------------
 
-def own_block(t: int) -> int:
+def own_block(t: int, block: int = BLOCK) -> int:
     """Block holding position t; it is the 'current fractional part'."""
-    return t // BLOCK
+    return t // block
 
 
-def n_candidates(t: int) -> int:
+def n_candidates(t: int, block: int = BLOCK) -> int:
     """Blocks strictly before the own block compete for selection."""
-    return own_block(t)
+    return own_block(t, block)
 
 
 # --------------------------------------------------------------------------
@@ -188,14 +195,15 @@ def select_blocks(scores: np.ndarray, top_k: int) -> np.ndarray:
 # step 5: the token set attended by one query
 # --------------------------------------------------------------------------
 
-def token_set(sel: np.ndarray, t: int) -> np.ndarray:
+def token_set(sel: np.ndarray, t: int, block: int = BLOCK) -> np.ndarray:
     """Tokens of the selected blocks, then the own block up to t, ascending."""
-    toks = [BLOCK * int(b) + i for b in sel for i in range(BLOCK)]
-    toks += list(range(BLOCK * own_block(t), t + 1))
+    toks = [block * int(b) + i for b in sel for i in range(block)]
+    toks += list(range(block * own_block(t, block), t + 1))
     return np.asarray(toks, dtype=np.int64)
 
 
-def token_set_shared(sel: np.ndarray, t_sel: int, t: int) -> np.ndarray:
+def token_set_shared(sel: np.ndarray, t_sel: int, t: int,
+                     block: int = BLOCK) -> np.ndarray:
     """Tokens attended at position t >= t_sel by a query that reuses the
     selection made for the query at t_sel (multi-token prediction reusing
     the top index across speculative steps: [QSA glossary], FAQ on whether
@@ -206,8 +214,8 @@ def token_set_shared(sel: np.ndarray, t_sel: int, t: int) -> np.ndarray:
     (the tail grows with the drafted tokens).  For t == t_sel this is
     token_set(sel, t).
     """
-    toks = [BLOCK * int(b) + i for b in sel for i in range(BLOCK)]
-    toks += list(range(BLOCK * own_block(t_sel), t + 1))
+    toks = [block * int(b) + i for b in sel for i in range(block)]
+    toks += list(range(block * own_block(t_sel, block), t + 1))
     return np.asarray(toks, dtype=np.int64)
 
 
@@ -270,23 +278,23 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, tokens: np.ndarray,
 # --------------------------------------------------------------------------
 
 def qsa_select_row(kbar: np.ndarray, q_idx: np.ndarray, w: np.ndarray, t: int,
-                   top_k: int) -> np.ndarray:
+                   top_k: int, block: int = BLOCK) -> np.ndarray:
     """Selected block ids of the query at position t (steps 2-4)."""
-    n = n_candidates(t)
+    n = n_candidates(t, block)
     s = block_scores(kbar[:n], q_idx, w)
     return select_blocks(s, top_k)
 
 
 def qsa_row(k: np.ndarray, v: np.ndarray, kbar: np.ndarray, q: np.ndarray,
             q_idx: np.ndarray, w: np.ndarray, t: int, top_k: int,
-            scale: float) -> tuple[np.ndarray, np.ndarray]:
+            scale: float, block: int = BLOCK) -> tuple[np.ndarray, np.ndarray]:
     """(selected ids, attention output [Hq, D]) of the query at position t.
 
     k, v: [L, Hkv, D] with L > t (the query's own K/V are in the cache);
     kbar: the pooled keys of at least the blocks before the own block.
     """
-    sel = qsa_select_row(kbar, q_idx, w, t, top_k)
-    out = attend(q, k, v, token_set(sel, t), scale)
+    sel = qsa_select_row(kbar, q_idx, w, t, top_k, block)
+    out = attend(q, k, v, token_set(sel, t, block), scale)
     return sel, out
 
 
@@ -304,7 +312,7 @@ def dense_causal(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return masked_attention(q, k, v, mask, scale)
 
 
-def qsa_mask(sels: list, pos: np.ndarray, n_keys: int) -> np.ndarray:
+def qsa_mask(sels: list, pos: np.ndarray, n_keys: int, block: int = BLOCK) -> np.ndarray:
     """The boolean [T, L] table a materialised kq_mask would hold.
 
     Row i allows token j iff block(j) is selected for row i, or j lies in
@@ -314,8 +322,8 @@ def qsa_mask(sels: list, pos: np.ndarray, n_keys: int) -> np.ndarray:
     m = np.zeros((len(sels), n_keys), dtype=bool)
     j = np.arange(n_keys)
     for i, sel in enumerate(sels):
-        m[i] = np.isin(j // BLOCK, np.asarray(sel))
-        m[i] |= (j >= BLOCK * own_block(int(pos[i]))) & (j <= pos[i])
+        m[i] = np.isin(j // block, np.asarray(sel))
+        m[i] |= (j >= block * own_block(int(pos[i]), block)) & (j <= pos[i])
     return m
 
 

@@ -12,9 +12,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE = os.path.join(ROOT, "oracle", "qsa_oracle.py")
 
 MUTATIONS = {
-    "pool_drops_last_row": ("rows = kidx[BLOCK * b: BLOCK * b + BLOCK]",
-                            "rows = kidx[BLOCK * b: BLOCK * b + BLOCK - 1]"),
-    "pool_sum_not_mean": ("rows.sum(axis=0) / BLOCK", "rows.sum(axis=0)"),
+    "pool_drops_last_row": ("rows = kidx[block * b: block * b + block]",
+                            "rows = kidx[block * b: block * b + block - 1]"),
+    "pool_sum_not_mean": ("rows.sum(axis=0) / block", "rows.sum(axis=0)"),
+    "pool_ignores_block_size": ("rows = kidx[block * b: block * b + block]",
+                                "rows = kidx[BLOCK * b: BLOCK * b + BLOCK]"),
+    "pool_divides_by_four": ("rows.sum(axis=0) / block", "rows.sum(axis=0) / BLOCK"),
+    "token_set_four_tokens": ("toks = [block * int(b) + i for b in sel for i in range(block)]\n    toks += list(range(block * own_block(t, block), t + 1))",
+                              "toks = [block * int(b) + i for b in sel for i in range(BLOCK)]\n    toks += list(range(block * own_block(t, block), t + 1))"),
+    "own_block_default_size": ("    return own_block(t, block)\n", "    return own_block(t)\n"),
     "relu_sign": ("np.maximum(dots, 0.0)", "np.maximum(-dots, 0.0)"),
     "no_relu": ("np.maximum(dots, 0.0)", "dots"),
     "weight_index": ("s += w[h] *", "s += w[0] *"),
@@ -22,17 +28,17 @@ MUTATIONS = {
                          "order = np.lexsort((-ids, -scores))"),
     "select_lowest": ("order = np.lexsort((ids, -scores))",
                       "order = np.lexsort((ids, scores))"),
-    "own_block_cut": ("toks += list(range(BLOCK * own_block(t), t + 1))",
-                      "toks += list(range(BLOCK * own_block(t), t))"),
-    "shared_tail_from_own_block": ("range(BLOCK * own_block(t_sel), t + 1)",
-                                   "range(BLOCK * own_block(t), t + 1)"),
-    "shared_tail_cut": ("range(BLOCK * own_block(t_sel), t + 1)",
-                        "range(BLOCK * own_block(t_sel), t)"),
+    "own_block_cut": ("toks += list(range(block * own_block(t, block), t + 1))",
+                      "toks += list(range(block * own_block(t, block), t))"),
+    "shared_tail_from_own_block": ("range(block * own_block(t_sel, block), t + 1)",
+                                   "range(block * own_block(t, block), t + 1)"),
+    "shared_tail_cut": ("range(block * own_block(t_sel, block), t + 1)",
+                        "range(block * own_block(t_sel, block), t)"),
     "project_head_order": ("return q.reshape(x.shape[0], n_heads, -1), k, w",
                            "return q.reshape(x.shape[0], -1, n_heads).transpose(0, 2, 1), k, w"),
     "project_key_from_query_weights": ("k = round_to_storage(x @ np.asarray(wk, dtype=np.float64).T, dtype)",
                                        "k = round_to_storage(x @ np.asarray(wq, dtype=np.float64)[: len(wk)].T, dtype)"),
-    "own_block_competes": ("return own_block(t)\n", "return own_block(t) + 1\n"),
+    "own_block_competes": ("return own_block(t, block)\n", "return own_block(t, block) + 1\n"),
     "gqa_interleaved": ("return hq // (n_q_heads // n_kv_heads)",
                         "return hq % n_kv_heads"),
     "softmax_no_scale": ("z = scale * (kk @ q[hq])", "z = (kk @ q[hq])"),

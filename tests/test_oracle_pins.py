@@ -422,3 +422,110 @@ def test_end_to_end_hand_example():
     assert sel.tolist() == [1]
     want = v[[4, 5, 6, 7, 8, 9], 0].mean(0)
     assert np.allclose(out[0], want, atol=1e-13) and np.allclose(out[1], want, atol=1e-13)
+
+
+# ---------------------------------------------------------------- block sizes
+# Block size 1 is the token-granular (DeepSeek-style) selection the pages
+# contrast QSA with; the budget stays 2,048 tokens, so top_k = 2048 / block.
+
+def test_pool_block_sizes_closed_forms():
+    kidx = np.arange(32, dtype=np.float64)[:, None] * np.array([[1.0, -2.0]])
+    # a block of one token pools to its own key
+    assert np.array_equal(O.pool_blocks(kidx, "f32", block=1), kidx)
+    # pairs: mean of rows 2b, 2b+1 = (4b + 1) / 2 * (1, -2)
+    got2 = O.pool_blocks(kidx, "f32", block=2)
+    assert got2.shape == (16, 2)
+    assert np.array_equal(got2[:, 0], 2.0 * np.arange(16) + 0.5)
+    # blocks of 8 and 16: midpoints of the ramp
+    assert np.array_equal(O.pool_blocks(kidx, "f32", block=8)[:, 0], [3.5, 11.5, 19.5, 27.5])
+    assert np.array_equal(O.pool_blocks(kidx, "f32", block=16)[:, 1], [-15.0, -47.0])
+    # an incomplete trailing block is not pooled
+    assert O.pool_blocks(kidx[:31], "f32", block=8).shape == (3, 2)
+
+
+@pytest.mark.parametrize("block", [1, 2, 8, 16])
+@pytest.mark.parametrize("t", [0, 1, 15, 16, 17, 2047, 2048, 4097, 70001])
+def test_budget_counts_block_sizes(block, t):
+    """n_sel = min(2048 / block, t // block); at most 2,048 tokens are
+    selected and the own block adds t % block + 1."""
+    top_k = O.BUDGET_TOKENS // block
+    n_cand = O.n_candidates(t, block)
+    assert n_cand == t // block
+    sel = O.select_blocks(np.zeros(n_cand), top_k)
+    toks = O.token_set(sel, t, block)
+    assert len(toks) == block * min(top_k, t // block) + t % block + 1
+    assert len(toks) <= O.BUDGET_TOKENS + block
+    assert toks.max() == t and len(np.unique(toks)) == len(toks)
+
+
+def test_token_set_block_sizes_closed_forms():
+    assert O.token_set(np.array([3, 7]), 9, 1).tolist() == [3, 7, 9]
+    assert O.token_set(np.array([0, 2]), 7, 2).tolist() == [0, 1, 4, 5, 6, 7]
+    assert O.token_set(np.array([1]), 20, 8).tolist() == list(range(8, 21))
+    assert O.token_set(np.array([0]), 33, 16).tolist() == list(range(16)) + [32, 33]
+    assert O.token_set_shared(np.array([2, 5]), 9, 11, 1).tolist() == [2, 5, 9, 10, 11]
+    assert O.token_set_shared(np.array([0]), 17, 18, 8).tolist() == list(range(8)) + [16, 17, 18]
+
+
+@pytest.mark.parametrize("block", [2, 4, 8, 16])
+@pytest.mark.parametrize("seed", range(3))
+def test_token_granular_selection_of_blockwise_constant_keys(block, seed):
+    """When the indexer keys are constant inside every block and t is a
+    block start, the token-granular selection with budget k * block picks
+    exactly the tokens of the k blocks the block-level selection picks:
+    tokens of one block tie and ties go to the lower id, so whole blocks
+    are taken in the block order, and the two own blocks are both {t}."""
+    rng = np.random.default_rng(40 + seed)
+    n_blocks = int(rng.integers(5, 40))
+    t = block * n_blocks
+    keys = np.round(rng.standard_normal((n_blocks + 1, 8)) * 4) / 4
+    kidx = np.repeat(keys, block, axis=0)               # [t + block, 8]
+    q_idx = np.round(rng.standard_normal((3, 8)) * 4) / 4
+    w = rng.integers(1, 9, 3) / 8
+    k = int(rng.integers(1, n_blocks + 3))
+    sel_b = O.qsa_select_row(O.pool_blocks(kidx, "f32", block=block), q_idx, w, t, k, block)
+    sel_t = O.qsa_select_row(O.pool_blocks(kidx, "f32", block=1), q_idx, w, t, k * block, 1)
+    assert O.token_set(sel_t, t, 1).tolist() == O.token_set(sel_b, t, block).tolist()
+
+
+@pytest.mark.parametrize("block", [1, 2, 8])
+def test_dense_equivalence_block_sizes(block):
+    """With t // block <= k every earlier block is selected: dense causal."""
+    rng = np.random.default_rng(31 + block)
+    L = 40
+    k, v, kidx = _random_problem(rng, L, hq=4, hkv=2, d=8, hi=2, di=8)
+    kbar = O.pool_blocks(kidx, "f32", block=block)
+    q = rng.standard_normal((L, 4, 8))
+    q_idx = np.round(rng.standard_normal((L, 2, 8)) * 8) / 8
+    w = rng.integers(1, 17, (L, 2)) / 16
+    dense = O.dense_causal(q, k, v, np.arange(L), 0.3)
+    for t in range(L):
+        sel, out = O.qsa_row(k, v, kbar, q[t], q_idx[t], w[t], t, L, 0.3, block)
+        assert sel.tolist() == list(range(t // block))
+        assert np.allclose(out, dense[t], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("block", [1, 2, 16])
+def test_masked_bruteforce_block_sizes(block):
+    """Per-row attention over the token set equals the masked matrix form
+    and torch's masked SDPA at other block sizes too."""
+    rng = np.random.default_rng(50 + block)
+    L = 70
+    k, v, kidx = _random_problem(rng, L)
+    kbar = O.pool_blocks(kidx, "f32", block=block)
+    pos = np.sort(rng.choice(L, size=6, replace=False))
+    q = rng.standard_normal((len(pos), 4, 8))
+    q_idx = np.round(rng.standard_normal((len(pos), 2, 8)) * 8) / 8
+    w = rng.integers(1, 17, (len(pos), 2)) / 16
+    top_k = 3
+    sels, rows = [], []
+    for i, t in enumerate(pos):
+        sel, out = O.qsa_row(k, v, kbar, q[i], q_idx[i], w[i], int(t), top_k, 0.3, block)
+        sels.append(sel)
+        rows.append(out)
+    mask = O.qsa_mask(sels, pos, L, block)
+    for i, t in enumerate(pos):
+        assert mask[i].sum() == block * len(sels[i]) + int(t) % block + 1
+    mat = O.masked_attention(q, k, v, mask, 0.3)
+    assert np.allclose(np.stack(rows), mat, rtol=0, atol=1e-12)
+    assert np.allclose(mat, _sdpa(q, k, v, mask, 0.3), rtol=0, atol=1e-12)
