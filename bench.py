@@ -74,7 +74,8 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
     qs = W.make_queries(wl, cache, seq_id, pos, device=dev)
     cv = B.CacheView.from_cache(cache)
     rows = B.QueriesView(qs.seq_id, qs.pos, max(pos))
-    n_blocks = wl.total_len // 4
+    bk = wl.block
+    n_blocks = wl.total_len // bk
     P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
     step = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "decode")
     newest = torch.full((wl.n_seqs,), n_blocks - 1, dtype=torch.int32, device=dev)
@@ -87,8 +88,8 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
 
     wall, kern = _timed(one, steps, warmup)
     n_sel = step.n_sel.cpu().numpy()
-    n_tok = int(sum(4 * int(n) + p % 4 + 1 for n, p in zip(n_sel, pos)))
-    cand = sum(p // 4 for p in pos)
+    n_tok = int(sum(bk * int(n) + p % bk + 1 for n, p in zip(n_sel, pos)))
+    cand = sum(p // bk for p in pos)
     esz = 2 if wl.dtype == "bf16" else 4
     work = {
         "topk": {"bytes": cand * wl.di * esz, "bound": "hbm", "kernel": "topk_kernel",
@@ -96,8 +97,8 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
         "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm",
                  "kernel": "attn_mfma_kernel",
                  "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
-        "pool": {"bytes": wl.n_seqs * 5 * wl.di * esz, "bound": "hbm", "kernel": "pool_kernel",
-                 "files": ("index.hip", "index.hpp", "common.hpp")},
+        "pool": {"bytes": wl.n_seqs * (bk + 1) * wl.di * esz, "bound": "hbm",
+                 "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
     }
     dense_ms = None
     if dense:
@@ -121,7 +122,8 @@ def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
     qs = W.make_queries(wl, cache, seq_id, pos, device=dev)
     cv = B.CacheView.from_cache(cache)
     rows = B.QueriesView(qs.seq_id, qs.pos, max(pos))
-    n_blocks = wl.total_len // 4
+    bk = wl.block
+    n_blocks = wl.total_len // bk
     P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
     sel_of_t = torch.tensor(sel_of, dtype=torch.int32, device=dev)
     step = P.MtpStep(cv, rows, qs.q, qs.q_idx, qs.w, sel_of_t, wl.n_seqs, wl.top_k, wl.scale)
@@ -135,8 +137,9 @@ def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
 
     wall, kern = _timed(one, steps, warmup)
     n_sel = step.n_sel.cpu().numpy()
-    n_tok = int(sum(4 * int(n_sel[s]) + p - 4 * (pos[s] // 4) + 1 for s, p in zip(sel_of, pos)))
-    cand = sum(pos[s] // 4 for s in range(wl.n_seqs))
+    n_tok = int(sum(bk * int(n_sel[s]) + p - bk * (pos[s] // bk) + 1
+                    for s, p in zip(sel_of, pos)))
+    cand = sum(pos[s] // bk for s in range(wl.n_seqs))
     esz = 2 if wl.dtype == "bf16" else 4
     work = {
         "topk": {"bytes": cand * wl.di * esz, "bound": "hbm", "kernel": "topk_kernel",
@@ -144,8 +147,8 @@ def run_mtp(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
         "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm",
                  "kernel": "attn_mfma_kernel",
                  "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
-        "pool": {"bytes": wl.n_seqs * 5 * wl.di * esz, "bound": "hbm", "kernel": "pool_kernel",
-                 "files": ("index.hip", "index.hpp", "common.hpp")},
+        "pool": {"bytes": wl.n_seqs * (bk + 1) * wl.di * esz, "bound": "hbm",
+                 "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
     }
     dense_ms = None
     if dense:
@@ -226,6 +229,7 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
     log(f"[bench] drawing {wl.name} cache on {dev}")
     cache = W.make_cache(wl, device=dev)
     cv = B.CacheView.from_cache(cache)
+    bk = wl.block
     n_chunks = max(1, -(-wl.n_new // (wl.chunk or wl.n_new)))
     chunks = []
     for ci in range(n_chunks):
@@ -233,11 +237,11 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
         qs = W.make_queries(wl, cache, seq_id, pos, device=dev, seed=wl.seed + 7919 + ci)
         rows = B.QueriesView(qs.seq_id, qs.pos, max(pos))
         st = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "prefill")
-        b0 = pos[0] // 4
+        b0 = pos[0] // bk
         begin = torch.full((1,), b0, dtype=torch.int32, device=dev)
-        chunks.append((st, begin, (pos[-1] + 1) // 4 - b0, pos, qs, rows))
+        chunks.append((st, begin, (pos[-1] + 1) // bk - b0, pos, qs, rows))
     if wl.n_ctx:
-        P.pool_all(cv, 1, wl.n_ctx // 4, dev)               # set-up, untimed
+        P.pool_all(cv, 1, wl.n_ctx // bk, dev)              # set-up, untimed
 
     sched = P.ChunkedPrefill(cv, [(c[0], c[1], c[2]) for c in chunks], overlap=overlap)
 
@@ -252,8 +256,8 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
     for st, _, _, pos, _, _ in chunks:
         ns = st.n_sel.cpu().numpy().astype(np.int64)
         p_ = np.asarray(pos, dtype=np.int64)
-        n_tok += int((4 * ns + p_ % 4 + 1).sum())
-        cand += int((p_ // 4).sum())
+        n_tok += int((bk * ns + p_ % bk + 1).sum())
+        cand += int((p_ // bk).sum())
         dense_flop.append(4.0 * wl.hq * wl.d * float((p_ + 1).sum()))
     esz = 2 if wl.dtype == "bf16" else 4
     work = {
@@ -263,7 +267,7 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
         "topk": {"flops": 2 * wl.hi * wl.di * cand, "bound": "mfma",
                  "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_kernel",
                  "files": ("index_mfma.hip", "index.hpp", "select.hpp", "common.hpp")},
-        "pool": {"bytes": (wl.n_new // 4) * 5 * wl.di * esz, "bound": "hbm",
+        "pool": {"bytes": (wl.n_new // bk) * (bk + 1) * wl.di * esz, "bound": "hbm",
                  "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
     }
     # dense GQA attention over the same rows, chunk by chunk in order while
@@ -359,7 +363,7 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
         for s, *_ in rows:
             e = seq(s)
             if e[3] is None:
-                e[3] = O.pool_blocks(e[2], wl.dtype)        # set-up, untimed
+                e[3] = O.pool_blocks(e[2], wl.dtype, block=wl.block)   # set-up, untimed
         pool_s = 0.0
         sample = f"decode rows of {wl.name}, repeated"
     else:
@@ -367,7 +371,7 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
         e = seq(0)
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            e[3] = O.pool_blocks(e[2], wl.dtype)
+            e[3] = O.pool_blocks(e[2], wl.dtype, block=wl.block)
             pool_s = time.perf_counter() - t0
         rng = np.random.default_rng(wl.seed + 1)
         rows = []
@@ -386,9 +390,11 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
             for s, t, q, qi, w in rows:
                 k, v, _, kbar = seq(s)
                 if wl.mode == "decode":
-                    nb = (t + 1) // 4
-                    kbar[nb - 1:nb] = O.pool_blocks(seq(s)[2][: 4 * nb], wl.dtype, nb - 1, nb)
-                O.qsa_row(k, v, kbar, q, qi, w, t, wl.top_k, wl.scale)
+                    bk = wl.block
+                    nb = (t + 1) // bk
+                    kbar[nb - 1:nb] = O.pool_blocks(seq(s)[2][: bk * nb], wl.dtype, nb - 1, nb,
+                                                    block=bk)
+                O.qsa_row(k, v, kbar, q, qi, w, t, wl.top_k, wl.scale, wl.block)
                 done += 1
                 el = time.perf_counter() - t0
                 if el >= budget_s:
@@ -439,7 +445,7 @@ def cpu_baseline_mtp(wl, ctx, seq, budget_s):
     for s in set(seq_ids):
         e = seq(s)
         if e[3] is None:
-            e[3] = O.pool_blocks(e[2], wl.dtype)        # set-up, untimed
+            e[3] = O.pool_blocks(e[2], wl.dtype, block=wl.block)   # set-up, untimed
     done, el = 0, 0.0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -449,8 +455,9 @@ def cpu_baseline_mtp(wl, ctx, seq, budget_s):
                 k, v, _, kbar = seq(s)
                 r = sel_of[i]
                 if r not in sels:
-                    sels[r] = O.qsa_select_row(kbar, qi[r], w[r], pos[r], wl.top_k)
-                O.attend(q[i], k, v, O.token_set_shared(sels[r], pos[r], pos[i]), wl.scale)
+                    sels[r] = O.qsa_select_row(kbar, qi[r], w[r], pos[r], wl.top_k, wl.block)
+                O.attend(q[i], k, v, O.token_set_shared(sels[r], pos[r], pos[i], wl.block),
+                         wl.scale)
                 done += 1
             el = time.perf_counter() - t0
     return {"value": round(done / el, 3), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
@@ -531,7 +538,8 @@ def main():
            "new_tokens": wl.n_new, "query_rows_per_step": ctx["rows"],
            "chunk": (wl.chunk or wl.n_new) if not decode else None,
            "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "idx_heads": wl.hi, "idx_dim": wl.di,
-           "top_k": wl.top_k, "page_size": wl.page_size, "parallelism": "single-gpu"}
+           "top_k": wl.top_k, "block_tokens": wl.block, "page_size": wl.page_size,
+           "parallelism": "single-gpu"}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),

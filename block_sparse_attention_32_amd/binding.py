@@ -17,7 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqsa.so")
 
 QSA_BLOCK = 4
-QSA_MAX_TOPK = 512
+QSA_MAX_BLOCK = 16
+QSA_BUDGET_TOKENS = 2048
+QSA_MAX_TOPK = 2048
 QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_TOPK, QSA_OP_ATTN_DECODE, QSA_OP_ATTN_PREFILL = 0, 1, 2
 QSA_OP_DENSE_DECODE, QSA_OP_DENSE_PREFILL, QSA_OP_ATTN_DECODE_SHARED = 3, 4, 5
@@ -43,6 +45,7 @@ class QsaError(RuntimeError):
 class _Cache(ctypes.Structure):
     _fields_ = [
         ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("idx_dim", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
@@ -127,8 +130,9 @@ class CacheView:
     """qsa_cache over torch tensors (keeps them alive while in use).
 
     k, v: [n_pages, page, Hkv, D]; kidx: [n_pages, page, Di];
-    kbar: [n_pages, page/4, Di]; block_table: [n_seqs, max_pages] int32;
-    seq_len: [n_seqs] int32; max_seq_len: host upper bound of seq_len.
+    kbar: [n_pages, page/B, Di] (B tokens per pooled block: its shape gives
+    B); block_table: [n_seqs, max_pages] int32; seq_len: [n_seqs] int32;
+    max_seq_len: host upper bound of seq_len.
     """
 
     def __init__(self, k, v, kidx, kbar, block_table, seq_len, max_seq_len: int):
@@ -139,13 +143,17 @@ class CacheView:
         if k.dtype not in _DT:
             raise ValueError("cache dtype must be float32 or bfloat16")
         n_pages, page, hkv, d = k.shape
+        if kbar.dim() != 3 or kbar.shape[1] < 1 or page % kbar.shape[1] != 0:
+            raise ValueError("kbar must be [n_pages, page_size / block, Di]")
+        self.block = page // kbar.shape[1]
         self.tensors = (k, v, kidx, kbar, block_table, seq_len)
         self.device = k.device
         self.dtype = k.dtype
         self.head_dim = d
         self.n_kv_heads = hkv
         self.s = _Cache(
-            dtype=_DT[k.dtype], page_size=page, n_kv_heads=hkv, head_dim=d,
+            dtype=_DT[k.dtype], page_size=page, block_size=self.block,
+            n_kv_heads=hkv, head_dim=d,
             idx_dim=kidx.shape[-1], n_seqs=block_table.shape[0],
             max_pages_per_seq=block_table.shape[1], max_seq_len=int(max_seq_len),
             n_pages=n_pages, block_table=_ptr(block_table), seq_len=_ptr(seq_len),

@@ -28,10 +28,15 @@ int log2i(int x) {
   return s;
 }
 
+// tokens per pooled block (0 stands for QSA's 4)
+int cache_block(const qsa_cache* c) { return c->block_size == 0 ? QSA_BLOCK : c->block_size; }
+
 qsa_status check_cache(const qsa_cache* c) {
   if (c == nullptr) return QSA_ERR_INVALID_ARG;
   if (c->dtype != QSA_F32 && c->dtype != QSA_BF16) return QSA_ERR_INVALID_ARG;
-  if (!is_pow2(c->page_size) || c->page_size < QSA_BLOCK) return QSA_ERR_INVALID_ARG;
+  if (!is_pow2(c->page_size) || c->page_size < 4) return QSA_ERR_INVALID_ARG;
+  const int blk = cache_block(c);
+  if (!is_pow2(blk) || blk > QSA_MAX_BLOCK || blk > c->page_size) return QSA_ERR_INVALID_ARG;
   if (c->n_kv_heads < 1 || c->n_seqs < 1 || c->max_pages_per_seq < 1) return QSA_ERR_INVALID_ARG;
   if (c->max_seq_len < 1 || c->n_pages < 1) return QSA_ERR_INVALID_ARG;
   if ((int64_t)c->max_seq_len > (int64_t)c->max_pages_per_seq * c->page_size)
@@ -49,7 +54,7 @@ qsa_status check_queries(const qsa_cache* c, const qsa_queries* qm) {
   if (qm->n_rows < 0 || qm->max_pos < 0) return QSA_ERR_INVALID_ARG;
   if (qm->n_rows > 0 && (qm->seq_id == nullptr || qm->pos == nullptr)) return QSA_ERR_INVALID_ARG;
   if (qm->max_pos >= c->max_seq_len) return QSA_ERR_INVALID_ARG;
-  if (qm->max_pos / QSA_BLOCK > QSA_MAX_BLOCKS) return QSA_ERR_UNSUPPORTED;
+  if (qm->max_pos / cache_block(c) > QSA_MAX_BLOCKS) return QSA_ERR_UNSUPPORTED;
   if (qm->n_rows > 65535) return QSA_ERR_UNSUPPORTED;  // grid y
   return QSA_OK;
 }
@@ -59,6 +64,7 @@ PageMap page_map(const qsa_cache* c) {
   pm.table = c->block_table;
   pm.max_pages = c->max_pages_per_seq;
   pm.page_shift = log2i(c->page_size);
+  pm.blk_shift = log2i(cache_block(c));
   return pm;
 }
 
@@ -100,9 +106,9 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
   return p;
 }
 
-TopkPlan topk_plan(const qsa_queries* qm) {
+TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm) {
   TopkPlan p;
-  const int max_n = qm->max_pos / QSA_BLOCK;
+  const int max_n = qm->max_pos / cache_block(c);
   p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
   if (p.rows < 1) p.rows = 1;
   p.w_max = (max_n + kChunk - 1) / kChunk;
@@ -130,27 +136,31 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
   const bool dense = (op == QSA_OP_DENSE_DECODE || op == QSA_OP_DENSE_PREFILL);
   const bool split = (op == QSA_OP_ATTN_DECODE || op == QSA_OP_DENSE_DECODE ||
                      op == QSA_OP_ATTN_DECODE_SHARED);
-  // a row reusing another row's selection also attends up to kMaxBridge
-  // whole blocks before its own
-  const int entries = (dense ? qm->max_pos / QSA_BLOCK : top_k) + 1 +
-                      (op == QSA_OP_ATTN_DECODE_SHARED ? kMaxBridge : 0);
+  // a row reusing another row's selection also attends up to
+  // ceil(QSA_MAX_SHARED_LAG / B) whole blocks before its own
+  const int blk = cache_block(c);
+  const int entries = (dense ? qm->max_pos / blk : top_k) + 1 +
+                      (op == QSA_OP_ATTN_DECODE_SHARED ? (QSA_MAX_SHARED_LAG + blk - 1) / blk : 0);
   p.mfma = attn_mfma_supported(c->dtype, hq, c->n_kv_heads, c->head_dim) ? 1 : 0;
-  p.tile = p.mfma ? kMfmaTileTok : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim);
+  p.tile = p.mfma ? kMfmaTileTok
+                  : attn_tile_tokens(c->dtype, hq, c->n_kv_heads, c->head_dim, blk);
   const int rows = qm->n_rows > 0 ? qm->n_rows : 1;
   if (split && p.mfma) {
-    // split workgroups have 8 waves, wph of them per KV head, and each
-    // wave gets two 4-entry tiles (kMfmaSplitEnt = 16 entries per wave
+    // Planned in 4-token units (one QSA block), then converted to entries.
+    // Split workgroups have 8 waves, wph of them per KV head, and each
+    // wave gets two 16-token tiles (kMfmaSplitEnt = 16 units per wave
     // pair); grow the split when rows x splits would exceed kMaxSplitWgs
+    const int units = (int)(((int64_t)entries * blk + 3) / 4);
     const int wph = 8 / c->n_kv_heads;
     int eps = kMfmaSplitEnt * wph / 2;
     // a row's last split merges up to 16 partials in one round trip: when a
-    // few more entries per split (at most a quarter) bring the count to 16,
+    // few more units per split (at most a quarter) bring the count to 16,
     // take them
-    const int e16 = ((entries + 15) / 16 + 3) / 4 * 4;
-    if ((entries + eps - 1) / eps > 16 && e16 * 4 <= eps * 5) eps = e16;
-    while ((int64_t)rows * ((entries + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
-    p.eps = eps;
-    p.splits = (entries + eps - 1) / eps;
+    const int e16 = ((units + 15) / 16 + 3) / 4 * 4;
+    if ((units + eps - 1) / eps > 16 && e16 * 4 <= eps * 5) eps = e16;
+    while ((int64_t)rows * ((units + eps - 1) / eps) > kMaxSplitWgs) eps *= 2;
+    p.eps = eps * 4 / blk > 0 ? eps * 4 / blk : 1;
+    p.splits = (entries + p.eps - 1) / p.eps;
   } else if (split) {
     int s = (kTargetSplitWgs + rows - 1) / rows;
     int s_max = (entries + kMinEntriesPerSplit - 1) / kMinEntriesPerSplit;
@@ -191,7 +201,7 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
   if (qm->n_rows > 0 && (q == nullptr || out == nullptr)) return QSA_ERR_INVALID_ARG;
   if (c->k == nullptr || c->v == nullptr) return QSA_ERR_INVALID_ARG;
   const AttnPlan p = attn_plan(op, c, qm, hq, top_k);
-  if (p.tile < QSA_BLOCK) return QSA_ERR_UNSUPPORTED;
+  if (p.tile < 4) return QSA_ERR_UNSUPPORTED;
   if (p.total > 0 && (ws == nullptr || ws_bytes < p.total)) return QSA_ERR_WORKSPACE;
   if (qm->n_rows == 0) return QSA_OK;
   AttnArgs a;
@@ -264,7 +274,7 @@ qsa_status qsa_index_scores(const qsa_cache* c, const qsa_queries* qm, const voi
   if (st != QSA_OK) return st;
   if ((st = check_queries(c, qm)) != QSA_OK) return st;
   if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
-  const int max_n = qm->max_pos / QSA_BLOCK;
+  const int max_n = qm->max_pos / cache_block(c);
   if (ld < (int64_t)max_n) return QSA_ERR_INVALID_ARG;
   if (qm->n_rows == 0 || max_n == 0) return QSA_OK;
   if (q_idx == nullptr || w == nullptr || scores == nullptr || c->kbar == nullptr)
@@ -291,7 +301,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   if (st != QSA_OK) return st;
   if ((st = check_queries(c, qm)) != QSA_OK) return st;
   if (top_k < 1 || top_k > QSA_MAX_TOPK) return QSA_ERR_INVALID_ARG;
-  const int max_n = qm->max_pos / QSA_BLOCK;
+  const int max_n = qm->max_pos / cache_block(c);
   if (scores != nullptr) {
     if (ld < (int64_t)max_n) return QSA_ERR_INVALID_ARG;
   } else {
@@ -299,7 +309,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
     if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
   }
   if (qm->n_rows > 0 && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
-  const TopkPlan p = topk_plan(qm);
+  const TopkPlan p = topk_plan(c, qm);
   const PidxPlan pp = pidx_plan(qm);
   const bool mfma = scores == nullptr && qm->n_rows >= kPMinRows &&
                     pidx_supported(c->dtype, c->idx_dim, n_idx_heads);
@@ -451,7 +461,7 @@ size_t qsa_workspace_size(int32_t op, const qsa_cache* c, const qsa_queries* qm,
   if (check_cache(c) != QSA_OK || check_queries(c, qm) != QSA_OK) return 0;
   switch (op) {
     case QSA_OP_TOPK: {
-      const size_t a = topk_plan(qm).total, b = pidx_plan(qm).total;
+      const size_t a = topk_plan(c, qm).total, b = pidx_plan(qm).total;
       return a > b ? a : b;
     }
     case QSA_OP_ATTN_DECODE:

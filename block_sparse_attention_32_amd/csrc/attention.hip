@@ -66,18 +66,19 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
   constexpr int V = Vec<T>::N;
   const T* kg = static_cast<const T*>(a.k);
   const T* vg = static_cast<const T*>(a.v);
-  const int ept = TT / kBlock;  // entries per tile
+  const int bs = a.pm.blk_shift, nb = 1 << bs;  // tokens per block
+  const int ept = TT >> bs;  // entries per tile (TT is a multiple of the block)
   for (int e0 = e_beg; e0 < e_end; e0 += ept) {
     __syncthreads();
     for (int j = tid; j < TT; j += kAttnThreads) {
-      const int e = e0 + j / kBlock, i = j % kBlock;
+      const int e = e0 + (j >> bs), i = j & (nb - 1);
       int64_t r = -1;
       if (e < e_end) {
         const bool own = (e == rl.e_own);
         bool ok = true;
         const int b = own ? b_own : rl.block(e, DENSE, ok);
-        const int ntok = own ? (t % kBlock) + 1 : kBlock;
-        if (ok && i < ntok) r = a.pm.token_slot(seq, b * kBlock + i);
+        const int ntok = own ? (t & (nb - 1)) + 1 : nb;
+        if (ok && i < ntok) r = a.pm.token_slot(seq, (b << bs) + i);
       }
       trow[j] = r;
     }
@@ -190,9 +191,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
   }
 }
 
-int attn_tile_tokens(int dtype, int hq, int hkv, int d) {
+int attn_tile_tokens(int dtype, int hq, int hkv, int d, int block) {
   const int esz = dtype == QSA_F32 ? 4 : 2;
-  for (int tt = 64; tt >= kBlock; tt -= kBlock)
+  const int step = block > 4 ? block : 4;  // tiles hold whole blocks
+  for (int tt = 64; tt >= step; tt -= step)
     if (attn_layout(esz, hq, hkv, d, tt).total <= (size_t)kAttnLds) return tt;
   return 0;
 }

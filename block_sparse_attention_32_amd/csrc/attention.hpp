@@ -36,8 +36,9 @@ struct AttnArgs {
 };
 
 // A row reusing another row's selection attends at most this many whole
-// blocks between that row's own block and its own (QSA_MAX_SHARED_LAG).
-constexpr int kMaxBridge = (QSA_MAX_SHARED_LAG + QSA_BLOCK - 1) / QSA_BLOCK;
+// blocks between that row's own block and its own (QSA_MAX_SHARED_LAG
+// tokens: as many blocks at block size 1).
+constexpr int kMaxBridge = QSA_MAX_SHARED_LAG;
 
 // The block list of one row: n_list selected entries, then n_bridge whole
 // blocks b_sel .. b_own - 1, then the own block (the last entry).  Selected
@@ -46,13 +47,14 @@ struct RowList {
   int b_own, b_sel, n_list, n_bridge, e_own;
   const int32_t* sel;
   __device__ __forceinline__ RowList(const AttnArgs& a, int row, int t, bool dense) {
-    b_own = t / QSA_BLOCK;
+    const int bs = a.pm.blk_shift;
+    b_own = t >> bs;
     int rs = row;
     b_sel = b_own;
     if (!dense && a.sel_of != nullptr) {
       rs = min(max(a.sel_of[row], 0), a.n_rows - 1);
       const int ts = min(max(a.pos[rs], 0), a.max_pos);
-      b_sel = max(min(ts / QSA_BLOCK, b_own), b_own - kMaxBridge);
+      b_sel = max(min(ts >> bs, b_own), b_own - (((QSA_MAX_SHARED_LAG - 1) >> bs) + 1));
     }
     n_list = dense ? b_own : min(max(a.n_sel[rs], 0), a.top_k);
     n_bridge = b_own - b_sel;
@@ -90,7 +92,7 @@ __host__ __device__ inline AttnLayout attn_layout(int esz, int hq, int hkv, int 
   L.total = o;
   return L;
 }
-int attn_tile_tokens(int dtype, int hq, int hkv, int d);
+int attn_tile_tokens(int dtype, int hq, int hkv, int d, int block);
 void run_attention(const AttnArgs& a, int dtype, int d, bool dense, int n_rows, hipStream_t st);
 
 }  // namespace qsa

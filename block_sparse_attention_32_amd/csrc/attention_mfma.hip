@@ -172,8 +172,9 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   constexpr int KP = 2 * D, NCH = D / 8;
   constexpr int kStage = NW * kMfmaTileTok * (VP + KP);  // per-wave K and V tiles
   constexpr int kMerge = NW * 16 * (D + 2) * 4;         // per-wave results
-  // The token rows of the staged list, tile by tile: a tile is 4 entries
-  // (blocks) x 4 tokens, kept as [token j][entry i]; each value is the
+  // The token rows of the staged list, tile by tile: token p of the list
+  // (the tokens of its blocks in list order) is tile row 4i + j of tile
+  // p / 16, i = (p % 16) / 4, j = p % 4, kept as [j][i]; each value is the
   // byte offset of the token's row in the K and V arrays (WIDE: its row
   // index).  Tokens not to attend point at the row's own first token.
   __shared__ __align__(16) uint32_t trow[kMfmaEntChunk * 4];
@@ -196,12 +197,14 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int n_entries = rl.e_own + 1;
   const int e_beg = split * a.eps;
   const int e_end = min(n_entries, e_beg + a.eps);
-  const int tail = (t % kBlock) + 1;  // tokens of the own block
+  const int bs = a.pm.blk_shift, nb = 1 << bs;  // tokens per block
+  const int tail = (t & (nb - 1)) + 1;        // tokens of the own block
+  const int epp = (kMfmaEntChunk * 4) >> bs;  // entries staged per pass
 
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + hk * D * 2;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + hk * D * 2;
   const int64_t rowbytes = (int64_t)hkv * D * 2;
-  const int64_t own_row = a.pm.token_slot(seq, b_own * kBlock);  // always present
+  const int64_t own_row = a.pm.token_slot(seq, b_own << bs);  // always present
   const uint32_t own_t = WIDE ? (uint32_t)own_row : (uint32_t)(own_row * rowbytes);
   const int cv = c16 < D / 8 ? c16 : 0;
   const uint32_t lane_c = 16 * cv;  // 16-byte chunk cv of a K or V row
@@ -236,13 +239,15 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   // order of the Q fragments)
   const uint32_t kr_off = c16 * KP;
 
-  for (int cb = e_beg; cb < e_end; cb += kMfmaEntChunk) {
-    const int nloc = min(e_end, cb + kMfmaEntChunk) - cb;
+  // list token p -> its place in trow
+  auto tslot = [](int p) { return (p >> 4) * 16 + ((p & 3) << 2) + ((p & 15) >> 2); };
+  for (int cb = e_beg; cb < e_end; cb += epp) {
+    const int nloc = min(e_end, cb + epp) - cb;
     __syncthreads();
     // Stage the valid entries of [cb, cb + nloc) at the front, in list
     // order (a block-wide prefix count of the valid flags), so that every
-    // tile but the last holds four whole blocks.  The own block is the last
-    // entry of the list, hence the last valid entry of its chunk.
+    // tile but the last holds only tokens to attend.  The own block is the
+    // last entry of the list, hence the last valid entry of its chunk.
     int nv = 0;
     for (int i0 = 0; i0 < nloc; i0 += NT) {
       const int i = i0 + (int)threadIdx.x;
@@ -262,27 +267,32 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
         tot += c;
       }
       if (ok) {
-        const int64_t r0 = a.pm.token_slot(seq, b * kBlock);
-        const int nt = own ? tail : kBlock;
-        uint32_t* tp = trow + (pos / 4) * 16 + (pos % 4);
+        const int64_t r0 = a.pm.token_slot(seq, b << bs);
+        const int nt = own ? tail : nb;
+        const int p0 = pos << bs;
+        if (nb == 4) {  // QSA blocks: four stores, no loop
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t r = j < nt ? r0 + j : own_row;
-          tp[4 * j] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+          for (int j = 0; j < 4; ++j) {
+            const int64_t r = j < nt ? r0 + j : own_row;
+            trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+          }
+        } else {
+          for (int j = 0; j < nt; ++j) {
+            const int64_t r = r0 + j;
+            trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+          }
         }
       }
       nv = tot;
       __syncthreads();
     }
-    for (int i = nv + (int)threadIdx.x; i < ((nv + 3) & ~3); i += NT) {
-      uint32_t* tp = trow + (i / 4) * 16 + (i % 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tp[4 * j] = own_t;
-    }
-    __syncthreads();
-    const int n_tiles = (nv + 3) / 4;
-    const int last = n_tiles - 1;
     const bool own_here = rl.e_own >= cb && rl.e_own < cb + nloc;
+    // tokens to attend: whole blocks, the own block's tail last
+    const int ntok = own_here ? ((nv - 1) << bs) + tail : (nv << bs);
+    for (int p = ntok + (int)threadIdx.x; p < ((ntok + 15) & ~15); p += NT) trow[tslot(p)] = own_t;
+    __syncthreads();
+    const int n_tiles = (ntok + 15) / 16;
+    const int last = n_tiles - 1;
     // A tile is 16 tokens, tile row 4i + j = entry i, token j.  The K and
     // V rows of the wave's next tile are loaded while the current one is
     // computed, both the same way: load i reads entry i, lane group g its
@@ -332,10 +342,9 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
       }
       float x[4];
       if constexpr (MASK) {
-        const int pos = tile * 4 + g;
-        const int nt = pos < nv - 1 ? kBlock : (pos == nv - 1 ? (own_here ? tail : kBlock) : 0);
+        const int p0 = tile * 16 + 4 * g;  // list token of row r: p0 + r
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = r < nt ? sc[r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) x[r] = p0 + r < ntok ? sc[r] : -INFINITY;
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = sc[r];

@@ -11,7 +11,6 @@ namespace qsa {
 using bf16_t = uint16_t;  // bfloat16 storage (upper half of a binary32)
 
 constexpr int kWave = 64;
-constexpr int kBlock = QSA_BLOCK;
 
 // ---------------------------------------------------------------- dtypes
 
@@ -85,16 +84,18 @@ struct PageMap {
   const int32_t* table;   // [n_seqs][max_pages]
   int32_t max_pages;
   int32_t page_shift;     // log2(page_size)
+  int32_t blk_shift;      // log2(tokens per pooled block)
   __device__ __forceinline__ int64_t token_slot(int seq, int tok) const {
     // global token-row index: page * page_size + slot
     int32_t page = table[(int64_t)seq * max_pages + (tok >> page_shift)];
     return ((int64_t)page << page_shift) + (tok & ((1 << page_shift) - 1));
   }
+  // log2(pooled blocks per page)
+  __device__ __forceinline__ int bpp_shift() const { return page_shift - blk_shift; }
   // row index of block b of sequence seq in the pooled-key array
   __device__ __forceinline__ int64_t block_slot(int seq, int b) const {
-    int tok = b * kBlock;
-    int32_t page = table[(int64_t)seq * max_pages + (tok >> page_shift)];
-    int sh = page_shift - 2;
+    const int sh = bpp_shift();
+    int32_t page = table[(int64_t)seq * max_pages + (b >> sh)];
     return ((int64_t)page << sh) + (b & ((1 << sh) - 1));
   }
 };

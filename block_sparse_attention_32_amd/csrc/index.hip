@@ -40,18 +40,34 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   const int b0 = a.blk_begin[s];
   const int b = (b0 < 0 ? 0 : b0) + bl;
   const int len = min(a.seq_len[s], a.max_seq_len);
-  if (b >= len / kBlock) return;
+  if (b >= (len >> a.pm.blk_shift)) return;
   const T* kidx = static_cast<const T*>(a.kidx);
   T* kbar = static_cast<T*>(a.kbar);
-  const int64_t row0 = a.pm.token_slot(s, b * kBlock);  // 4 rows, one page
+  const int nb = 1 << a.pm.blk_shift;
+  const int64_t row0 = a.pm.token_slot(s, b << a.pm.blk_shift);  // nb rows, one page
   const T* src = kidx + row0 * DI + part * V;
-  float r0[V], r1[V], r2[V], r3[V], o[V];
-  Vec<T>::load(src, r0);
-  Vec<T>::load(src + DI, r1);
-  Vec<T>::load(src + 2 * DI, r2);
-  Vec<T>::load(src + 3 * DI, r3);
+  float o[V];
+  if (nb == 4) {  // QSA: all four loads in flight at once
+    float r0[V], r1[V], r2[V], r3[V];
+    Vec<T>::load(src, r0);
+    Vec<T>::load(src + DI, r1);
+    Vec<T>::load(src + 2 * DI, r2);
+    Vec<T>::load(src + 3 * DI, r3);
 #pragma unroll
-  for (int i = 0; i < V; ++i) o[i] = (((r0[i] + r1[i]) + r2[i]) + r3[i]) * 0.25f;
+    for (int i = 0; i < V; ++i) o[i] = ((r0[i] + r1[i]) + r2[i]) + r3[i];
+  } else {
+    Vec<T>::load(src, o);
+    for (int j = 1; j < nb; ++j) {
+      float r[V];
+      Vec<T>::load(src + j * DI, r);
+#pragma unroll
+      for (int i = 0; i < V; ++i) o[i] += r[i];
+    }
+  }
+  // the mean: a power-of-two scale, exact
+  const float inv = 1.0f / (float)nb;
+#pragma unroll
+  for (int i = 0; i < V; ++i) o[i] *= inv;
   Vec<T>::store(kbar + a.pm.block_slot(s, b) * DI + part * V, o);
 }
 
@@ -148,9 +164,9 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 // Page ids of the blocks [c0, c0 + kChunk) of sequence seq, staged in LDS.
 __device__ __forceinline__ void stage_pages(const PageMap& pm, int seq, int c0, int n,
                                             int32_t* pages) {
-  const int first = (c0 * kBlock) >> pm.page_shift;
+  const int first = c0 >> pm.bpp_shift();
   const int last_b = min(c0 + kChunk, n) - 1;
-  const int cnt = ((last_b * kBlock) >> pm.page_shift) - first + 1;
+  const int cnt = (last_b >> pm.bpp_shift()) - first + 1;
   const int32_t* row = pm.table + (int64_t)seq * pm.max_pages + first;
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) pages[i] = row[i];
   __syncthreads();
@@ -192,8 +208,8 @@ __device__ __forceinline__ void chunk_scores(const IdxArgs& a, int seq, int n, i
   stage_pages(a.pm, seq, c0, n, pages);
   const T* kbar = static_cast<const T*>(a.kbar);
   const int gi = threadIdx.x / G, part = threadIdx.x % G;
-  const int first = (c0 * kBlock) >> a.pm.page_shift;
-  const int bsh = a.pm.page_shift - 2;  // log2(blocks per page)
+  const int bsh = a.pm.bpp_shift();  // log2(blocks per page)
+  const int first = c0 >> bsh;
 #pragma unroll 1
   for (int it0 = 0; it0 < NIT; it0 += U) {
     uint4 raw[U][LPR];
@@ -202,7 +218,7 @@ __device__ __forceinline__ void chunk_scores(const IdxArgs& a, int seq, int n, i
       const int b = c0 + (it0 + u) * RPI + gi;
       if (b < n) {
         const int64_t slot =
-            ((int64_t)pages[((b * kBlock) >> a.pm.page_shift) - first] << bsh) +
+            ((int64_t)pages[(b >> bsh) - first] << bsh) +
             (b & ((1 << bsh) - 1));
         const T* rowp = kbar + slot * DI;
         if constexpr (kBf) {
@@ -239,7 +255,7 @@ __global__ void __launch_bounds__(256) scores_kernel(IdxArgs a, float* scores, i
   __shared__ int32_t pages[kChunk];
   const int row = blockIdx.y;
   const int seq = a.seq_of(row);
-  const int n = a.pos_of(row) / kBlock;
+  const int n = a.pos_of(row) >> a.pm.blk_shift;
   const int c0 = blockIdx.x * kChunk;
   if (c0 >= n) return;
   typename RowQuery<T, DI, HI>::type iq;
@@ -257,7 +273,7 @@ struct RowPlan {
   int seq, n, W, jw;
   __device__ __forceinline__ RowPlan(const TopkArgs& t, int row) {
     seq = t.idx.seq_of(row);
-    n = t.idx.pos_of(row) / kBlock;
+    n = t.idx.pos_of(row) >> t.idx.pm.blk_shift;
     W = (n + kChunk - 1) / kChunk;
     jw = row_jw(n, t.top_k);
   }
@@ -368,6 +384,10 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
   constexpr int E = kUnionCap / kSelThreads;
   constexpr int R = E / JW;
   const int un = nw * JW;
+  if (un < top_k) {  // the union bounds nothing: exact select over every key
+    select_full(src, n, top_k, sel_row, n_sel, row, sh);
+    return;
+  }
   const int e0 = (int)threadIdx.x * E;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t k[E];

@@ -10,17 +10,18 @@ namespace qsa {
 constexpr int kChunk = 1024;        // candidate blocks per workgroup (4 per thread)
 constexpr int kDirectCap = 8192;    // rows with <= this many candidates select in one pass
 constexpr int kUnionCap = 4096;     // (key, id) pairs of the per-wave tops of one row
-constexpr int kSelCap = 2048;       // survivors gathered into LDS for the final select
+constexpr int kSelCap = 4096;       // survivors gathered into LDS for the final select
 constexpr int kMaxIdxHeads = 8;
 constexpr int kMaxJw = 16;
 
 // Per-wave top count: each wave of each chunk publishes its jw best
 // (key, id) pairs: the largest power of two that fits kUnionCap, at most
-// kMaxJw.  Rows that take
-// this path have at least 9 chunks (more than kDirectCap candidates); the
-// union then holds at least 4 * W * jw >= 1024 > QSA_MAX_TOPK pairs.  A larger
-// jw makes a wave whose jw-th key still reaches the bound (a "saturated"
-// wave, rescanned in full) rarer.
+// kMaxJw.  Rows that take this path have at least 9 chunks (more than
+// kDirectCap candidates); the union then holds 4 * W * jw >= 576 pairs, at
+// least 2048 from 64 chunks on.  A union smaller than top_k gives no bound:
+// such rows select exactly over every key.  A larger jw makes a wave whose
+// jw-th key still reaches the bound (a "saturated" wave, rescanned in full)
+// rarer.
 __host__ __device__ inline int row_jw(int n, int top_k) {
   (void)top_k;
   int W = (n + kChunk - 1) / kChunk;

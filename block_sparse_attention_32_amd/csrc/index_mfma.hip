@@ -73,7 +73,7 @@ __device__ __forceinline__ void load_tile_meta(const PIdxArgs& a, int tile, Tile
     const bool ok = rl < a.rows;
     const int row = a.row0 + rl;
     tm.seq[i] = ok ? a.idx.seq_of(row) : -1;
-    tm.n[i] = ok ? a.idx.pos_of(row) / kBlock : 0;
+    tm.n[i] = ok ? a.idx.pos_of(row) >> a.idx.pm.blk_shift : 0;
     tm.tau[i] = (ok && with_tau) ? a.tau[rl] : 0u;
     tm.done[i] = ok ? 0 : 1;
   }
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
       lmax[at] = kNegInf;
     }
     const int region = kPSurvCap / a.splits;
-    const int bpp_sh = a.idx.pm.page_shift - 2;  // log2(blocks per page)
+    const int bpp_sh = a.idx.pm.bpp_shift();  // log2(blocks per page)
     const int n_hi = tm.n_hi;
     // blocks at or past a row's candidate count only occur in tiles that
     // reach past the pass's smallest count
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
   __syncthreads();
   for (int i = threadIdx.x; i < kPQT; i += blockDim.x) {
     const int rl = tile * kPQT + i;
-    if (rl < a.rows) atomicMin(&lo, a.idx.pos_of(a.row0 + rl) / kBlock);
+    if (rl < a.rows) atomicMin(&lo, a.idx.pos_of(a.row0 + rl) >> a.idx.pm.blk_shift);
   }
   __syncthreads();
   if (threadIdx.x == 0) a.tile_stride[tile] = pass_stride(lo, a.top_k);
@@ -330,7 +330,7 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
 __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
-  const int n = a.idx.pos_of(row) / kBlock;
+  const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
   if (n <= a.top_k) return;
   const int s = a.row_stride[rl];
   const int n_groups = (n + kPGrp - 1) / kPGrp;
@@ -383,7 +383,7 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
   __shared__ uint32_t offs[kPMaxSplits + 1];
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
-  const int n = a.idx.pos_of(row) / kBlock;
+  const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
   int32_t* sel_row = a.sel + (int64_t)row * a.top_k;
   if (n <= a.top_k) {
     for (int j = threadIdx.x; j < a.top_k; j += blockDim.x) sel_row[j] = j < n ? j : -1;

@@ -15,9 +15,11 @@ workloads they discuss, see the design notes):
   summation order gives the same scores bit for bit.
 * Head weights w = (round(15 u) + 1) / 16 with u ~ U(0, 1): multiples of
   1/16 in [1/16, 1], never zero.
-* Needle blocks: all 4 indexer keys of the block equal 3 * s_seq, which makes
-  the block score far above every other block for every query that can see
-  it (the generator does not check this; the tests do).
+* Needle blocks: all 4 indexer keys of a 4-token span equal 3 * s_seq, which
+  makes the block score far above every other block for every query that can
+  see it (the generator does not check this; the tests do).  Needles are
+  placed in 4-token units whatever the block size, so that workloads that
+  differ only in the block size draw identical inputs.
 * The KV cache is paged: page_size tokens per page; a sequence's pages are
   listed in block_table (a seeded permutation of the page pool when
   permute_pages is set, the identity otherwise).
@@ -30,7 +32,7 @@ from dataclasses import dataclass
 
 import torch
 
-BLOCK_TOKENS = 4  # micro-block length used to place needles
+BLOCK_TOKENS = 4  # span length used to place needles (QSA's micro-block)
 
 
 @dataclass(frozen=True)
@@ -55,6 +57,7 @@ class Workload:
     chunk: int = 0          # prefill chunk length; 0 = all rows in one step
     hidden: int = 0         # hidden size of the indexer projections ("project")
     seed: int = 0
+    block: int = 4          # tokens per pooled block (1: token-granular selection)
 
     @property
     def torch_dtype(self):
@@ -107,6 +110,16 @@ WORKLOADS = {
         name="prefill_1m", mode="prefill", dtype="bf16", n_seqs=1, n_ctx=0,
         n_new=1048576, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
         n_needles=32, chunk=32768, seed=1005),
+    # token-granular selection (block size 1) with the same 2,048-token
+    # budget, on the same inputs as the block workloads they are named after
+    "prefill_8k_at_128k_tok": Workload(
+        name="prefill_8k_at_128k_tok", mode="prefill", dtype="bf16", n_seqs=1,
+        n_ctx=131072, n_new=8192, hq=16, hkv=2, d=128, hi=4, di=64,
+        top_k=2048, n_needles=16, seed=1004, block=1),
+    "decode_8x32k_tok": Workload(
+        name="decode_8x32k_tok", mode="decode", dtype="bf16", n_seqs=8,
+        n_ctx=32768, n_new=1, hq=16, hkv=2, d=128, hi=4, di=64, top_k=2048,
+        n_needles=8, permute_pages=True, seed=1002, block=1),
 }
 
 
@@ -128,7 +141,7 @@ class Cache:
     k: torch.Tensor            # [n_pages, page, Hkv, D]
     v: torch.Tensor            # [n_pages, page, Hkv, D]
     kidx: torch.Tensor         # [n_pages, page, Di]
-    kbar: torch.Tensor         # [n_pages, page/4, Di] (filled by pooling)
+    kbar: torch.Tensor         # [n_pages, page/block, Di] (filled by pooling)
     block_table: torch.Tensor  # [n_seqs, pages_per_seq] int32
     seq_len: torch.Tensor      # [n_seqs] int32
     direction: torch.Tensor    # [n_seqs, Di] float32, entries +-1
@@ -160,7 +173,7 @@ def make_cache(wl: Workload, device="cpu", seed: int | None = None) -> Cache:
     v = torch.randn(shape_kv, generator=g, device=device).to(dt)
     kidx = grid8(torch.randn((n_pages, wl.page_size, wl.di), generator=g,
                              device=device)).to(dt)
-    kbar = torch.zeros((n_pages, wl.page_size // BLOCK_TOKENS, wl.di),
+    kbar = torch.zeros((n_pages, wl.page_size // wl.block, wl.di),
                        dtype=dt, device=device)
     direction = (torch.randint(0, 2, (wl.n_seqs, wl.di), generator=g,
                                device=device) * 2 - 1).to(torch.float32)

@@ -24,6 +24,12 @@
  *   - keieiax.jp glossary, section 長文AIのコストと応答時間にどう影響する？: the
  *     reference point is dense grouped-query attention (GQA); the dense calls
  *     below provide it on the same cache.
+ *   - blog.cecily.jp/6295, paragraph on Raschka's explanation: DeepSeek
+ *     Sparse Attention selects single tokens where QSA selects 4-token
+ *     blocks; paragraph on the trade-offs: the block index is the coarser
+ *     one.  The block size B is therefore a cache parameter: B = 4 is QSA,
+ *     B = 1 the token-granular selection (with the same 2,048-token budget,
+ *     top_k = 2048 / B), and 2, 8, 16 lie around them.
  *
  * The indexer score is not printed on the pages; this library fixes it as
  *     s[b] = sum_h w[h] * max(0, q_idx[h] . kbar[b])
@@ -44,9 +50,10 @@
  *     out-of-range device data is undefined behaviour.
  *   - Positions: query row i belongs to sequence seq_id[i] and sits at
  *     absolute position pos[i] (0-based); its own K/V/indexer key is already
- *     in the cache, and it may see tokens 0..pos[i] only.  Its own block is
- *     b_own = pos[i] / 4; blocks 0..b_own-1 are its candidates; the own
- *     block's tokens 4*b_own..pos[i] are always attended.
+ *     in the cache, and it may see tokens 0..pos[i] only.  With B tokens per
+ *     block (qsa_cache.block_size) its own block is b_own = pos[i] / B;
+ *     blocks 0..b_own-1 are its candidates; the own block's tokens
+ *     B*b_own..pos[i] are always attended.
  *   - Workspaces: size them with qsa_workspace_size().  A workspace must be
  *     zero-filled once before its first use; every call leaves its counters
  *     at zero again when its kernels finish, so a workspace can be reused by
@@ -63,9 +70,11 @@
 extern "C" {
 #endif
 
-#define QSA_BLOCK 4        /* tokens per micro-block */
-#define QSA_MAX_TOPK 512   /* largest supported top_k (the pages' budget) */
-#define QSA_MAX_BLOCKS (1 << 20) /* candidate blocks per query (4M tokens) */
+#define QSA_BLOCK 4        /* tokens per micro-block of QSA (block_size 0 means this) */
+#define QSA_MAX_BLOCK 16   /* largest supported block_size */
+#define QSA_BUDGET_TOKENS 2048 /* the pages' selection budget in tokens */
+#define QSA_MAX_TOPK 2048  /* largest supported top_k (the budget at block size 1) */
+#define QSA_MAX_BLOCKS (1 << 20) /* candidate blocks per query */
 #define QSA_MAX_SHARED_LAG 60    /* qsa_attn_decode_shared: pos[i] - pos[sel_of[i]] */
 
 typedef enum qsa_status {
@@ -92,7 +101,9 @@ typedef enum qsa_op {
  * block_table[s * max_pages_per_seq + j / page_size], slot j % page_size. */
 typedef struct qsa_cache {
   int32_t dtype;             /* qsa_dtype of k, v, kidx, kbar, q, q_idx, out */
-  int32_t page_size;         /* tokens per page: a power of two, >= 4        */
+  int32_t page_size;         /* tokens per page: a power of two, >= 4 and >= B */
+  int32_t block_size;        /* B, tokens per pooled block: 1, 2, 4, 8 or 16;
+                                0 means QSA_BLOCK (4)                        */
   int32_t n_kv_heads;        /* Hkv                                          */
   int32_t head_dim;          /* D: 32, 64 or 128                             */
   int32_t idx_dim;           /* Di: 16, 32, 64 or 128                        */
@@ -105,7 +116,7 @@ typedef struct qsa_cache {
   const void *k;             /* [n_pages][page_size][Hkv][D]                 */
   const void *v;             /* [n_pages][page_size][Hkv][D]                 */
   const void *kidx;          /* [n_pages][page_size][Di]   indexer keys      */
-  void *kbar;                /* [n_pages][page_size/4][Di] pooled keys       */
+  void *kbar;                /* [n_pages][page_size/B][Di] pooled keys       */
 } qsa_cache;
 
 /* Query rows of one call. */
@@ -119,27 +130,28 @@ typedef struct qsa_queries {
 /* Step 1 -- pooling (glossary: 4-token micro-blocks; PR #30965 digest:
  * the indexer averages the keys of each block).
  * For every sequence s, for the complete blocks b with
- *   blk_begin[s] <= b < min(seq_len[s] / 4, blk_begin[s] + max_new_blocks),
- * writes kbar[b] = (((kidx[4b] + kidx[4b+1]) + kidx[4b+2]) + kidx[4b+3]) / 4,
- * summed in float32 and rounded to nearest-even in the cache dtype.
+ *   blk_begin[s] <= b < min(seq_len[s] / B, blk_begin[s] + max_new_blocks),
+ * writes kbar[b] = ((kidx[Bb] + kidx[Bb+1]) + ... + kidx[Bb+B-1]) / B,
+ * summed left to right in float32 and rounded to nearest-even in the cache
+ * dtype (for B = 1, the key itself).
  * blk_begin: [n_seqs] device.  max_new_blocks (host) bounds the launch; 0 is
  * a no-op. */
 qsa_status qsa_pool_blocks(const qsa_cache *c, const int32_t *blk_begin,
                            int32_t max_new_blocks, void *stream);
 
 /* Step 2 -- indexer scores (glossary: the indexer rates every block).
- * For every row i and candidate block b < pos[i] / 4:
+ * For every row i and candidate block b < pos[i] / B:
  *   scores[i * ld + b] = sum_h w[i*Hi + h] * max(0, q_idx[i][h] . kbar[b])
- * accumulated in float32 (a -0 result is stored as +0).  Columns >= pos[i]/4
+ * accumulated in float32 (a -0 result is stored as +0).  Columns >= pos[i]/B
  * are not written.  q_idx: [T][Hi][Di] in the cache dtype; w: [T][Hi]
- * float32; 1 <= n_idx_heads <= 8; ld >= max_pos / 4 (host). */
+ * float32; 1 <= n_idx_heads <= 8; ld >= max_pos / B (host). */
 qsa_status qsa_index_scores(const qsa_cache *c, const qsa_queries *qm,
                             const void *q_idx, const float *w,
                             int32_t n_idx_heads, float *scores, int64_t ld,
                             void *stream);
 
 /* Step 3 -- top-k block selection (glossary: at most 512 blocks per query,
- * best first).  For every row i with n = pos[i] / 4 candidates:
+ * best first).  For every row i with n = pos[i] / B candidates:
  *   n_sel[i] = min(top_k, n);
  *   sel[i * top_k + j], j < n_sel[i]: the ids of the n_sel[i] highest scores,
  *       ties broken toward the lower block id, written in ascending order;
@@ -147,7 +159,9 @@ qsa_status qsa_index_scores(const qsa_cache *c, const qsa_queries *qm,
  * Score source: if scores != NULL they are read from scores[i * ld + b]
  * (as written by qsa_index_scores); if scores == NULL (fused mode) they are
  * computed from q_idx, w and kbar as in qsa_index_scores, and q_idx, w,
- * n_idx_heads must be given.  1 <= top_k <= QSA_MAX_TOPK.
+ * n_idx_heads must be given.  1 <= top_k <= QSA_MAX_TOPK (the pages'
+ * budget is 2048 / B).  Selections of more than 512 blocks of rows with
+ * fewer than about 64 K candidates take an exact but slower path.
  * ws: workspace of qsa_workspace_size(QSA_OP_TOPK, ...) bytes. */
 qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
                            const float *scores, int64_t ld,
@@ -160,11 +174,11 @@ qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
  * whole selected blocks plus the current fractional block; sparse FA
  * explainer: tiled softmax attention).  For every row i and query head hq
  * (KV head hk = hq / (n_q_heads / Hkv)), over the token set
- *   S_i = {4b .. 4b+3 : b in sel[i][0 .. n_sel[i]-1]} U {4*(pos[i]/4) .. pos[i]}
+ *   S_i = {Bb .. Bb+B-1 : b in sel[i][0 .. n_sel[i]-1]} U {B*(pos[i]/B) .. pos[i]}
  *   out[i][hq] = sum_{j in S_i} softmax_j(scale * q[i][hq] . K[j][hk]) V[j][hk]
  * accumulated in float32 and rounded to nearest-even in the cache dtype.
  * q, out: [T][n_q_heads][D] in the cache dtype; sel/n_sel as written by
- * qsa_topk_blocks (row stride top_k).  Ids outside [0, pos[i]/4) among
+ * qsa_topk_blocks (row stride top_k).  Ids outside [0, pos[i]/B) among
  * the first n_sel[i] entries are skipped.
  * qsa_attn_decode splits each row's token set across workgroups (for few
  * rows); qsa_attn_prefill gives each row its own workgroup (for many rows).
@@ -205,8 +219,8 @@ qsa_status qsa_index_project(const qsa_cache *c, const qsa_queries *qm,
  * s = sel_of[i] (a row of the same call, same sequence, at position
  * pos[s] <= pos[i] <= pos[s] + QSA_MAX_SHARED_LAG), and everything from the
  * start of that row's own block up to its own position:
- *   S_i = {4b .. 4b+3 : b in sel[s][0 .. n_sel[s]-1], b < pos[s]/4}
- *         U {4*(pos[s]/4) .. pos[i]}
+ *   S_i = {Bb .. Bb+B-1 : b in sel[s][0 .. n_sel[s]-1], b < pos[s]/B}
+ *         U {B*(pos[s]/B) .. pos[i]}
  * sel_of[i] = i gives exactly qsa_attn_decode's result.  sel_of: [T] device
  * int32; rows outside the limits above are clamped to them (their result
  * is unspecified).  ws: qsa_workspace_size(QSA_OP_ATTN_DECODE_SHARED, ...). */

@@ -37,7 +37,7 @@ class Problem:
 
     # ---- HIP path
     def pool_all(self):
-        P.pool_all(self.cv, self.wl.n_seqs, self.wl.total_len // 4, self.device)
+        P.pool_all(self.cv, self.wl.n_seqs, self.wl.total_len // self.wl.block, self.device)
 
     def step(self, mode=None):
         mode = mode or self.wl.mode
@@ -49,7 +49,7 @@ class Problem:
     def gpu_kbar(self, s: int) -> np.ndarray:
         """Pooled keys of sequence s as written by the GPU, in block order."""
         wl = self.wl
-        nb = wl.total_len // 4
+        nb = wl.total_len // wl.block
         n_p = -(-wl.total_len // wl.page_size)
         pages = self.cache.block_table[s, :n_p].long()
         kb = self.cache.kbar[pages].reshape(-1, wl.di)[:nb]
@@ -59,17 +59,17 @@ class Problem:
     def kbar_oracle(self, s: int) -> np.ndarray:
         if s not in self._kbar_oracle:
             _, _, kidx = W.seq_view(self.cache, s)
-            self._kbar_oracle[s] = O.pool_blocks(f64(kidx), self.wl.dtype)
+            self._kbar_oracle[s] = O.pool_blocks(f64(kidx), self.wl.dtype, block=self.wl.block)
         return self._kbar_oracle[s]
 
     def oracle_select(self, i: int) -> np.ndarray:
         s, t = self.seq_id_list[i], self.pos_list[i]
         return O.qsa_select_row(self.kbar_oracle(s), f64(self.qs.q_idx[i]),
-                                f64(self.qs.w[i]), t, self.wl.top_k)
+                                f64(self.qs.w[i]), t, self.wl.top_k, self.wl.block)
 
     def oracle_scores(self, i: int) -> np.ndarray:
         s, t = self.seq_id_list[i], self.pos_list[i]
-        n = O.n_candidates(t)
+        n = O.n_candidates(t, self.wl.block)
         return O.block_scores(self.kbar_oracle(s)[:n], f64(self.qs.q_idx[i]), f64(self.qs.w[i]))
 
     def token_kv(self, s: int, tokens: np.ndarray):
@@ -82,7 +82,7 @@ class Problem:
 
     def oracle_attend(self, i: int, sel: np.ndarray) -> np.ndarray:
         s, t = self.seq_id_list[i], self.pos_list[i]
-        toks = O.token_set(sel, t)
+        toks = O.token_set(sel, t, self.wl.block)
         k, v = self.token_kv(s, toks)
         return O.attend(f64(self.qs.q[i]), k, v, np.arange(len(toks)), self.wl.scale)
 

@@ -71,6 +71,7 @@ def test_workspace_sizes(libqsa):
     ("dtype", 7, -1), ("page_size", 48, -1), ("page_size", 2, -1), ("n_kv_heads", 0, -1),
     ("head_dim", 96, -2), ("idx_dim", 24, -2), ("max_seq_len", 5000, -1),
     ("block_table", None, -1), ("seq_len", None, -1),
+    ("block_size", 3, -1), ("block_size", 32, -1), ("block_size", -4, -1),
 ])
 def test_cache_validation(libqsa, field, value, status):
     c = _cache(**{field: value})
@@ -96,7 +97,7 @@ def test_call_validation(libqsa):
     ws = L.qsa_workspace_size(B.QSA_OP_TOPK, R(c), R(q), 0, 512)
     tk = L.qsa_topk_blocks
     assert tk(R(c), R(q), 8, 512, None, None, 0, 0, 8, 8, 8, ws, None) == -1      # top_k 0
-    assert tk(R(c), R(q), 8, 512, None, None, 0, 513, 8, 8, 8, ws, None) == -1    # > 512
+    assert tk(R(c), R(q), 8, 512, None, None, 0, 2049, 8, 8, 8, ws, None) == -1   # > 2048
     assert tk(R(c), R(q), None, 0, None, 8, 4, 512, 8, 8, 8, ws, None) == -1      # fused, no q_idx
     assert tk(R(c), R(q), 8, 512, None, None, 0, 512, None, 8, 8, ws, None) == -1  # no sel
     assert tk(R(c), R(q), 8, 512, None, None, 0, 512, 8, 8, 8, ws - 1, None) == -3
@@ -129,3 +130,33 @@ def test_call_validation(libqsa):
     # zero rows: valid and a no-op
     z = _rows(n_rows=0, seq_id=None, pos=None)
     assert L.qsa_attn_prefill(R(c), R(z), None, 16, 8, 8, 512, f(0.1), None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("block", [0, 1, 2, 4, 8, 16])
+def test_block_sizes_accepted(libqsa, block):
+    """Block sizes 1..16 (0 = QSA's 4) are valid; a block longer than a page
+    is not.  Finer blocks mean more candidates: the top-k workspace never
+    shrinks as the block gets finer."""
+    c, q = _cache(block_size=block), _rows()
+    ws = libqsa.qsa_workspace_size
+    assert ws(B.QSA_OP_TOPK, R(c), R(q), 0, 512) > 0
+    assert ws(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 2048) > 0
+    assert libqsa.qsa_pool_blocks(R(c), None, 0, None) == 0
+    if block:
+        coarser = _cache(block_size=min(16, 2 * block))
+        assert ws(B.QSA_OP_TOPK, R(c), R(q), 0, 512) >= ws(B.QSA_OP_TOPK, R(coarser), R(q), 0, 512)
+    small_page = _cache(block_size=16, page_size=8)
+    assert libqsa.qsa_pool_blocks(R(small_page), 8, 4, None) == -1
+
+
+def test_top_k_limit(libqsa):
+    c, q = _cache(block_size=1), _rows()
+    f = ctypes.c_float
+    tk = libqsa.qsa_topk_blocks
+    wsz = libqsa.qsa_workspace_size(B.QSA_OP_TOPK, R(c), R(q), 0, 2048)
+    assert B.QSA_MAX_TOPK == 2048
+    assert tk(R(c), R(q), None, 0, 8, 8, 4, 2049, 8, 8, 8, wsz, None) == -1
+    assert tk(R(c), R(q), None, 0, 8, 8, 4, 0, 8, 8, 8, wsz, None) == -1
+    at = libqsa.qsa_attn_decode
+    wsa = libqsa.qsa_workspace_size(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 2048)
+    assert at(R(c), R(q), 8, 16, 8, 8, 2049, f(0.1), 8, 8, wsa, None) == -1

@@ -112,3 +112,32 @@ def test_generation_is_seeded():
     b = W.make_cache(wl)
     assert torch.equal(a.k, b.k) and torch.equal(a.kidx, b.kidx)
     assert a.needles == b.needles
+
+
+@pytest.mark.parametrize("tok,blk", [("prefill_8k_at_128k_tok", "prefill_8k_at_128k"),
+                                     ("decode_8x32k_tok", "decode_8x32k")])
+def test_token_granular_workloads_share_inputs(tok, blk):
+    """The token-granular workloads draw the same inputs as the block
+    workloads they are named after; only the block size (1) and the budget
+    (2,048 tokens, so top_k = 2048) differ."""
+    a, b = W.WORKLOADS[tok], W.WORKLOADS[blk]
+    assert (a.block, a.top_k) == (1, 2048) and (b.block, b.top_k) == (4, 512)
+    assert a.replace(name=b.name, block=4, top_k=512) == b
+    small = dict(n_ctx=2048, n_new=4, n_seqs=1)
+    ca, cb = W.make_cache(a.replace(**small)), W.make_cache(b.replace(**small))
+    assert torch.equal(ca.k, cb.k) and torch.equal(ca.kidx, cb.kidx) and ca.needles == cb.needles
+    assert ca.kbar.shape[1] == 4 * cb.kbar.shape[1] == a.page_size
+
+
+def test_token_granular_selects_needle_tokens():
+    """At block size 1 every token of a planted needle span is selected."""
+    wl = W.WORKLOADS["decode_8x32k_tok"].replace(n_ctx=12000, n_seqs=1)
+    c = W.make_cache(wl)
+    seq_id, pos = W.decode_rows(wl)
+    qs = W.make_queries(wl, c, seq_id, pos)
+    _, _, kidx = W.seq_view(c, 0)
+    kbar = O.pool_blocks(_np(kidx), wl.dtype, block=1)
+    sel = O.qsa_select_row(kbar, _np(qs.q_idx[0]), qs.w[0].double().numpy(), pos[0],
+                           wl.top_k, block=1)
+    toks = {4 * b + i for b in c.needles[0] for i in range(4)}
+    assert len(sel) == 2048 and toks <= set(sel.tolist())
