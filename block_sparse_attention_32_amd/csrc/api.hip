@@ -106,7 +106,7 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
   return p;
 }
 
-TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm) {
+TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm, int top_k) {
   TopkPlan p;
   const int max_n = qm->max_pos / cache_block(c);
   p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
@@ -118,7 +118,7 @@ TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm) {
   p.ws_ld = p.materialize ? full : (full < kDirectCap ? full : kDirectCap);
   size_t o = 0;
   p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
-  p.off_tops = o;   o = align256(o + (size_t)p.rows * kUnionCap * 8);
+  p.off_tops = o;   o = align256(o + (size_t)p.rows * union_cap(top_k) * 8);
   p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
   p.total = o;
   return p;
@@ -309,7 +309,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
     if (n_idx_heads < 1 || n_idx_heads > kMaxIdxHeads) return QSA_ERR_INVALID_ARG;
   }
   if (qm->n_rows > 0 && (sel == nullptr || n_sel == nullptr)) return QSA_ERR_INVALID_ARG;
-  const TopkPlan p = topk_plan(c, qm);
+  const TopkPlan p = topk_plan(c, qm, top_k);
   const PidxPlan pp = pidx_plan(qm);
   const bool mfma = scores == nullptr && qm->n_rows >= kPMinRows &&
                     pidx_supported(c->dtype, c->idx_dim, n_idx_heads);
@@ -461,7 +461,7 @@ size_t qsa_workspace_size(int32_t op, const qsa_cache* c, const qsa_queries* qm,
   if (check_cache(c) != QSA_OK || check_queries(c, qm) != QSA_OK) return 0;
   switch (op) {
     case QSA_OP_TOPK: {
-      const size_t a = topk_plan(c, qm).total, b = pidx_plan(qm).total;
+      const size_t a = topk_plan(c, qm, top_k).total, b = pidx_plan(qm).total;
       return a > b ? a : b;
     }
     case QSA_OP_ATTN_DECODE:

@@ -305,17 +305,22 @@ struct RowKeys {
   const T* kbar;
   const T* qrow;     // the row's q_idx, [hi][DI]
   const float* wrow; // the row's head weights
-  int hi, seq;
-  PageMap pm;
+  const int32_t* pages;  // the sequence's row of the page table
+  int hi, bsh;           // heads; log2(blocks per page)
+  // (56 bytes: small enough to travel in registers to the out-of-line
+  // selection routines)
   __device__ __forceinline__ RowKeys(const float* g, const uint32_t* st, const TopkArgs& t, int row,
                                      int sq)
       : given(g), stored(st), kbar(static_cast<const T*>(t.idx.kbar)),
         qrow(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI),
-        wrow(t.idx.w + (int64_t)row * t.idx.hi), hi(t.idx.hi), seq(sq), pm(t.idx.pm) {}
+        wrow(t.idx.w + (int64_t)row * t.idx.hi),
+        pages(t.idx.pm.table + (int64_t)sq * t.idx.pm.max_pages), hi(t.idx.hi),
+        bsh(t.idx.pm.bpp_shift()) {}
   __device__ __forceinline__ uint32_t operator()(int e) const {
     if (given != nullptr) return score_key(given[e]);
     if (stored != nullptr) return stored[e];
-    const T* p = kbar + pm.block_slot(seq, e) * DI;
+    const int64_t slot = ((int64_t)pages[e >> bsh] << bsh) + (e & ((1 << bsh) - 1));
+    const T* p = kbar + slot * DI;
     float s = 0.0f;
     for (int h = 0; h < hi; ++h) {
       float d = 0.0f;
@@ -370,24 +375,20 @@ struct LongShared {
 };
 
 // Tail of a long row (the last chunk to finish), JW keys per published run.
-// Thread t holds union entries [E t, E t + E) -- whole runs, E = kUnionCap /
+// Thread t holds union entries [E t, E t + E) -- whole runs, E = union cap /
 // 256 -- in registers, loaded at once.  tau = the k-th largest union key
 // (low bits past two radix digits cleared); a run whose last published key
 // reaches tau is saturated and rescanned from the key source; the other
 // runs' survivors (key >= tau) are placed in id order straight from the
 // registers, each run's entries ranked by id (a run lists one wave's keys
 // best first).  Then the exact select among the survivors.
-template <int JW, class Src>
+template <int JW, int E, class Src>
 __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, int nw, int n,
                                           int top_k, int32_t* sel_row, int32_t* n_sel, int row,
                                           LongShared& ls, SelShared& sh) {
-  constexpr int E = kUnionCap / kSelThreads;
+  static_assert(JW <= E, "a thread holds whole runs");
   constexpr int R = E / JW;
   const int un = nw * JW;
-  if (un < top_k) {  // the union bounds nothing: exact select over every key
-    select_full(src, n, top_k, sel_row, n_sel, row, sh);
-    return;
-  }
   const int e0 = (int)threadIdx.x * E;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t k[E];
@@ -403,8 +404,8 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
     }
   }
   if (threadIdx.x == 0) ls.n_sat = 0u;
-  uint32_t tau;
-  {
+  uint32_t tau = 1u;  // a union smaller than top_k bounds nothing: every key survives
+  if (un >= top_k) {
     int r;
     bool resolved;
     radix_kth_regs<E>(k, un, top_k, sh, tau, r, resolved, 2);
@@ -533,7 +534,9 @@ __device__ __noinline__ void select_direct(Get get, int n, int top_k, int32_t* s
   if (threadIdx.x == 0) n_sel[row] = top_k;
 }
 
-template <typename T, int DI, int HI>
+// LARGE: selections of more than kLargeTopk blocks (their wider union of
+// per-wave tops is held 32 entries per thread in the tail).
+template <typename T, int DI, int HI, bool LARGE>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   __shared__ uint32_t keys[kChunk];
   __shared__ int32_t pages[kChunk];
@@ -571,7 +574,8 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
         st_agent(ws_row + c0 + i, keys[i]);
     }
   }
-  uint64_t* tops = t.tops + (int64_t)rl * kUnionCap;
+  constexpr int UCAP = LARGE ? kUnionCapL : kUnionCap;
+  uint64_t* tops = t.tops + (int64_t)rl * UCAP;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   if (!direct) {
     // per-wave top-jw (key, id) pairs of this chunk, best first (key 0 =
@@ -606,12 +610,17 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   // ---- last chunk of a long row
   const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
   const int nw = p.W * kSelWaves;
+  constexpr int E = UCAP / kSelThreads;
   switch (p.jw) {
-    case 1: long_tail<1>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 2: long_tail<2>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 4: long_tail<4>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 8: long_tail<8>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    default: long_tail<16>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    default:
+      if constexpr (LARGE)
+        long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
+      break;
   }
 }
 
@@ -635,7 +644,10 @@ static void launch_scores(const IdxArgs& a, int n_rows, int max_n, float* scores
 template <typename T, int DI, int HI>
 static void launch_topk(const TopkArgs& t, int rows, hipStream_t st) {
   dim3 grid((unsigned)t.w_max, (unsigned)rows);
-  hipLaunchKernelGGL((topk_kernel<T, DI, HI>), grid, dim3(256), 0, st, t);
+  if (large_topk(t.top_k))
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, true>), grid, dim3(256), 0, st, t);
+  else
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, false>), grid, dim3(256), 0, st, t);
 }
 
 // compile-time indexer head count: the real count rounded up to 2, 4 or 8
