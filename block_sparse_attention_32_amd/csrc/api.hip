@@ -76,7 +76,7 @@ qsa_status launched() {
 // ------------------------------------------------------------- top-k plan
 
 struct TopkPlan {
-  int rows, w_max, materialize;
+  int rows, w_max, materialize, ucap;
   int64_t ws_ld;
   size_t off_ctr, off_tops, off_scores, total;
 };
@@ -109,16 +109,19 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
 TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm, int top_k) {
   TopkPlan p;
   const int max_n = qm->max_pos / cache_block(c);
-  p.rows = qm->n_rows < kRowBatch ? qm->n_rows : kRowBatch;
-  if (p.rows < 1) p.rows = 1;
   p.w_max = (max_n + kChunk - 1) / kChunk;
   if (p.w_max < 1) p.w_max = 1;
+  p.ucap = union_cap(top_k, p.w_max);
+  // rows per launch (fewer for the wider unions)
+  const int batch = kRowBatch * kUnionCap / p.ucap;
+  p.rows = qm->n_rows < batch ? qm->n_rows : batch;
+  if (p.rows < 1) p.rows = 1;
   const int64_t full = (int64_t)p.w_max * kChunk;
   p.materialize = (size_t)p.rows * (size_t)full * 4 <= kMaterializeBytes;
   p.ws_ld = p.materialize ? full : (full < kDirectCap ? full : kDirectCap);
   size_t o = 0;
   p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
-  p.off_tops = o;   o = align256(o + (size_t)p.rows * union_cap(top_k) * 8);
+  p.off_tops = o;   o = align256(o + (size_t)p.rows * p.ucap * 8);
   p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
   p.total = o;
   return p;
@@ -372,6 +375,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   t.ws_ld = p.ws_ld;
   t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);
   t.tops = reinterpret_cast<uint64_t*>(base + p.off_tops);
+  t.ucap = p.ucap;
   for (int r0 = 0; r0 < qm->n_rows; r0 += p.rows) {
     const int rows = (qm->n_rows - r0) < p.rows ? (qm->n_rows - r0) : p.rows;
     t.row0 = r0;

@@ -275,7 +275,7 @@ struct RowPlan {
     seq = t.idx.seq_of(row);
     n = t.idx.pos_of(row) >> t.idx.pm.blk_shift;
     W = (n + kChunk - 1) / kChunk;
-    jw = row_jw(n, t.top_k);
+    jw = row_jw(n, t.ucap);
   }
 };
 
@@ -534,9 +534,10 @@ __device__ __noinline__ void select_direct(Get get, int n, int top_k, int32_t* s
   if (threadIdx.x == 0) n_sel[row] = top_k;
 }
 
-// LARGE: selections of more than kLargeTopk blocks (their wider union of
-// per-wave tops is held 32 entries per thread in the tail).
-template <typename T, int DI, int HI, bool LARGE>
+// UCAP: the union capacity of the call.  With kUnionCapL the tail of the
+// long rows runs in topk_tail_kernel (64 union entries per thread would
+// crowd this kernel's registers).
+template <typename T, int DI, int HI, int UCAP>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   __shared__ uint32_t keys[kChunk];
   __shared__ int32_t pages[kChunk];
@@ -574,7 +575,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
         st_agent(ws_row + c0 + i, keys[i]);
     }
   }
-  constexpr int UCAP = LARGE ? kUnionCapL : kUnionCap;
+  constexpr bool OWN_TAIL = UCAP <= kUnionCapM;  // the tail runs here
   uint64_t* tops = t.tops + (int64_t)rl * UCAP;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   if (!direct) {
@@ -601,6 +602,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
       }
     }
   }
+  if (!OWN_TAIL && !direct) return;  // the tail follows in topk_tail_kernel
   if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
   if (direct) {
     select_direct(KeyArray{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
@@ -608,19 +610,48 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   }
 
   // ---- last chunk of a long row
+  if constexpr (OWN_TAIL) {
+    const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+    const int nw = p.W * kSelWaves;
+    constexpr int E = UCAP / kSelThreads;
+    switch (p.jw) {
+      case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      default:
+        if constexpr (E >= 32)
+          long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
+        break;
+    }
+  }
+}
+
+// The tail of the long rows of a large selection, after topk_kernel has
+// published every chunk's per-wave tops: one workgroup per row.
+template <typename T, int DI>
+__global__ void __launch_bounds__(256) topk_tail_kernel(TopkArgs t) {
+  __shared__ LongShared ls;
+  __shared__ SelShared sh;
+  const int rl = blockIdx.x, row = t.row0 + rl;
+  const RowPlan p(t, row);
+  if (p.n <= t.top_k || p.n <= kDirectCap) return;  // done by topk_kernel
+  int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
+  const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
+  uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
+  const bool keep = !given && t.materialize;
   const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+  const uint64_t* tops = t.tops + (int64_t)rl * kUnionCapL;
   const int nw = p.W * kSelWaves;
-  constexpr int E = UCAP / kSelThreads;
+  constexpr int E = kUnionCapL / kSelThreads;
   switch (p.jw) {
     case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
     case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
     case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
     case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
     case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    default:
-      if constexpr (LARGE)
-        long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
-      break;
+    default: long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
   }
 }
 
@@ -644,10 +675,14 @@ static void launch_scores(const IdxArgs& a, int n_rows, int max_n, float* scores
 template <typename T, int DI, int HI>
 static void launch_topk(const TopkArgs& t, int rows, hipStream_t st) {
   dim3 grid((unsigned)t.w_max, (unsigned)rows);
-  if (large_topk(t.top_k))
-    hipLaunchKernelGGL((topk_kernel<T, DI, HI, true>), grid, dim3(256), 0, st, t);
-  else
-    hipLaunchKernelGGL((topk_kernel<T, DI, HI, false>), grid, dim3(256), 0, st, t);
+  if (t.ucap == kUnionCapL) {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapL>), grid, dim3(256), 0, st, t);
+    hipLaunchKernelGGL((topk_tail_kernel<T, DI>), dim3((unsigned)rows), dim3(256), 0, st, t);
+  } else if (t.ucap == kUnionCapM) {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapM>), grid, dim3(256), 0, st, t);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCap>), grid, dim3(256), 0, st, t);
+  }
 }
 
 // compile-time indexer head count: the real count rounded up to 2, 4 or 8

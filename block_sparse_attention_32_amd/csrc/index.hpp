@@ -10,32 +10,35 @@ namespace qsa {
 constexpr int kChunk = 1024;        // candidate blocks per workgroup (4 per thread)
 constexpr int kDirectCap = 8192;    // rows with <= this many candidates select in one pass
 constexpr int kUnionCap = 4096;     // (key, id) pairs of the per-wave tops of one row
-constexpr int kLargeTopk = 512;     // larger selections use the wide union below
-constexpr int kUnionCapL = 8192;    // union of a row selecting more than kLargeTopk
+constexpr int kLargeTopk = 512;     // larger selections use the wider unions below
+constexpr int kUnionCapM = 8192;    // larger selections, rows of up to kUnionMChunks chunks
+constexpr int kUnionCapL = 16384;   // larger selections, longer rows (tail in its own kernel)
+constexpr int kUnionMChunks = 256;
 constexpr int kSelCap = 4096;       // survivors gathered into LDS for the final select
 constexpr int kMaxIdxHeads = 8;
 constexpr int kMaxJw = 16;
 constexpr int kMaxJwL = 32;         // per-wave tops of a large selection
 
 // Per-wave top count: each wave of each chunk publishes its jw best
-// (key, id) pairs: the largest power of two that fits the union (kUnionCap,
-// or kUnionCapL for selections of more than kLargeTopk), at most kMaxJw
-// (kMaxJwL).  Rows that take this path have at least 9 chunks (more than
-// kDirectCap candidates); the union then holds 4 * W * jw >= 576 pairs
-// (1152 for large selections), at least half its capacity from 64 chunks
-// (32 for large selections) on.  A union smaller than top_k gives no bound:
-// such rows select exactly over every key.  A larger jw makes a wave whose
-// jw-th key still reaches the bound (a "saturated" wave, rescanned in full)
-// rarer.
-__host__ __device__ inline bool large_topk(int top_k) { return top_k > kLargeTopk; }
-__host__ __device__ inline int union_cap(int top_k) {
-  return large_topk(top_k) ? kUnionCapL : kUnionCap;
+// (key, id) pairs: the largest power of two that fits the call's union
+// capacity ucap, at most kMaxJw (kMaxJwL for the wider unions).  The union
+// is kUnionCap for selections of at most kLargeTopk blocks; larger ones
+// take kUnionCapM, or kUnionCapL when the longest row has more than
+// kUnionMChunks chunks.  Rows that take this path have at least 9 chunks
+// (more than kDirectCap candidates); the union then holds 4 * W * jw >= 576
+// pairs (1152 for the wider unions), at least half its capacity from
+// ucap / 64 chunks on.  A union smaller than top_k gives no bound: such rows
+// select exactly over every key.  A larger jw makes a wave whose jw-th key
+// still reaches the bound (a "saturated" wave, rescanned in full) rarer.
+__host__ __device__ inline int union_cap(int top_k, int w_max) {
+  if (top_k <= kLargeTopk) return kUnionCap;
+  return w_max <= kUnionMChunks ? kUnionCapM : kUnionCapL;
 }
-__host__ __device__ inline int row_jw(int n, int top_k) {
+__host__ __device__ inline int row_jw(int n, int ucap) {
   int W = (n + kChunk - 1) / kChunk;
   if (W <= 0) return 1;
-  const int cap = union_cap(top_k) / (4 * W);
-  const int jmax = large_topk(top_k) ? kMaxJwL : kMaxJw;
+  const int cap = ucap / (4 * W);
+  const int jmax = ucap == kUnionCap ? kMaxJw : kMaxJwL;
   int jw = 1;
   while (jw * 2 <= cap && jw * 2 <= jmax) jw *= 2;  // a power of two
   return jw;
@@ -84,7 +87,8 @@ struct TopkArgs {
   float* ws_scores;      // [R][ws_ld]
   int64_t ws_ld;
   uint32_t* cnt;         // [R] arrival counters
-  uint64_t* tops;        // [R][union_cap(top_k)] (block id << 32 | key)
+  int ucap;              // union capacity per row (union_cap)
+  uint64_t* tops;        // [R][ucap] (block id << 32 | key)
 };
 
 // ---- MFMA prefill indexer (index_mfma.hip)

@@ -116,6 +116,10 @@ WORKLOADS = {
         name="prefill_8k_at_128k_tok", mode="prefill", dtype="bf16", n_seqs=1,
         n_ctx=131072, n_new=8192, hq=16, hkv=2, d=128, hi=4, di=64,
         top_k=2048, n_needles=16, seed=1004, block=1),
+    "decode_1m_tok": Workload(
+        name="decode_1m_tok", mode="decode", dtype="bf16", n_seqs=1,
+        n_ctx=1048576, n_new=1, hq=16, hkv=2, d=128, hi=4, di=64, top_k=2048,
+        needle_depths=(0.0, 0.25, 0.5, 0.75, 0.99), seed=1003, block=1),
     "decode_8x32k_tok": Workload(
         name="decode_8x32k_tok", mode="decode", dtype="bf16", n_seqs=8,
         n_ctx=32768, n_new=1, hq=16, hkv=2, d=128, hi=4, di=64, top_k=2048,

@@ -140,7 +140,7 @@ def test_attention_decode_shared_block_sizes(gpu, block):
         assert err <= TOL[wl.dtype], f"row {i} t={pos[i]} (selection at {pos[s_]}) err={err}"
 
 
-@pytest.mark.parametrize("name", ["decode_8x32k_tok"])
+@pytest.mark.parametrize("name", ["decode_8x32k_tok", "decode_1m_tok"])
 def test_e2e_token_granular_workload(gpu, name):
     """The token-granular benchmark workload itself: every token of every
     planted needle span is selected."""

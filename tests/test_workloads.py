@@ -115,7 +115,8 @@ def test_generation_is_seeded():
 
 
 @pytest.mark.parametrize("tok,blk", [("prefill_8k_at_128k_tok", "prefill_8k_at_128k"),
-                                     ("decode_8x32k_tok", "decode_8x32k")])
+                                     ("decode_8x32k_tok", "decode_8x32k"),
+                                     ("decode_1m_tok", "decode_1m")])
 def test_token_granular_workloads_share_inputs(tok, blk):
     """The token-granular workloads draw the same inputs as the block
     workloads they are named after; only the block size (1) and the budget
