@@ -8,9 +8,9 @@
 // nearest-even), organised for many rows: a workgroup (8 waves) owns 256
 // query vectors -- (row, head) pairs of one KV head, G = Hq/Hkv heads per
 // row, so 256/G consecutive rows -- and walks the KV tokens 64 at a time.
-// Each 64-token tile of K (row-major) and V (transposed, dims x tokens) is
-// staged in LDS once for all 256 vectors, double-buffered: the next tile's
-// global loads are in flight while the current tile is computed.
+// Each 64-token tile of K and V (both row-major) is staged in LDS once for
+// all 256 vectors, double-buffered: the next tile's global loads are in
+// flight while the current tile is computed.
 //
 // Per wave: 32 query vectors (two 16-column groups).
 //   S^T[64 tok x 16 vec] = K[64 x D] . Q^T       v_mfma_f32_16x16x32_bf16
@@ -18,9 +18,11 @@
 //   O^T[D x 16 vec] += V^T[D x 64 tok] . P^T     v_mfma_f32_16x16x32_bf16
 //     B = the softmax numerators in the registers where S^T left them (the
 //     32 contraction slots of lane group g are tokens 4g..4g+3 of two
-//     16-token tiles, and V^T is read in that order)
-// Online softmax in log2 units; the sum of numerators is kept per lane
-// (four partial sums per column) and combined at the end.
+//     16-token tiles); A = V^T in that order, read from the row-major V
+//     tile with the gfx950 transposing LDS read ds_read_b64_tr_b16
+// Online softmax in log2 units; the sum of the numerators is one more
+// product on the matrix core (a ones operand against the same bf16
+// numerators the O^T product uses).
 #include <type_traits>
 
 #include "attention.hpp"
@@ -33,6 +35,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kFTok = 64;                     // KV tokens per tile
 constexpr int kFNC = 2;                       // 16-vector column groups per wave
@@ -60,9 +64,11 @@ struct FGeom {
   static constexpr int KS = D / 32;               // k steps of Q.K
   static constexpr int NDT = D / 16;              // 16-dim tiles of the output
   static constexpr int KPITCH = D * 2 + 16;       // bytes per staged K row
-  static constexpr int VPITCH = kFTok * 2 + 8;    // bytes per staged V^T row (one dim)
+  // bytes per staged V row: 32 more than the row, so that the four rows one
+  // lane group reads in a transposing load start 8 banks apart
+  static constexpr int VPITCH = D * 2 + 32;
   static constexpr int KBYTES = kFTok * KPITCH;
-  static constexpr int BUF = KBYTES + D * VPITCH; // one stage (K then V^T)
+  static constexpr int BUF = KBYTES + kFTok * VPITCH;  // one stage (K then V)
   static constexpr int CPR = D / 8;               // 16-byte chunks per token row
   static constexpr int CPT = kFTok * CPR / kFThreads;  // chunks per thread per tensor
 };
@@ -147,72 +153,65 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
       for (int s = 0; s < Gm::KS; ++s)
         qf[c][s] = act ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    float m[kFNC], lp[kFNC];
-    f32x4_t acc[kFNC][Gm::NDT];
+    float m[kFNC];
+    f32x4_t acc[kFNC][Gm::NDT], lacc[kFNC];
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
 #pragma unroll
     for (int c = 0; c < kFNC; ++c) {
       m[c] = -INFINITY;
-      lp[c] = 0.0f;
+      lacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int n = 0; n < Gm::NDT; ++n) acc[c][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // staging.  K: chunk ch = threadIdx.x + kFThreads i -> token ch / CPR,
-    // dims 8 (ch % CPR) .. (a wave reads whole rows).  V: lane l of wave w
-    // -> token l, dims 8 (w + 8 i) .. , so that the transposed LDS writes of
-    // a wave go to 64 consecutive tokens of one dim row (no bank conflicts).
+    // staging, K and V alike: chunk ch = threadIdx.x + kFThreads i -> token
+    // ch / CPR, dims 8 (ch % CPR) .. (16 lanes read one whole row).
     // A tile's token rows come from one page lookup when pages hold whole
-    // tiles, else one per token.
+    // tiles, else one per token.  Tokens past kv_end read the last token's
+    // row instead (they are masked), so every load is unconditional and a
+    // tile's loads are all in flight together.
     const bool page_tiles = a.pm.page_shift >= 6;
     u32x4_t pk[Gm::CPT], pv[Gm::CPT];
     auto fetch = [&](int t) {
       const int j0 = t * kFTok;
-      const int64_t base = page_tiles ? a.pm.token_slot(seq, j0) : 0;
-      auto slot_of = [&](int j) {
-        return page_tiles ? base + (j - j0) : a.pm.token_slot(seq, j);
-      };
+      const int jl = kv_end - 1 - j0;  // last tile token with data
+      int64_t off[Gm::CPT];            // element offsets of the thread's rows
+      if (page_tiles) {
+        const int64_t base = a.pm.token_slot(seq, j0);
 #pragma unroll
-      for (int i = 0; i < Gm::CPT; ++i) {
-        const int ch = threadIdx.x + kFThreads * i;
-        const int j = j0 + ch / Gm::CPR, part = ch % Gm::CPR;
-        pk[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (j < kv_end) pk[i] = *reinterpret_cast<const u32x4_t*>(kg + slot_of(j) * rstride + 8 * part);
+        for (int i = 0; i < Gm::CPT; ++i) {
+          const int ch = threadIdx.x + kFThreads * i;
+          off[i] = (base + min(ch / Gm::CPR, jl)) * rstride + 8 * (ch % Gm::CPR);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Gm::CPT; ++i) {
+          const int ch = threadIdx.x + kFThreads * i;
+          off[i] = a.pm.token_slot(seq, j0 + min(ch / Gm::CPR, jl)) * rstride + 8 * (ch % Gm::CPR);
+        }
       }
-      const int jv = j0 + l;
 #pragma unroll
       for (int i = 0; i < Gm::CPT; ++i) {
-        const int part = w + kFWaves * i;
-        pv[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (jv < kv_end) pv[i] = *reinterpret_cast<const u32x4_t*>(vg + slot_of(jv) * rstride + 8 * part);
+        pk[i] = *reinterpret_cast<const u32x4_t*>(kg + off[i]);
+        pv[i] = *reinterpret_cast<const u32x4_t*>(vg + off[i]);
       }
     };
     auto park = [&](unsigned char* buf) {
       unsigned char* ks = buf;
-      unsigned char* vt = buf + Gm::KBYTES;
+      unsigned char* vs = buf + Gm::KBYTES;
 #pragma unroll
       for (int i = 0; i < Gm::CPT; ++i) {
         const int ch = threadIdx.x + kFThreads * i;
         const int jt = ch / Gm::CPR, part = ch % Gm::CPR;
         *reinterpret_cast<u32x4_t*>(ks + jt * Gm::KPITCH + part * 16) = pk[i];
-      }
-      // adjacent lanes (tokens 2m, 2m+1) swap their rows and each writes
-      // 32-bit token pairs: the even lane for even dims, the odd lane for
-      // odd dims (byte permute of own and partner words)
-      const uint32_t psel = (l & 1) ? 0x03020706u : 0x05040100u;
-#pragma unroll
-      for (int i = 0; i < Gm::CPT; ++i) {
-        const int part = w + kFWaves * i;
-        const uint32_t own[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
-        unsigned char* col = vt + (8 * part + (l & 1)) * Gm::VPITCH + (l & ~1) * 2;
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-          const uint32_t partner =
-              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own[k2], 0xB1, 0xF, 0xF, false);
-          *reinterpret_cast<uint32_t*>(col + 2 * k2 * Gm::VPITCH) =
-              __builtin_amdgcn_perm(partner, own[k2], psel);
-        }
+        *reinterpret_cast<u32x4_t*>(vs + jt * Gm::VPITCH + part * 16) = pv[i];
       }
     };
+    // transposing read of V^T: the lane supplies the address of tile token
+    // 4g + c16/4 (plus 32 kk, plus 16 for the upper half), dims
+    // 16n + 4(c16 % 4) .. +4; lane (g, c16) receives V[4g + j][16n + c16],
+    // j = 0..3
+    const uint32_t tr_off = (4 * g + c16 / 4) * Gm::VPITCH + 8 * (c16 % 4);
 
     const int n_tiles = (kv_end + kFTok - 1) / kFTok;
     fetch(0);
@@ -222,7 +221,7 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
       unsigned char* buf = smem + (t & 1) * Gm::BUF;
       if (t + 1 < n_tiles) fetch(t + 1);
       const unsigned char* ks = buf;
-      const unsigned char* vt = buf + Gm::KBYTES;
+      const unsigned char* vs = buf + Gm::KBYTES;
       // S^T: 4 token tiles x kFNC column groups
       f32x4_t sc[kFNC][4];
 #pragma unroll
@@ -262,8 +261,18 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mr = fmaxf(mr, masked(tt, i) ? -INFINITY : sc[c][tt][i]);
-          mr = fmaxf(mr, __shfl_xor(mr, 16));
-          mr = fmaxf(mr, __shfl_xor(mr, 32));
+          // the column's maximum over the four lane groups (rows 16 apart,
+          // then 32 apart) with lane swaps instead of LDS permutes
+          {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mr),
+                                                            __float_as_uint(mr), false, false);
+            mr = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          }
+          {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mr),
+                                                            __float_as_uint(mr), false, false);
+            mr = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+          }
           const float mx = mr * sl2;
           const bool grow = mx > m[c] + kSlack;
           const float m_new = grow ? mx : m[c];
@@ -273,7 +282,6 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
           m[c] = m_new;
           // (without masking some score is finite, so m_new is)
           const bool none = MASK && m_new == -INFINITY;
-          float ps = 0.0f;
           uint32_t pw[8];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
@@ -285,10 +293,8 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
                 p0 = (none || masked(tt, i)) ? 0.0f : p0;
                 p1 = (none || masked(tt, i + 1)) ? 0.0f : p1;
               }
-              ps += p0 + p1;
               pw[2 * tt + i / 2] = pack_bf16x2(p0, p1);
             }
-          lp[c] = lp[c] * corr[c] + ps;
           // k-slots of step kk: tokens 32kk + 4g + 0..3, then 32kk + 16 + 4g + 0..3
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
@@ -301,23 +307,32 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
         softmax(std::false_type{});
       if (__ballot(rescale) != 0ull) {
 #pragma unroll
-        for (int c = 0; c < kFNC; ++c)
+        for (int c = 0; c < kFNC; ++c) {
+          lacc[c] = lacc[c] * corr[c];
 #pragma unroll
           for (int n = 0; n < Gm::NDT; ++n) acc[c][n] = acc[c][n] * corr[c];
+        }
       }
       // O^T += V^T . P^T
 #pragma unroll
       for (int n = 0; n < Gm::NDT; ++n) {
-        const unsigned char* vrow = vt + (16 * n + c16) * Gm::VPITCH;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * kk + 4 * g) * 2);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * kk + 16 + 4 * g) * 2);
+          const unsigned char* vp = vs + tr_off + 32 * kk * Gm::VPITCH + 32 * n;
+          const u32x2_t lo = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp));
+          const u32x2_t hi = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * Gm::VPITCH)));
           const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int c = 0; c < kFNC; ++c) acc[c][n] = mfma(va, pb[c][kk], acc[c][n]);
         }
       }
+      // column sums of the numerators (every row of the product holds them)
+#pragma unroll
+      for (int c = 0; c < kFNC; ++c)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) lacc[c] = mfma(ones, pb[c][kk], lacc[c]);
       if (t + 1 < n_tiles) park(smem + ((t + 1) & 1) * Gm::BUF);
       __syncthreads();
     }
@@ -325,9 +340,7 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
     // normalise and write: lane holds dims 16n + 4g + i of its column
 #pragma unroll
     for (int c = 0; c < kFNC; ++c) {
-      float L = lp[c];
-      L += __shfl_xor(L, 16);
-      L += __shfl_xor(L, 32);
+      const float L = lacc[c][0];
       if (cpos[c] < 0) continue;
       const int v = w * (kFNC * 16) + c * 16 + c16;
       const int ri = v / G, hh = v % G;
