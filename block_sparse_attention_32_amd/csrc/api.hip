@@ -84,7 +84,7 @@ struct TopkPlan {
 // MFMA prefill indexer plan (fused mode, many rows)
 struct PidxPlan {
   int rows, splits;
-  size_t off_uni, off_tau, off_tstride, off_rstride, off_surv, off_scnt, total;
+  size_t off_uni, off_tau, off_tstride, off_rstride, off_surv, off_scnt, off_done, total;
 };
 
 PidxPlan pidx_plan(const qsa_queries* qm) {
@@ -102,6 +102,7 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
   p.off_rstride = o; o = align256(o + (size_t)p.rows * 4);
   p.off_surv = o;    o = align256(o + (size_t)p.rows * kPSurvCap * 8);
   p.off_scnt = o;    o = align256(o + (size_t)p.rows * p.splits * 4);
+  p.off_done = o;    o = align256(o + (size_t)p.rows * 4);
   p.total = o;
   return p;
 }
@@ -342,6 +343,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
     a.row_stride = reinterpret_cast<int32_t*>(base + pp.off_rstride);
     a.surv = reinterpret_cast<uint64_t*>(base + pp.off_surv);
     a.surv_cnt = reinterpret_cast<uint32_t*>(base + pp.off_scnt);
+    a.done = reinterpret_cast<uint32_t*>(base + pp.off_done);
     a.sel = sel;
     a.n_sel = n_sel;
     for (int r0 = 0; r0 < qm->n_rows; r0 += pp.rows) {

@@ -102,6 +102,7 @@ constexpr int kPMaxStride = 8;    // largest group sampling stride of P1
 constexpr int kPMaxSplits = 16;   // block splits per tile
 constexpr int kPMinRows = 64;     // fused top-k of at least this many rows uses it
 constexpr int kPRowBatch = 32768; // rows per launch
+constexpr int kPWave = 16;        // survivors per lane of the one-wave select (1,024 per row)
 
 struct PIdxArgs {
   IdxArgs idx;
@@ -113,6 +114,7 @@ struct PIdxArgs {
   int32_t* row_stride;       // [rows] stride used for each row's union
   uint64_t* surv;            // [rows][splits][kPSurvCap / splits] (block << 32 | score bits)
   uint32_t* surv_cnt;        // [rows][splits]
+  uint32_t* done;            // [rows] set by the one-wave select, cleared by the fallback
   int32_t* sel;
   int32_t* n_sel;
 };

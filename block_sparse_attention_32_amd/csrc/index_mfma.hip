@@ -377,12 +377,121 @@ struct PRecomputed {
 struct IdSelf {
   __device__ __forceinline__ int32_t operator()(int e) const { return e; }
 };
-// P4: gather, exact select, ordered emission.
+// Sum over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v), kWave - 1);
+}
+
+// P4 for the common case, one wave per row: rows whose survivors fit
+// kPWave per lane (and are at least top_k, none lost to a full region).
+// Survivor jj of the row (splits in order, each in block order) is held by
+// lane jj % 64 as its element jj / 64; the k-th largest key is found bit by
+// bit (a count over the wave per bit, no barriers), then the keys above it
+// and the first of the keys equal to it, in block order, are written in
+// order.  Rows it does not take are left to pidx_select_kernel (done = 0).
+__global__ void __launch_bounds__(256) pidx_select_wave_kernel(PIdxArgs a) {
+  const int wv = threadIdx.x / kWave, l = lane_id();
+  const int rl = blockIdx.x * (256 / kWave) + wv;
+  if (rl >= a.rows) return;  // whole waves
+  const int row = a.row0 + rl;
+  const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
+  int32_t* sel_row = a.sel + (int64_t)row * a.top_k;
+  if (n <= a.top_k) {
+    for (int j = l; j < a.top_k; j += kWave) sel_row[j] = j < n ? j : -1;
+    if (l == 0) {
+      a.n_sel[row] = n;
+      a.done[rl] = 1u;
+    }
+    return;
+  }
+  // survivor counts of the splits (lane s: split s) -> offsets
+  const int region = kPSurvCap / a.splits;
+  const uint32_t c = l < a.splits ? a.surv_cnt[(int64_t)rl * a.splits + l] : 0u;
+  const uint32_t incl = wave_incl_scan_dpp(c);
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  if (ballot(c > (uint32_t)region) != 0ull || m > (uint32_t)(kWave * kPWave) ||
+      m < (uint32_t)a.top_k)
+    return;  // the fallback kernel takes the row
+  // survivor jj lives at slot jj + sum over splits s >= 1 with jj >= offs[s]
+  // of (region - count[s - 1]) of the row's regions
+  uint32_t so[kPMaxSplits], dl[kPMaxSplits];
+#pragma unroll
+  for (int sp = 1; sp < kPMaxSplits; ++sp) {
+    const int q = sp < a.splits ? sp : 0;
+    so[sp] = sp < a.splits ? (uint32_t)__builtin_amdgcn_readlane((int)(incl - c), q) : 0xffffffffu;
+    dl[sp] = (uint32_t)region - (uint32_t)__builtin_amdgcn_readlane((int)c, sp - 1);
+  }
+  const uint64_t* rs = a.surv + (int64_t)rl * a.splits * region;
+  uint32_t key[kPWave];
+  int32_t id[kPWave];
+#pragma unroll
+  for (int i = 0; i < kPWave; ++i) {
+    const uint32_t jj = (uint32_t)(i * kWave + l);
+    const bool ok = jj < m;
+    uint32_t slot = jj;
+#pragma unroll
+    for (int sp = 1; sp < kPMaxSplits; ++sp) slot += jj >= so[sp] ? dl[sp] : 0u;
+    const uint64_t v = ok ? rs[slot] : 0ull;
+    key[i] = ok ? ordered_key(__uint_as_float((uint32_t)v)) : 0u;
+    id[i] = ok ? (int32_t)(v >> 32) : 0;
+  }
+  // the k-th largest key T, and how many keys equal to T are taken
+  uint32_t mx = 0u, nmn = 0u;
+#pragma unroll
+  for (int i = 0; i < kPWave; ++i) {
+    if (key[i] != 0u) {
+      mx = max(mx, key[i]);
+      nmn = max(nmn, ~key[i]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  const uint32_t mn = ~wave_max_u32(nmn);
+  uint32_t T = mx, kk = (uint32_t)a.top_k;
+  if (mx != mn) {
+    const int hi = 31 - __clz(mx ^ mn);  // highest bit where the keys differ
+    T = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
+    for (int bit = hi; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      const uint32_t msk = ~((1u << bit) - 1u);  // the bits at and above `bit`
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kPWave; ++i) cnt += (key[i] & msk) == cand ? 1u : 0u;
+      cnt = wave_sum_u32(cnt);
+      if (cnt >= kk) T = cand; else kk -= cnt;
+    }
+  }
+  // in survivor order: keys above T, and the first kk keys equal to T
+  uint32_t eq_before = 0, taken = 0;
+#pragma unroll
+  for (int i = 0; i < kPWave; ++i) {
+    const uint64_t me = ballot(key[i] == T);
+    const bool tk = key[i] > T || (key[i] == T && eq_before + lanes_below(me) < kk);
+    const uint64_t mt = ballot(tk);
+    if (tk) sel_row[taken + lanes_below(mt)] = id[i];
+    eq_before += (uint32_t)__popcll(me);
+    taken += (uint32_t)__popcll(mt);
+  }
+  if (l == 0) {
+    a.n_sel[row] = a.top_k;
+    a.done[rl] = 1u;
+  }
+}
+
+// P4: gather, exact select, ordered emission (the rows the one-wave select
+// left: more survivors than it holds, a full region, or fewer than k).
 template <int DI>
 __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
   __shared__ uint32_t offs[kPMaxSplits + 1];
   __shared__ SelShared sh;
   const int rl = blockIdx.x, row = a.row0 + rl;
+  {
+    const bool done = a.done[rl] != 0u;
+    __syncthreads();
+    if (done) {
+      if (threadIdx.x == 0) a.done[rl] = 0u;  // cleared for the next call
+      return;
+    }
+  }
   const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
   int32_t* sel_row = a.sel + (int64_t)row * a.top_k;
   if (n <= a.top_k) {
@@ -461,16 +570,19 @@ bool pidx_supported(int dtype, int di, int hi) {
 void run_pidx(const PIdxArgs& a, int di, hipStream_t st) {
   const int tiles = (a.rows + kPQT - 1) / kPQT;
   dim3 grid((unsigned)a.splits, (unsigned)tiles);
+  const dim3 wave_grid((unsigned)((a.rows + 3) / 4));  // four rows (waves) per workgroup
   hipLaunchKernelGGL(pidx_stride_kernel, dim3(tiles), dim3(256), 0, st, a);
   if (di == 64) {
     hipLaunchKernelGGL((pidx_kernel<64, false>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<64>), dim3(a.rows), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<128>), dim3(a.rows), dim3(256), 0, st, a);
   }
 }
