@@ -364,6 +364,7 @@ __device__ __noinline__ void select_full(Get get, int n, int top_k, int32_t* sel
 // ascending id order, and the exact radix select + ordered emission of
 // select.hpp picks the k best with ties to the lower id.
 constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
+constexpr int kWaveSel = 16;  // survivors per lane of the one-wave final select (1,024)
 
 // LDS of the tail of a long row.
 struct LongShared {
@@ -427,18 +428,21 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
   __syncthreads();
   const int ns = (int)ls.n_sat;
   bool fits = ns <= kMaxSat;
-  // survivor counts of saturated runs (whole workgroup, one run at a time)
+  // survivor counts of saturated runs (a run is one scoring wave's 256
+  // candidates; wave w of this workgroup counts runs w, w + 4, ..., its
+  // lanes reading 4 keys each, with no workgroup barrier per run)
 #pragma unroll 1
-  for (int i = 0; fits && i < ns; ++i) {
-    const int e = ls.sat_w[i] * 256 + (int)threadIdx.x;
-    const bool hit = e < n && src(e) >= tau;
-    const uint32_t cw = (uint32_t)__popcll(ballot(hit));
-    if (lane == 0) sh.wcnt[1][wave] = cw;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      ls.sat_cnt[i] = sh.wcnt[1][0] + sh.wcnt[1][1] + sh.wcnt[1][2] + sh.wcnt[1][3];
-    __syncthreads();
+  for (int i = wave; fits && i < ns; i += kSelWaves) {
+    const int e0 = ls.sat_w[i] * 256 + lane;
+    uint32_t cw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 64 * j;
+      cw += (uint32_t)__popcll(ballot(e < n && src(e) >= tau));
+    }
+    if (lane == 0) ls.sat_cnt[i] = cw;
   }
+  __syncthreads();
   // survivors of the unsaturated runs placed, saturated runs' places reserved
   uint32_t cnt[R], mine = 0;
 #pragma unroll
@@ -477,27 +481,44 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
     }
   }
   __syncthreads();
-  // survivors of saturated runs, in id order (whole workgroup per run)
+  // survivors of saturated runs, in id order (wave w places runs w, w + 4,
+  // ...; a run's ids ascend with 64 j + lane)
 #pragma unroll 1
-  for (int i = 0; fits && i < ns; ++i) {
-    const int e = ls.sat_w[i] * 256 + (int)threadIdx.x;
-    const uint32_t kk = e < n ? src(e) : 0u;
-    const bool hit = e < n && kk >= tau;
-    const uint64_t m = ballot(hit);
-    if (lane == 0) sh.wcnt[1][wave] = (uint32_t)__popcll(m);
-    __syncthreads();
+  for (int i = wave; fits && i < ns; i += kSelWaves) {
+    const int e0 = ls.sat_w[i] * 256 + lane;
     uint32_t base = ls.sat_off[i];
-    for (int w2 = 0; w2 < wave; ++w2) base += sh.wcnt[1][w2];
-    if (hit) {
-      ls.skey[base + lanes_below(m)] = kk;
-      ls.sid[base + lanes_below(m)] = e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 64 * j;
+      const uint32_t kk = e < n ? src(e) : 0u;
+      const bool hit = e < n && kk >= tau;
+      const uint64_t m = ballot(hit);
+      if (hit) {
+        ls.skey[base + lanes_below(m)] = kk;
+        ls.sid[base + lanes_below(m)] = e;
+      }
+      base += (uint32_t)__popcll(m);
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (fits && m_total == (uint32_t)top_k) {
     // exactly k survivors: all of them, already in id order
     for (int j = threadIdx.x; j < top_k; j += kSelThreads) sel_row[j] = ls.sid[j];
     if (threadIdx.x == 0) n_sel[row] = top_k;
+  } else if (fits && m_total <= (uint32_t)(kWave * kWaveSel)) {
+    // few survivors: one wave selects them (element jj at lane jj % 64)
+    if (wave == 0) {
+      uint32_t key[kWaveSel];
+      int32_t sid[kWaveSel];
+#pragma unroll
+      for (int i = 0; i < kWaveSel; ++i) {
+        const uint32_t jj = (uint32_t)(i * kWave + lane);
+        key[i] = jj < m_total ? ls.skey[jj] : 0u;
+        sid[i] = jj < m_total ? ls.sid[jj] : 0;
+      }
+      wave_topk_ordered<kWaveSel>(key, sid, top_k, sel_row);
+      if (lane == 0) n_sel[row] = top_k;
+    }
   } else if (fits) {
     uint32_t thr;
     int r;

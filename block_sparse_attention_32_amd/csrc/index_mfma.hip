@@ -377,18 +377,11 @@ struct PRecomputed {
 struct IdSelf {
   __device__ __forceinline__ int32_t operator()(int e) const { return e; }
 };
-// Sum over the wave, in every lane.
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v), kWave - 1);
-}
-
 // P4 for the common case, one wave per row: rows whose survivors fit
 // kPWave per lane (and are at least top_k, none lost to a full region).
 // Survivor jj of the row (splits in order, each in block order) is held by
-// lane jj % 64 as its element jj / 64; the k-th largest key is found bit by
-// bit (a count over the wave per bit, no barriers), then the keys above it
-// and the first of the keys equal to it, in block order, are written in
-// order.  Rows it does not take are left to pidx_select_kernel (done = 0).
+// lane jj % 64 as its element jj / 64 (wave_topk_ordered).  Rows it does
+// not take are left to pidx_select_kernel (done = 0).
 __global__ void __launch_bounds__(256) pidx_select_wave_kernel(PIdxArgs a) {
   const int wv = threadIdx.x / kWave, l = lane_id();
   const int rl = blockIdx.x * (256 / kWave) + wv;
@@ -435,42 +428,7 @@ __global__ void __launch_bounds__(256) pidx_select_wave_kernel(PIdxArgs a) {
     key[i] = ok ? ordered_key(__uint_as_float((uint32_t)v)) : 0u;
     id[i] = ok ? (int32_t)(v >> 32) : 0;
   }
-  // the k-th largest key T, and how many keys equal to T are taken
-  uint32_t mx = 0u, nmn = 0u;
-#pragma unroll
-  for (int i = 0; i < kPWave; ++i) {
-    if (key[i] != 0u) {
-      mx = max(mx, key[i]);
-      nmn = max(nmn, ~key[i]);
-    }
-  }
-  mx = wave_max_u32(mx);
-  const uint32_t mn = ~wave_max_u32(nmn);
-  uint32_t T = mx, kk = (uint32_t)a.top_k;
-  if (mx != mn) {
-    const int hi = 31 - __clz(mx ^ mn);  // highest bit where the keys differ
-    T = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
-    for (int bit = hi; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      const uint32_t msk = ~((1u << bit) - 1u);  // the bits at and above `bit`
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kPWave; ++i) cnt += (key[i] & msk) == cand ? 1u : 0u;
-      cnt = wave_sum_u32(cnt);
-      if (cnt >= kk) T = cand; else kk -= cnt;
-    }
-  }
-  // in survivor order: keys above T, and the first kk keys equal to T
-  uint32_t eq_before = 0, taken = 0;
-#pragma unroll
-  for (int i = 0; i < kPWave; ++i) {
-    const uint64_t me = ballot(key[i] == T);
-    const bool tk = key[i] > T || (key[i] == T && eq_before + lanes_below(me) < kk);
-    const uint64_t mt = ballot(tk);
-    if (tk) sel_row[taken + lanes_below(mt)] = id[i];
-    eq_before += (uint32_t)__popcll(me);
-    taken += (uint32_t)__popcll(mt);
-  }
+  wave_topk_ordered<kPWave>(key, id, a.top_k, sel_row);
   if (l == 0) {
     a.n_sel[row] = a.top_k;
     a.done[rl] = 1u;

@@ -50,6 +50,58 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
   return v;
 }
 
+// Sum over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(v), kWave - 1);
+}
+
+// Exact top-k of at most 64 * EPW keys held by one wave, element jj at lane
+// jj % 64, slot jj / 64 (key 0 = no element; real keys are >= 1), elements
+// in ascending id order by jj.  The k-th largest key T is found bit by bit
+// (a count over the wave per bit, no barriers); then the keys above T and
+// the first of the keys equal to T, in element order, are written to out in
+// element order (k ids; at least k elements must be present).
+template <int EPW>
+__device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
+                                                  const int32_t (&id)[EPW], int k,
+                                                  int32_t* out) {
+  uint32_t mx = 0u, nmn = 0u;
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) {
+    if (key[i] != 0u) {
+      mx = max(mx, key[i]);
+      nmn = max(nmn, ~key[i]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  const uint32_t mn = ~wave_max_u32(nmn);
+  uint32_t T = mx, kk = (uint32_t)k;
+  if (mx != mn) {
+    const int hi = 31 - __clz(mx ^ mn);  // highest bit where the keys differ
+    T = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
+    for (int bit = hi; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      const uint32_t msk = ~((1u << bit) - 1u);  // the bits at and above `bit`
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) cnt += (key[i] & msk) == cand ? 1u : 0u;
+      cnt = wave_sum_u32(cnt);
+      if (cnt >= kk) T = cand; else kk -= cnt;
+    }
+  }
+  // in element order: keys above T, and the first kk keys equal to T
+  uint32_t eq_before = 0, taken = 0;
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) {
+    const uint64_t me = __ballot(key[i] == T);
+    const bool tk = key[i] > T || (key[i] == T && eq_before + lanes_below(me) < kk);
+    const uint64_t mt = __ballot(tk);
+    if (tk) out[taken + lanes_below(mt)] = id[i];
+    eq_before += (uint32_t)__popcll(me);
+    taken += (uint32_t)__popcll(mt);
+  }
+}
+
 // Inclusive prefix sum of one value per thread over the workgroup (one
 // barrier pair).  total receives the workgroup sum.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, SelShared& sh, uint32_t& total) {
