@@ -102,9 +102,8 @@ namespace qsa {
 // MFMA path (bfloat16, head_dim 64 or 128, up to 16 query heads per KV
 // head, 1, 2 or 4 KV heads): tile geometry.
 constexpr int kMfmaTileTok = 16;    // tokens per wave tile
-constexpr int kMfmaTileEnt = 4;     // token-list entries (blocks) per tile
-constexpr int kMfmaSplitEnt = 16;   // entries per split and KV head (split-K decode)
-constexpr int kMfmaEntChunk = 512;  // entries staged in LDS per pass
+constexpr int kMfmaSplitEnt = 16;   // 4-token units per split and KV head (split-K decode)
+constexpr int kMfmaListTok = 2048;  // list tokens staged in LDS per pass
 
 bool attn_mfma_supported(int dtype, int hq, int hkv, int d);
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st);

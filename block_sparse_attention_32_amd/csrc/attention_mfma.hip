@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   // p / 16, i = (p % 16) / 4, j = p % 4, kept as [j][i]; each value is the
   // byte offset of the token's row in the K and V arrays (WIDE: its row
   // index).  Tokens not to attend point at the row's own first token.
-  __shared__ __align__(16) uint32_t trow[kMfmaEntChunk * 4];
+  __shared__ __align__(16) uint32_t trow[kMfmaListTok];
   __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
   __shared__ int wcnt[NW];
   __shared__ uint32_t flag;
@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int e_end = min(n_entries, e_beg + a.eps);
   const int bs = a.pm.blk_shift, nb = 1 << bs;  // tokens per block
   const int tail = (t & (nb - 1)) + 1;        // tokens of the own block
-  const int epp = (kMfmaEntChunk * 4) >> bs;  // entries staged per pass
+  const int epp = kMfmaListTok >> bs;  // entries staged per pass
 
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + hk * D * 2;
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + hk * D * 2;
