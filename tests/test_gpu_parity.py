@@ -677,3 +677,17 @@ def test_determinism_and_poison(gpu):
     a.run()
     torch.cuda.synchronize()
     assert torch.equal(sel1, a.sel) and torch.equal(out1, a.out)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_e2e_sharp_softmax(gpu, mode):
+    """Queries scaled by 4 make the softmax sharp, so a wrong token in (or
+    out of) the attended set moves the output far beyond the tolerance:
+    the output check then also checks the selection's use."""
+    _say(f"e2e sharp softmax {mode}")
+    pos = MIXED_POS if mode == "decode" else sorted(MIXED_POS * 4)
+    pb = Problem(MIXED.replace(mode=mode), gpu, [0] * len(pos), pos)
+    pb.qs.q.mul_(4.0)
+    pb.pool_all()
+    _, worst = _e2e(pb)
+    _say(f"  max err {worst:.3g}")

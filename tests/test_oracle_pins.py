@@ -529,3 +529,31 @@ def test_masked_bruteforce_block_sizes(block):
     mat = O.masked_attention(q, k, v, mask, 0.3)
     assert np.allclose(np.stack(rows), mat, rtol=0, atol=1e-12)
     assert np.allclose(mat, _sdpa(q, k, v, mask, 0.3), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- properties
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None)
+@given(L=st.integers(1, 80), block=st.sampled_from([1, 2, 4, 8]), top_k=st.integers(1, 12),
+       seed=st.integers(0, 2 ** 16))
+def test_property_row_equals_masked_matrix_form(L, block, top_k, seed):
+    """On random tiny problems (context 1..80, every t mod block): the token
+    set is causal, holds the own block's tail and block * n_sel selected
+    tokens, and per-row attention equals the masked matrix form."""
+    rng = np.random.default_rng(seed)
+    k, v, kidx = _random_problem(rng, L)
+    kbar = O.pool_blocks(kidx, "f32", block=block)
+    t = int(rng.integers(0, L))
+    q = rng.standard_normal((1, 4, 8))
+    q_idx = np.round(rng.standard_normal((2, 8)) * 8) / 8
+    w = rng.integers(1, 17, 2) / 16
+    sel, out = O.qsa_row(k, v, kbar, q[0], q_idx, w, t, top_k, 0.3, block)
+    assert len(sel) == min(top_k, t // block)
+    toks = O.token_set(sel, t, block)
+    assert toks.max() == t and len(toks) == block * len(sel) + t % block + 1
+    mask = O.qsa_mask([sel], np.array([t]), L, block)
+    assert mask.sum() == len(toks) and not mask[0, t + 1:].any()
+    assert np.allclose(out[None], O.masked_attention(q, k, v, mask, 0.3), rtol=0, atol=1e-12)
