@@ -265,7 +265,7 @@ def run_prefill(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True
                  "bound": "hbm", "kernel": "attn_mfma_kernel",
                  "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
         "topk": {"flops": 2 * wl.hi * wl.di * cand, "bound": "mfma",
-                 "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_kernel",
+                 "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_wave_kernel+pidx_select_kernel",
                  "files": ("index_mfma.hip", "index.hpp", "select.hpp", "common.hpp")},
         "pool": {"bytes": (wl.n_new // bk) * (bk + 1) * wl.di * esz, "bound": "hbm",
                  "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
