@@ -80,7 +80,7 @@ extern "C" {
 typedef enum qsa_status {
   QSA_OK = 0,
   QSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
-  QSA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype this build lacks   */
+  QSA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype the library lacks */
   QSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
   QSA_ERR_HIP = -4          /* the HIP runtime reported an error           */
 } qsa_status;
