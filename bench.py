@@ -336,6 +336,44 @@ def memory_report(wl, ctx, dev):
 
 # ------------------------------------------------------------------ CPU oracle
 
+def measured_peaks(dev, reps=10):
+    """What this GPU achieves beside the published peaks: a plain 1 GiB
+    device-to-device copy (bytes read + written per second) and an
+    8192^3 bf16 GEMM (torch.matmul, i.e. the vendor BLAS).  Context for the
+    roofline fractions, which stay against the published peaks."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e-3 / reps
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    copy_gbs = 2 * src.numel() / t_copy / 1e9
+    del src, dst
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, b, out=c))
+    gemm_tflops = 2 * n ** 3 / t_mm / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(copy_gbs, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+            "how": "1 GiB device copy (read + write bytes) and an 8192^3 bf16 torch.matmul, "
+                   f"{reps} timed repetitions each (library kernels: lower bounds on what "
+                   "the chip sustains)"}
+
+
 def cpu_baseline(wl, ctx, budget_s=12.0):
     """The oracle (numpy float64, one thread) on a bounded sample of the same
     workload, scaled to query-tokens/s of the whole job."""
@@ -481,6 +519,8 @@ def main():
                          "next chunk's selection (per-kernel times then overlap)")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the mask-free vs materialised-kq_mask memory measurement")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable copy bandwidth and bf16 GEMM rate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -570,6 +610,19 @@ def main():
                             "how": ctx.get("dense_note", "")}
         if "dense_tflops" in ctx:
             out["dense_gqa"]["achieved_tflops"] = round(ctx["dense_tflops"], 1)
+    if not args.no_peaks:
+        mp = measured_peaks(dev)
+        out["measured_peaks"] = mp
+        meas = mp["hbm_copy_gbs"] if unit == "GB/s" else mp["bf16_gemm_tflops"]
+        roof["measured_peak"] = meas
+        roof["frac_of_measured_peak"] = round(achieved / meas, 4)
+        for key in ("indexer_mfma", "projection_mfma"):
+            if key in out:
+                out[key]["frac_of_measured_peak"] = round(
+                    out[key]["achieved_tflops"] / mp["bf16_gemm_tflops"], 4)
+        if "achieved_tflops" in out.get("dense_gqa", {}):
+            out["dense_gqa"]["frac_of_measured_peak"] = round(
+                out["dense_gqa"]["achieved_tflops"] / mp["bf16_gemm_tflops"], 4)
     if not args.no_memory and wl.mode != "project":
         out["memory"] = memory_report(wl, ctx, dev)
     out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ctx)
