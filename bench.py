@@ -190,6 +190,9 @@ def run_project(wl: W.Workload, steps: int, warmup: int, dev):
     return wall, kern, work, ctx
 
 
+STEP_MS: list = []  # per-step times (HIP events, per group of steps) after the timed region
+
+
 def _timed(one, steps, warmup):
     for _ in range(warmup):
         one()
@@ -199,6 +202,20 @@ def _timed(one, steps, warmup):
         one()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the spread of the step times, in a separate run: HIP events around
+    # groups of m steps (an event between microsecond steps slows them down
+    # by a few microseconds, so short steps are timed 20 at a time)
+    m = 20 if wall / steps < 1e-3 else 1
+    n = 10 if m > 1 else max(1, min(steps, 10))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        for _ in range(m):
+            one()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    global STEP_MS
+    STEP_MS = [ev[i].elapsed_time(ev[i + 1]) / m for i in range(n)]
     timer = Timer()
     for _ in range(max(1, min(steps, 50))):
         one(timer)
@@ -583,6 +600,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "step_ms": {"min": round(min(STEP_MS), 4), "median": round(float(np.median(STEP_MS)), 4),
+                    "max": round(max(STEP_MS), 4)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic", "config": cfg,
         "roofline": roof,
