@@ -537,7 +537,8 @@ def main():
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the mask-free vs materialised-kq_mask memory measurement")
     ap.add_argument("--no-peaks", action="store_true",
-                    help="skip measuring the achievable copy bandwidth and bf16 GEMM rate")
+                    help="skip measuring the achievable copy bandwidth and bf16 GEMM rate "
+                         "(also skipped with --copy-calibration)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -629,7 +630,8 @@ def main():
                             "how": ctx.get("dense_note", "")}
         if "dense_tflops" in ctx:
             out["dense_gqa"]["achieved_tflops"] = round(ctx["dense_tflops"], 1)
-    if not args.no_peaks:
+    # a counter run's only device copy must be the calibration copy
+    if not args.no_peaks and not args.copy_calibration:
         mp = measured_peaks(dev)
         out["measured_peaks"] = mp
         meas = mp["hbm_copy_gbs"] if unit == "GB/s" else mp["bf16_gemm_tflops"]
