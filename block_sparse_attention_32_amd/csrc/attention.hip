@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
   const int t = min(max(a.pos[row], 0), a.max_pos);
   // n_sel is clamped to [0, top_k]; selected ids the row may not attend are
   // skipped
-  const RowList rl(a, row, t, DENSE);
+  const RowList rl(a, row, t, DENSE, DENSE ? 0 : a.n_sel[row]);
   const int b_own = rl.b_own;
   const int n_entries = rl.e_own + 1;
   const int e_beg = split * a.eps;

@@ -45,18 +45,24 @@ constexpr int kMaxBridge = QSA_MAX_SHARED_LAG;
 // ids outside [0, b_sel) are skipped.
 struct RowList {
   int b_own, b_sel, n_list, n_bridge, e_own;
+  bool own_sel;  // the row's own selection (not another row's)
   const int32_t* sel;
-  __device__ __forceinline__ RowList(const AttnArgs& a, int row, int t, bool dense) {
+  // n_sel_row: n_sel[row] (the caller reads it beside the row's other
+  // values, so that the reads overlap)
+  __device__ __forceinline__ RowList(const AttnArgs& a, int row, int t, bool dense,
+                                     int n_sel_row) {
     const int bs = a.pm.blk_shift;
     b_own = t >> bs;
     int rs = row;
     b_sel = b_own;
+    n_list = dense ? b_own : min(max(n_sel_row, 0), a.top_k);
     if (!dense && a.sel_of != nullptr) {
       rs = min(max(a.sel_of[row], 0), a.n_rows - 1);
       const int ts = min(max(a.pos[rs], 0), a.max_pos);
       b_sel = max(min(ts >> bs, b_own), b_own - (((QSA_MAX_SHARED_LAG - 1) >> bs) + 1));
+      if (rs != row) n_list = min(max(a.n_sel[rs], 0), a.top_k);
     }
-    n_list = dense ? b_own : min(max(a.n_sel[rs], 0), a.top_k);
+    own_sel = rs == row;
     n_bridge = b_own - b_sel;
     e_own = n_list + n_bridge;
     sel = dense ? nullptr : a.sel + (int64_t)rs * a.top_k;

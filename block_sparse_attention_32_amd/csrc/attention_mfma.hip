@@ -190,12 +190,21 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int hk = w % hkv, wsub = w / hkv;
   const int row = blockIdx.y, split = blockIdx.x;
 
-  const int seq = min(max(a.seq_id[row], 0), a.n_seqs - 1);
-  const int t = min(max(a.pos[row], 0), a.max_pos);
-  const RowList rl(a, row, t, DENSE);
+  // the reads that depend on the row index alone, issued together so that
+  // their latencies overlap: sequence, position, selection length, and the
+  // first selected id this thread stages (a selection row always holds
+  // top_k entries; used only when the row attends its own selection)
+  const int e_beg = split * a.eps;
+  const int sid_raw = a.seq_id[row];
+  const int pos_raw = a.pos[row];
+  const int nsel_raw = DENSE ? 0 : a.n_sel[row];
+  const int32_t pre =
+      DENSE ? -1 : a.sel[(int64_t)row * a.top_k + min(e_beg + (int)threadIdx.x, a.top_k - 1)];
+  const int seq = min(max(sid_raw, 0), a.n_seqs - 1);
+  const int t = min(max(pos_raw, 0), a.max_pos);
+  const RowList rl(a, row, t, DENSE, nsel_raw);
   const int b_own = rl.b_own;
   const int n_entries = rl.e_own + 1;
-  const int e_beg = split * a.eps;
   const int e_end = min(n_entries, e_beg + a.eps);
   const int bs = a.pm.blk_shift, nb = 1 << bs;  // tokens per block
   const int tail = (t & (nb - 1)) + 1;        // tokens of the own block
@@ -255,7 +264,14 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
       const bool own = (E == rl.e_own);
       bool ok = i < nloc;
       int b = b_own;
-      if (ok && !own) b = rl.block(E, DENSE, ok);
+      if (ok && !own) {
+        if (!DENSE && rl.own_sel && cb == e_beg && i0 == 0 && E < rl.n_list) {
+          b = pre;
+          ok = b >= 0 && b < rl.b_sel;
+        } else {
+          b = rl.block(E, DENSE, ok);
+        }
+      }
       const uint64_t bal = __ballot(ok);
       if (l == 0) wcnt[w] = __popcll(bal);
       __syncthreads();
