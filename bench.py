@@ -2,8 +2,9 @@
 
 A step is one pass of the whole path over one batch of synthetic query rows,
 with the cache already resident in HBM:
-  decode : pool the newest complete block -> fused indexer scores and exact
-           top-k -> split-K sparse attention (one query row per sequence)
+  decode : pool the newest complete block, fused indexer scores and exact
+           top-k (one call) -> split-K sparse attention (one query row per
+           sequence)
   prefill: for every chunk of the prefill in order: pool the chunk's complete
            blocks -> fused scores + top-k -> per-row sparse attention
 The default workload is the full 1M-token prefill (32 chunks of 32,768 rows).
@@ -65,8 +66,9 @@ class Timer:
 # ------------------------------------------------------------------ decode
 
 def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True):
-    """One step = pool the newest complete block -> fused indexer scores and
-    exact top-k -> split-K sparse attention, for one query row per sequence."""
+    """One step = pool the newest complete block, fused indexer scores and
+    exact top-k (one call: the block is pooled by the top-k workgroup that
+    scores it) -> split-K sparse attention, for one query row per sequence."""
     from block_sparse_attention_32_amd import pipeline as P
     log(f"[bench] drawing {wl.name} cache on {dev}")
     cache = W.make_cache(wl, device=dev)
@@ -78,12 +80,10 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
     n_blocks = wl.total_len // bk
     P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
     step = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "decode")
-    newest = torch.full((wl.n_seqs,), n_blocks - 1, dtype=torch.int32, device=dev)
 
     def one(timer=None):
         call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
-        call("pool", B.qsa_pool_blocks, cv, newest, 1)
-        call("topk", step.select)          # fused: scores computed inside
+        call("topk", step.select_pooling_newest)   # pools, scores and selects
         call("attn", step.attend)
 
     wall, kern = _timed(one, steps, warmup)
@@ -92,13 +92,13 @@ def run_decode(wl: W.Workload, steps: int, warmup: int, dev, dense: bool = True)
     cand = sum(p // bk for p in pos)
     esz = 2 if wl.dtype == "bf16" else 4
     work = {
-        "topk": {"bytes": cand * wl.di * esz, "bound": "hbm", "kernel": "topk_kernel",
+        # the pooled keys streamed, plus each row's newest block pooled
+        "topk": {"bytes": (cand + len(pos) * (bk + 1)) * wl.di * esz, "bound": "hbm",
+                 "kernel": "topk_kernel",
                  "files": ("index.hip", "index.hpp", "select.hpp", "common.hpp")},
         "attn": {"bytes": n_tok * wl.hkv * wl.d * esz * 2, "bound": "hbm",
                  "kernel": "attn_mfma_kernel",
                  "files": ("attention_mfma.hip", "attention.hpp", "common.hpp")},
-        "pool": {"bytes": wl.n_seqs * (bk + 1) * wl.di * esz, "bound": "hbm",
-                 "kernel": "pool_kernel", "files": ("index.hip", "index.hpp", "common.hpp")},
     }
     dense_ms = None
     if dense:

@@ -29,7 +29,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -
 
 SYMBOLS = (
     "qsa_pool_blocks", "qsa_index_project", "qsa_index_scores", "qsa_topk_blocks",
-    "qsa_attn_decode",
+    "qsa_topk_blocks_pool_newest", "qsa_attn_decode",
     "qsa_attn_decode_shared", "qsa_attn_prefill", "qsa_dense_attn_decode",
     "qsa_dense_attn_prefill",
     "qsa_workspace_size", "qsa_status_string", "qsa_version",
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "qsa_index_scores": [P, P, P, P, I32, P, I64, P],
             "qsa_index_project": [P, P, P, I32, P, P, P, I32, P, P, P, P],
             "qsa_topk_blocks": [P, P, P, I64, P, P, I32, I32, P, P, P, SZ, P],
+            "qsa_topk_blocks_pool_newest": [P, P, P, P, I32, I32, P, P, P, SZ, P],
             "qsa_attn_decode": [P, P, P, I32, P, P, I32, F, P, P, SZ, P],
             "qsa_attn_decode_shared": [P, P, P, I32, P, P, P, I32, F, P, P, SZ, P],
             "qsa_attn_prefill": [P, P, P, I32, P, P, I32, F, P, P, SZ, P],
@@ -236,6 +237,18 @@ def qsa_topk_blocks(cache: CacheView, queries: QueriesView, top_k: int, sel, n_s
         ld = 0
     _call("qsa_topk_blocks", cache.ref, queries.ref, _ptr(scores), int(ld), _ptr(q_idx),
           _ptr(w), hi, int(top_k), _ptr(sel), _ptr(n_sel), _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(stream))
+
+
+def qsa_topk_blocks_pool_newest(cache: CacheView, queries: QueriesView, top_k: int, sel,
+                                n_sel, ws, q_idx, w, stream=None):
+    _check(sel, "sel", torch.int32, cache.device)
+    _check(n_sel, "n_sel", torch.int32, cache.device)
+    _check(ws, "ws", None, cache.device)
+    _check(q_idx, "q_idx", cache.dtype, cache.device)
+    _check(w, "w", torch.float32, cache.device)
+    _call("qsa_topk_blocks_pool_newest", cache.ref, queries.ref, _ptr(q_idx), _ptr(w),
+          int(q_idx.shape[1]), int(top_k), _ptr(sel), _ptr(n_sel), _ptr(ws),
           ws.numel() * ws.element_size(), _stream(stream))
 
 

@@ -297,14 +297,18 @@ qsa_status qsa_index_scores(const qsa_cache* c, const qsa_queries* qm, const voi
   return launched();
 }
 
-qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const float* scores,
-                           int64_t ld, const void* q_idx, const float* w, int32_t n_idx_heads,
-                           int32_t top_k, int32_t* sel, int32_t* n_sel, void* ws,
-                           size_t ws_bytes, void* stream) {
+// qsa_topk_blocks, and with pool_newest its variant that first pools each
+// row's newest complete block (fused scoring only)
+static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const float* scores,
+                              int64_t ld, const void* q_idx, const float* w,
+                              int32_t n_idx_heads, int32_t top_k, int32_t* sel,
+                              int32_t* n_sel, void* ws, size_t ws_bytes, void* stream,
+                              bool pool_newest) {
   qsa_status st = check_cache(c);
   if (st != QSA_OK) return st;
   if ((st = check_queries(c, qm)) != QSA_OK) return st;
   if (top_k < 1 || top_k > QSA_MAX_TOPK) return QSA_ERR_INVALID_ARG;
+  if (pool_newest && (scores != nullptr || c->kidx == nullptr)) return QSA_ERR_INVALID_ARG;
   const int max_n = qm->max_pos / cache_block(c);
   if (scores != nullptr) {
     if (ld < (int64_t)max_n) return QSA_ERR_INVALID_ARG;
@@ -346,6 +350,10 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
     a.done = reinterpret_cast<uint32_t*>(base + pp.off_done);
     a.sel = sel;
     a.n_sel = n_sel;
+    if (pool_newest) {
+      run_pool_rows(a.idx, c->kidx, c->dtype, c->idx_dim, qm->n_rows, as_stream(stream));
+      if ((st = launched()) != QSA_OK) return st;
+    }
     for (int r0 = 0; r0 < qm->n_rows; r0 += pp.rows) {
       a.row0 = r0;
       a.rows = (qm->n_rows - r0) < pp.rows ? (qm->n_rows - r0) : pp.rows;
@@ -378,6 +386,7 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
   t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);
   t.tops = reinterpret_cast<uint64_t*>(base + p.off_tops);
   t.ucap = p.ucap;
+  t.pool_kidx = pool_newest ? c->kidx : nullptr;
   for (int r0 = 0; r0 < qm->n_rows; r0 += p.rows) {
     const int rows = (qm->n_rows - r0) < p.rows ? (qm->n_rows - r0) : p.rows;
     t.row0 = r0;
@@ -385,6 +394,22 @@ qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const floa
     if ((st = launched()) != QSA_OK) return st;
   }
   return QSA_OK;
+}
+
+qsa_status qsa_topk_blocks(const qsa_cache* c, const qsa_queries* qm, const float* scores,
+                           int64_t ld, const void* q_idx, const float* w, int32_t n_idx_heads,
+                           int32_t top_k, int32_t* sel, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return topk_common(c, qm, scores, ld, q_idx, w, n_idx_heads, top_k, sel, n_sel, ws, ws_bytes,
+                     stream, false);
+}
+
+qsa_status qsa_topk_blocks_pool_newest(const qsa_cache* c, const qsa_queries* qm,
+                                       const void* q_idx, const float* w, int32_t n_idx_heads,
+                                       int32_t top_k, int32_t* sel, int32_t* n_sel, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return topk_common(c, qm, nullptr, 0, q_idx, w, n_idx_heads, top_k, sel, n_sel, ws, ws_bytes,
+                     stream, true);
 }
 
 qsa_status qsa_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void* q,

@@ -29,22 +29,14 @@ namespace qsa {
 
 // ================================================================ pooling
 
+// Lane `part` (of Di / V) of the pooled key of block b of sequence s: the
+// mean of the block's indexer keys, summed in float32 in token order.
 template <typename T, int DI>
-__global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
+__device__ __forceinline__ void pool_part(const PageMap& pm, const T* kidx, T* kbar, int s,
+                                          int b, int part) {
   constexpr int V = Vec<T>::N;
-  constexpr int G = DI / V;  // lanes per block row
-  const int s = blockIdx.y;
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int bl = gid / G, part = gid % G;
-  if (bl >= a.max_new) return;
-  const int b0 = a.blk_begin[s];
-  const int b = (b0 < 0 ? 0 : b0) + bl;
-  const int len = min(a.seq_len[s], a.max_seq_len);
-  if (b >= (len >> a.pm.blk_shift)) return;
-  const T* kidx = static_cast<const T*>(a.kidx);
-  T* kbar = static_cast<T*>(a.kbar);
-  const int nb = 1 << a.pm.blk_shift;
-  const int64_t row0 = a.pm.token_slot(s, b << a.pm.blk_shift);  // nb rows, one page
+  const int nb = 1 << pm.blk_shift;
+  const int64_t row0 = pm.token_slot(s, b << pm.blk_shift);  // nb rows, one page
   const T* src = kidx + row0 * DI + part * V;
   float o[V];
   if (nb == 4) {  // QSA: all four loads in flight at once
@@ -68,7 +60,34 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   const float inv = 1.0f / (float)nb;
 #pragma unroll
   for (int i = 0; i < V; ++i) o[i] *= inv;
-  Vec<T>::store(kbar + a.pm.block_slot(s, b) * DI + part * V, o);
+  Vec<T>::store(kbar + pm.block_slot(s, b) * DI + part * V, o);
+}
+
+template <typename T, int DI>
+__global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
+  constexpr int G = DI / Vec<T>::N;  // lanes per block row
+  const int s = blockIdx.y;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int bl = gid / G, part = gid % G;
+  if (bl >= a.max_new) return;
+  const int b0 = a.blk_begin[s];
+  const int b = (b0 < 0 ? 0 : b0) + bl;
+  const int len = min(a.seq_len[s], a.max_seq_len);
+  if (b >= (len >> a.pm.blk_shift)) return;
+  pool_part<T, DI>(a.pm, static_cast<const T*>(a.kidx), static_cast<T*>(a.kbar), s, b, part);
+}
+
+// The newest complete block before each row's position (block pos/B - 1 of
+// its sequence), pooled per row: one workgroup of Di / V lanes per row.
+template <typename T, int DI>
+__global__ void __launch_bounds__(64) pool_rows_kernel(IdxArgs a, const void* kidx) {
+  constexpr int G = DI / Vec<T>::N;
+  const int row = blockIdx.x;
+  const int n = a.pos_of(row) >> a.pm.blk_shift;
+  if (threadIdx.x >= G || n < 1) return;
+  pool_part<T, DI>(a.pm, static_cast<const T*>(kidx),
+                   static_cast<T*>(const_cast<void*>(a.kbar)), a.seq_of(row), n - 1,
+                   threadIdx.x);
 }
 
 // ================================================================ scores
@@ -567,6 +586,19 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   __shared__ uint32_t flag;
   const int rl = blockIdx.y, row = t.row0 + rl, c = blockIdx.x;
   const RowPlan p(t, row);
+  if (t.pool_kidx != nullptr && p.n >= 1 && c == (p.n - 1) / kChunk) {
+    // the row's newest complete block, pooled by the workgroup whose chunk
+    // scores it, before the scores: published with an agent-scope release
+    // so that the row's tail, in whichever workgroup arrives last, reads it
+    constexpr int G = DI / Vec<T>::N;
+    if (threadIdx.x < G) {
+      pool_part<T, DI>(t.idx.pm, static_cast<const T*>(t.pool_kidx),
+                       static_cast<T*>(const_cast<void*>(t.idx.kbar)), p.seq, p.n - 1,
+                       threadIdx.x);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+    __syncthreads();
+  }
   int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
   if (p.n <= t.top_k) {
     if (c == 0) write_all(sel_row, t.n_sel, row, p.n, t.top_k);
@@ -734,6 +766,14 @@ static void with_types(int dtype, int di, F&& f) {
 void run_pool(const PoolArgs& a, int dtype, int di, int n_seqs, hipStream_t st) {
   with_types(dtype, di, [&](auto tag, auto dic) {
     launch_pool<decltype(tag), decltype(dic)::value>(a, n_seqs, st);
+  });
+}
+
+void run_pool_rows(const IdxArgs& a, const void* kidx, int dtype, int di, int n_rows,
+                   hipStream_t st) {
+  with_types(dtype, di, [&](auto tag, auto dic) {
+    hipLaunchKernelGGL((pool_rows_kernel<decltype(tag), decltype(dic)::value>),
+                       dim3((unsigned)n_rows), dim3(64), 0, st, a, kidx);
   });
 }
 

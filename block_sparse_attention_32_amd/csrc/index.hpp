@@ -89,6 +89,7 @@ struct TopkArgs {
   uint32_t* cnt;         // [R] arrival counters
   int ucap;              // union capacity per row (union_cap)
   uint64_t* tops;        // [R][ucap] (block id << 32 | key)
+  const void* pool_kidx; // non-null: pool each row's newest complete block first
 };
 
 // ---- MFMA prefill indexer (index_mfma.hip)
@@ -126,5 +127,8 @@ void run_pool(const PoolArgs& a, int dtype, int di, int n_seqs, hipStream_t st);
 void run_scores(const IdxArgs& a, int dtype, int di, int n_rows, int max_n, float* scores,
                 int64_t ld, hipStream_t st);
 void run_topk(const TopkArgs& t, int dtype, int di, int rows, hipStream_t st);
+// block pos/B - 1 of every row's sequence (rows with pos >= B), pooled
+void run_pool_rows(const IdxArgs& a, const void* kidx, int dtype, int di, int n_rows,
+                   hipStream_t st);
 
 }  // namespace qsa

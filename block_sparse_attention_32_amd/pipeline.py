@@ -42,6 +42,12 @@ class QsaStep:
         B.qsa_topk_blocks(self.cache, self.rows, self.top_k, self.sel, self.n_sel, self.ws_topk,
                           scores=scores, q_idx=self.q_idx, w=self.w)
 
+    def select_pooling_newest(self):
+        """The decode step's pooling and selection in one call: each row's
+        newest complete block is pooled, then the rows select (fused)."""
+        B.qsa_topk_blocks_pool_newest(self.cache, self.rows, self.top_k, self.sel, self.n_sel,
+                                      self.ws_topk, self.q_idx, self.w)
+
     def attend(self):
         fn = B.qsa_attn_decode if self.mode == "decode" else B.qsa_attn_prefill
         fn(self.cache, self.rows, self.q, self.sel, self.n_sel, self.top_k, self.scale,

@@ -170,6 +170,25 @@ qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
                            int32_t *n_sel, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* Steps 1 and 3 fused for a decode step (glossary: the keys of each block
+ * are averaged, then the indexer rates every block): for every row i with
+ * pos[i] >= B, block pos[i]/B - 1 of sequence seq_id[i] -- the newest
+ * complete block before the query -- is pooled into kbar exactly as
+ * qsa_pool_blocks would, then the row's selection is made as by
+ * qsa_topk_blocks in fused mode (scores computed from q_idx, w, kbar).
+ * Precondition: every other block that a row of the call scores is pooled
+ * already; in a decode step the sequence's newest block is the only one
+ * pooled here.  Rows of one sequence may pool the same block: they write
+ * identical values.  Arguments, layouts, workspace and errors as
+ * qsa_topk_blocks with scores == NULL; also QSA_ERR_INVALID_ARG when the
+ * cache has no kidx. */
+qsa_status qsa_topk_blocks_pool_newest(const qsa_cache *c,
+                                       const qsa_queries *qm,
+                                       const void *q_idx, const float *w,
+                                       int32_t n_idx_heads, int32_t top_k,
+                                       int32_t *sel, int32_t *n_sel, void *ws,
+                                       size_t ws_bytes, void *stream);
+
 /* Steps 4/5 -- block-sparse attention without a mask (PR #30965 digest:
  * whole selected blocks plus the current fractional block; sparse FA
  * explainer: tiled softmax attention).  For every row i and query head hq

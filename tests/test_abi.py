@@ -102,6 +102,13 @@ def test_call_validation(libqsa):
     assert tk(R(c), R(q), 8, 512, None, None, 0, 512, None, 8, 8, ws, None) == -1  # no sel
     assert tk(R(c), R(q), 8, 512, None, None, 0, 512, 8, 8, 8, ws - 1, None) == -3
     assert tk(R(c), R(q), 8, 512, None, None, 0, 512, 8, 8, None, ws, None) == -3
+    # top-k that pools each row's newest block first: fused scoring only,
+    # and the cache must hold the indexer keys
+    tp = L.qsa_topk_blocks_pool_newest
+    assert tp(R(_cache(kidx=None)), R(q), 8, 8, 4, 512, 8, 8, 8, ws, None) == -1
+    assert tp(R(c), R(q), None, 8, 4, 512, 8, 8, 8, ws, None) == -1             # no q_idx
+    assert tp(R(c), R(q), 8, 8, 4, 0, 8, 8, 8, ws, None) == -1                  # top_k 0
+    assert tp(R(c), R(q), 8, 8, 4, 512, 8, 8, 8, ws - 1, None) == -3
     # attention
     wd = L.qsa_workspace_size(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 512)
     ad = L.qsa_attn_decode

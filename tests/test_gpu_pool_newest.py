@@ -1,0 +1,105 @@
+"""GPU parity of qsa_topk_blocks_pool_newest: each row's newest complete
+block (pos/B - 1) is pooled inside the call, then the row selects.  The
+newest block of every sequence is overwritten with a poison value before
+the call; the pooled keys must come out bit-exact and every selection
+bit-exact against the oracle (which pools from the keys).  Both paths are
+covered: few rows (chunked top-k, pooled by the workgroup that scores the
+block) and many rows (per-row pooling launch, then the matrix-core
+indexer)."""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_32_amd import binding as B
+from block_sparse_attention_32_amd import workloads as W
+
+from gpu_helpers import Problem, assert_sel_row, sel_rows
+
+pytestmark = pytest.mark.gpu
+
+WL = W.WORKLOADS
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _poison_newest(pb):
+    """Overwrite, for every sequence, the newest block any row pools; return
+    {(seq, block)}."""
+    wl = pb.wl
+    bpp = wl.page_size // wl.block
+    newest = {}
+    for s, t in zip(pb.seq_id_list, pb.pos_list):
+        b = t // wl.block - 1
+        if b >= 0:
+            newest[s] = max(newest.get(s, -1), b)
+    for s, b in newest.items():
+        page = int(pb.cache.block_table[s, b // bpp])
+        pb.cache.kbar[page, b % bpp] = 3.0
+    torch.cuda.synchronize()
+    return set(newest.items())
+
+
+def _check(pb, sel, n_sel, pooled):
+    torch.cuda.synchronize()
+    for s, b in pooled:
+        got = pb.gpu_kbar(s)[b]
+        want = pb.kbar_oracle(s)[b]
+        assert np.array_equal(got, want), f"seq {s} block {b} not pooled"
+    _, sel_np, n_np = sel_rows(sel, n_sel)
+    for i in range(len(pb.pos_list)):
+        assert_sel_row(sel_np[i], int(n_np[i]), pb.oracle_select(i), pb.wl.top_k)
+
+
+def _run(pb):
+    wl = pb.wl
+    T = len(pb.pos_list)
+    sel = torch.full((T, wl.top_k), 7, dtype=torch.int32, device=pb.device)
+    n_sel = torch.full((T,), -5, dtype=torch.int32, device=pb.device)
+    ws = B.workspace(B.QSA_OP_TOPK, pb.cv, pb.rows, 0, wl.top_k)
+    B.qsa_topk_blocks_pool_newest(pb.cv, pb.rows, wl.top_k, sel, n_sel, ws, pb.qs.q_idx,
+                                  pb.qs.w)
+    return sel, n_sel
+
+
+@pytest.mark.parametrize("name", ["decode_8x32k", "decode_1m"])
+def test_pool_newest_decode_workloads(gpu, name):
+    _say(f"pool newest {name}")
+    pb = Problem(WL[name], gpu)
+    pb.pool_all()
+    pooled = _poison_newest(pb)
+    sel, n_sel = _run(pb)
+    _check(pb, sel, n_sel, pooled)
+
+
+@pytest.mark.parametrize("rows", [5, 80], ids=["chunked", "matrix-core"])
+def test_pool_newest_positions(gpu, rows):
+    """Rows of one sequence at positions around block edges, including
+    positions with no complete block (pos < 4) and rows sharing their
+    newest block; 80 rows take the matrix-core path."""
+    _say(f"pool newest positions rows={rows}")
+    wl = WL["decode_8x32k"].replace(n_ctx=20000, n_seqs=1, seed=91)
+    base = [0, 3, 4, 5, 2047, 2048, 2049, 2052, 9000, 9001, 19996, 19997, 19998, 19999, 20000]
+    pos = sorted((base * 6)[:rows])
+    pb = Problem(wl, gpu, [0] * len(pos), pos)
+    pb.pool_all()
+    pooled = _poison_newest(pb)
+    sel, n_sel = _run(pb)
+    _check(pb, sel, n_sel, pooled)
+
+
+def test_pool_newest_matches_separate_calls(gpu):
+    """Pool, then select with qsa_topk_blocks, gives the same selection as
+    the fused call on the same inputs."""
+    _say("pool newest vs separate")
+    pb = Problem(WL["decode_8x32k"], gpu)
+    pb.pool_all()
+    wl = pb.wl
+    st = pb.step()
+    torch.cuda.synchronize()
+    sel, n_sel = _run(pb)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.cpu(), st.sel.cpu())
+    assert torch.equal(n_sel.cpu(), st.n_sel.cpu())
