@@ -45,6 +45,11 @@ MUTATIONS = {
     "bf16_spacing": ("spacing = np.ldexp(1.0, e - 8)", "spacing = np.ldexp(1.0, e - 9)"),
     "bf16_truncates": ("return np.rint(x / spacing) * spacing",
                        "return np.trunc(x / spacing) * spacing"),
+    "f32_no_rounding": ("return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)",
+                        "return np.asarray(x, dtype=np.float64)"),
+    "f32_truncates": ("return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)",
+                      "return (lambda m, e: np.ldexp(np.trunc(np.ldexp(m, 24)), e - 24))"
+                      "(*np.frexp(np.asarray(x, dtype=np.float64)))"),
     "mask_wrong_head": ("z = scale * (q[:, hq, :] @ k[:, hk, :].T)",
                         "z = scale * (q[:, hq, :] @ k[:, hq % k.shape[1], :].T)"),
 }

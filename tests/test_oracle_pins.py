@@ -89,6 +89,35 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(got, ref)
 
 
+def test_f32_rounding_closed_forms():
+    """binary32 keeps 24 significant bits: the spacing above 1 is 2**-23 and
+    the smallest subnormal is 2**-149; exact halves go to the even neighbour."""
+    cases = {
+        1.0 + 2.0 ** -24: 1.0,                          # half -> even (down)
+        1.0 + 3 * 2.0 ** -24: 1.0 + 2.0 ** -22,         # half -> even (up)
+        1.0 + 2.0 ** -24 + 2.0 ** -40: 1.0 + 2.0 ** -23,  # above half -> up
+        1.0 + 2.0 ** -24 - 2.0 ** -40: 1.0,             # below half -> down
+        -(1.0 + 3 * 2.0 ** -24): -(1.0 + 2.0 ** -22),
+        2.0 ** -150: 0.0,                               # half the smallest subnormal -> 0
+        3 * 2.0 ** -150: 2.0 ** -148,                   # subnormal half -> even (up)
+        5 * 2.0 ** -150: 2.0 ** -148,                   # subnormal half -> even (down)
+        0.1: 13421773 * 2.0 ** -27,                     # the float32 nearest 0.1
+        3.0: 3.0,
+    }
+    for x, want in cases.items():
+        assert O.round_to_f32(np.array([x]))[0] == want, x
+
+
+def test_pool_f32_mean_rounds_to_nearest_even():
+    # rows 1, 1, 1, 1 + 2**-22: the exact mean 1 + 2**-24 lies halfway between
+    # the float32 neighbours 1 and 1 + 2**-23 and rounds to the even one, 1
+    kidx = np.array([[1.0], [1.0], [1.0], [1.0 + 2.0 ** -22]])
+    assert O.pool_blocks(kidx, "f32")[0, 0] == 1.0
+    # rows 1, 1, 1, 1 + 3 * 2**-22: mean 1 + 3 * 2**-24 -> 1 + 2**-22
+    kidx[3, 0] = 1.0 + 3 * 2.0 ** -22
+    assert O.pool_blocks(kidx, "f32")[0, 0] == 1.0 + 2.0 ** -22
+
+
 # ---------------------------------------------------------------- pooling
 
 def test_pool_closed_forms():
