@@ -1,6 +1,9 @@
 """Builds libqsa.so (the HIP library) for gfx950 with hipcc, in-tree.
 
-Usage: python -m block_sparse_attention_32_amd.build [--verbose]
+Usage: python -m block_sparse_attention_32_amd.build [--verbose] [--incremental]
+
+--incremental recompiles only the sources whose object is older than the
+source or than any header of csrc/ and include/ (a full build otherwise).
 """
 
 from __future__ import annotations
@@ -48,8 +51,17 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _headers_mtime() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
+    hs += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str, verbose: bool, newest_dep: float = None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if newest_dep is not None and os.path.exists(obj) and \
+            os.path.getmtime(obj) > max(newest_dep, os.path.getmtime(src)):
+        return obj
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -61,12 +73,17 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
     """Compile every csrc/*.hip for gfx950 and link libqsa.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
+    dep = _headers_mtime() if incremental else None
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, dep), srcs))
+    stale = set(os.listdir(BUILD)) - {os.path.basename(o) for o in objs}
+    for f in stale:  # objects of removed sources
+        if f.endswith(".hip.o"):
+            os.remove(os.path.join(BUILD, f))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -77,4 +94,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, incremental="--incremental" in sys.argv))

@@ -1,0 +1,458 @@
+// Exact per-query top-k block selection for few rows (decode): the chunked
+// top-k kernels.  Instantiated per (element type, indexer dimension) in the
+// topk_*.hip translation units, which the library build compiles in
+// parallel.
+#pragma once
+
+#include "index_device.hpp"
+#include "select.hpp"
+
+namespace qsa {
+
+// ================================================================ top-k
+
+// Per-row plan.
+struct RowPlan {
+  int seq, n, W, jw;
+  __device__ __forceinline__ RowPlan(const TopkArgs& t, int row) {
+    seq = t.idx.seq_of(row);
+    n = t.idx.pos_of(row) >> t.idx.pm.blk_shift;
+    W = (n + kChunk - 1) / kChunk;
+    jw = row_jw(n, t.ucap);
+  }
+};
+
+struct SelfId {
+  __device__ __forceinline__ int32_t operator()(int e) const { return e; }
+};
+struct KeyArray {  // keys in LDS or global memory
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
+};
+struct ScoreKeys {  // keys of caller scores
+  const float* s;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return score_key(s[e]); }
+};
+struct IdArray {
+  const int32_t* id;
+  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
+};
+
+// Key of candidate e of a row from whichever source the row has: caller
+// scores, keys stored in the workspace, or (rare exact fallback of rows
+// whose keys are not stored) recomputed by this lane alone.
+template <typename T, int DI>
+struct RowKeys {
+  const float* given;
+  const uint32_t* stored;
+  const T* kbar;
+  const T* qrow;     // the row's q_idx, [hi][DI]
+  const float* wrow; // the row's head weights
+  const int32_t* pages;  // the sequence's row of the page table
+  int hi, bsh;           // heads; log2(blocks per page)
+  // (56 bytes: small enough to travel in registers to the out-of-line
+  // selection routines)
+  __device__ __forceinline__ RowKeys(const float* g, const uint32_t* st, const TopkArgs& t, int row,
+                                     int sq)
+      : given(g), stored(st), kbar(static_cast<const T*>(t.idx.kbar)),
+        qrow(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI),
+        wrow(t.idx.w + (int64_t)row * t.idx.hi),
+        pages(t.idx.pm.table + (int64_t)sq * t.idx.pm.max_pages), hi(t.idx.hi),
+        bsh(t.idx.pm.bpp_shift()) {}
+  __device__ __forceinline__ uint32_t operator()(int e) const {
+    if (given != nullptr) return score_key(given[e]);
+    if (stored != nullptr) return stored[e];
+    const int64_t slot = ((int64_t)pages[e >> bsh] << bsh) + (e & ((1 << bsh) - 1));
+    const T* p = kbar + slot * DI;
+    float s = 0.0f;
+    for (int h = 0; h < hi; ++h) {
+      float d = 0.0f;
+      for (int c = 0; c < DI; ++c) d = fmaf(to_f32(qrow[h * DI + c]), to_f32(p[c]), d);
+      s = fmaf(wrow[h], fmaxf(d, 0.0f), s);
+    }
+    return score_key(s);
+  }
+};
+
+__device__ __forceinline__ void write_all(int32_t* sel_row, int32_t* n_sel, int row, int n,
+                                          int top_k) {
+  for (int j = threadIdx.x; j < top_k; j += blockDim.x) sel_row[j] = j < n ? j : -1;
+  if (threadIdx.x == 0) n_sel[row] = n;
+}
+
+// Exact selection over every candidate of a row straight from a key source.
+template <class Get>
+__device__ __noinline__ void select_full(Get get, int n, int top_k, int32_t* sel_row, int32_t* n_sel,
+                            int row, SelShared& sh) {
+  uint32_t thr;
+  int r;
+  radix_kth(get, n, top_k, sh, thr, r);
+  emit_topk(get, SelfId{}, n, thr, r, sel_row, top_k, sh);
+  if (threadIdx.x == 0) n_sel[row] = top_k;
+}
+
+// One workgroup per (row, chunk of kChunk candidates).
+//
+// Rows with at most kDirectCap candidates: the chunks store their keys; the
+// last chunk of the row to finish selects over all of them in LDS.
+//
+// Longer rows: each of the chunk's four waves publishes its jw largest
+// (key, id) pairs.  The last chunk takes tau = the k-th largest key of all
+// published pairs: tau is a key of the row, and at least k keys are >= tau,
+// so tau never exceeds the row's k-th largest key and every selected block
+// has key >= tau.  A wave whose jw-th published key is below tau has all of
+// its keys >= tau among its published pairs; only a wave whose jw-th key
+// reaches tau ("saturated", rare) is rescanned.  The survivors are gathered
+// wave by wave, ascending ids inside each wave, so they come out in
+// ascending id order, and the exact radix select + ordered emission of
+// select.hpp picks the k best with ties to the lower id.
+constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
+constexpr int kWaveSel = 16;  // survivors per lane of the one-wave final select (1,024)
+
+// LDS of the tail of a long row.
+struct LongShared {
+  uint32_t skey[kSelCap];  // survivors, in ascending id order
+  int32_t sid[kSelCap];
+  int32_t sat_w[kMaxSat];  // saturated runs
+  uint32_t sat_cnt[kMaxSat], sat_off[kMaxSat];
+  uint32_t n_sat;
+};
+
+// Tail of a long row (the last chunk to finish), JW keys per published run.
+// Thread t holds union entries [E t, E t + E) -- whole runs, E = union cap /
+// 256 -- in registers, loaded at once.  tau = the k-th largest union key
+// (low bits past two radix digits cleared); a run whose last published key
+// reaches tau is saturated and rescanned from the key source; the other
+// runs' survivors (key >= tau) are placed in id order straight from the
+// registers, each run's entries ranked by id (a run lists one wave's keys
+// best first).  Then the exact select among the survivors.
+template <int JW, int E, class Src>
+__device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, int nw, int n,
+                                          int top_k, int32_t* sel_row, int32_t* n_sel, int row,
+                                          LongShared& ls, SelShared& sh) {
+  static_assert(JW <= E, "a thread holds whole runs");
+  constexpr int R = E / JW;
+  const int un = nw * JW;
+  const int e0 = (int)threadIdx.x * E;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  uint32_t k[E];
+  int32_t id[E];
+  {
+    uint64_t v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = e0 + i < un ? tops[e0 + i] : 0ull;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      k[i] = (uint32_t)v[i];
+      id[i] = (int32_t)(v[i] >> 32);
+    }
+  }
+  if (threadIdx.x == 0) ls.n_sat = 0u;
+  uint32_t tau = 1u;  // a union smaller than top_k bounds nothing: every key survives
+  if (un >= top_k) {
+    int r;
+    bool resolved;
+    radix_kth_regs<E>(k, un, top_k, sh, tau, r, resolved, 2);
+  }
+  // saturated runs (index into sat_w, or 0xff)
+  int si[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    si[rr] = 0xff;
+    const uint32_t last = k[rr * JW + JW - 1];
+    if (e0 + rr * JW < un && last >= tau && last != 0u) {
+      const uint32_t sidx = atomicAdd(&ls.n_sat, 1u);
+      if (sidx < (uint32_t)kMaxSat) {
+        ls.sat_w[sidx] = e0 / JW + rr;
+        si[rr] = (int)sidx;
+      }
+    }
+  }
+  __syncthreads();
+  const int ns = (int)ls.n_sat;
+  bool fits = ns <= kMaxSat;
+  // survivor counts of saturated runs (a run is one scoring wave's 256
+  // candidates; wave w of this workgroup counts runs w, w + 4, ..., its
+  // lanes reading 4 keys each, with no workgroup barrier per run)
+#pragma unroll 1
+  for (int i = wave; fits && i < ns; i += kSelWaves) {
+    const int e0 = ls.sat_w[i] * 256 + lane;
+    uint32_t cw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 64 * j;
+      cw += (uint32_t)__popcll(ballot(e < n && src(e) >= tau));
+    }
+    if (lane == 0) ls.sat_cnt[i] = cw;
+  }
+  __syncthreads();
+  // survivors of the unsaturated runs placed, saturated runs' places reserved
+  uint32_t cnt[R], mine = 0;
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < JW; ++j) c += (k[rr * JW + j] >= tau && k[rr * JW + j] != 0u) ? 1u : 0u;
+    cnt[rr] = si[rr] != 0xff ? ls.sat_cnt[si[rr]] : c;
+    mine += cnt[rr];
+  }
+  uint32_t m_total;
+  uint32_t off = block_incl_scan(mine, sh, m_total) - mine;
+  fits = fits && m_total <= (uint32_t)kSelCap;
+  if (fits) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      if (si[rr] != 0xff) {
+        ls.sat_off[si[rr]] = off;
+      } else {
+#pragma unroll
+        for (int i = 0; i < JW; ++i) {
+          const uint32_t ki = k[rr * JW + i];
+          if (ki >= tau && ki != 0u) {
+            uint32_t rank = 0;
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+              const uint32_t kj = k[rr * JW + j];
+              rank += (kj >= tau && kj != 0u && id[rr * JW + j] < id[rr * JW + i]) ? 1u : 0u;
+            }
+            ls.skey[off + rank] = ki;
+            ls.sid[off + rank] = id[rr * JW + i];
+          }
+        }
+      }
+      off += cnt[rr];
+    }
+  }
+  __syncthreads();
+  // survivors of saturated runs, in id order (wave w places runs w, w + 4,
+  // ...; a run's ids ascend with 64 j + lane)
+#pragma unroll 1
+  for (int i = wave; fits && i < ns; i += kSelWaves) {
+    const int e0 = ls.sat_w[i] * 256 + lane;
+    uint32_t base = ls.sat_off[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 64 * j;
+      const uint32_t kk = e < n ? src(e) : 0u;
+      const bool hit = e < n && kk >= tau;
+      const uint64_t m = ballot(hit);
+      if (hit) {
+        ls.skey[base + lanes_below(m)] = kk;
+        ls.sid[base + lanes_below(m)] = e;
+      }
+      base += (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  if (fits && m_total == (uint32_t)top_k) {
+    // exactly k survivors: all of them, already in id order
+    for (int j = threadIdx.x; j < top_k; j += kSelThreads) sel_row[j] = ls.sid[j];
+    if (threadIdx.x == 0) n_sel[row] = top_k;
+  } else if (fits && m_total <= (uint32_t)(kWave * kWaveSel)) {
+    // few survivors: one wave selects them (element jj at lane jj % 64)
+    if (wave == 0) {
+      uint32_t key[kWaveSel];
+      int32_t sid[kWaveSel];
+#pragma unroll
+      for (int i = 0; i < kWaveSel; ++i) {
+        const uint32_t jj = (uint32_t)(i * kWave + lane);
+        key[i] = jj < m_total ? ls.skey[jj] : 0u;
+        sid[i] = jj < m_total ? ls.sid[jj] : 0;
+      }
+      wave_topk_ordered<kWaveSel>(key, sid, top_k, sel_row);
+      if (lane == 0) n_sel[row] = top_k;
+    }
+  } else if (fits) {
+    uint32_t thr;
+    int r;
+    radix_kth(KeyArray{ls.skey}, (int)m_total, top_k, sh, thr, r);
+    emit_topk(KeyArray{ls.skey}, IdArray{ls.sid}, (int)m_total, thr, r, sel_row, top_k, sh);
+    if (threadIdx.x == 0) n_sel[row] = top_k;
+  } else {
+    // rare: too many survivors (heavy ties): exact select over every key
+    select_full(src, n, top_k, sel_row, n_sel, row, sh);
+  }
+}
+
+// Exact top-k of a row of n <= kDirectCap candidates whose keys get(e)
+// returns: thread t holds keys t * EPT .. t * EPT + EPT - 1 in registers
+// (all of its loads in flight at once), then a register radix select and
+// ordered emission.  Kept out of line: it runs once per row.
+template <class Get>
+__device__ __noinline__ void select_direct(Get get, int n, int top_k, int32_t* sel_row,
+                                           int32_t* n_sel, int row, SelShared& sh) {
+  constexpr int EPT = kDirectCap / kSelThreads;
+  const int base = (int)threadIdx.x * EPT;
+  uint32_t key[EPT];
+  int32_t id[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    key[i] = get(min(base + i, n - 1));
+    id[i] = base + i;
+  }
+  uint32_t thr;
+  int r;
+  bool resolved;
+  radix_kth_regs<EPT>(key, n, top_k, sh, thr, r, resolved);
+  emit_regs<EPT>(key, id, n, thr, r, sel_row, top_k, sh);
+  if (threadIdx.x == 0) n_sel[row] = top_k;
+}
+
+// UCAP: the union capacity of the call.  With kUnionCapL the tail of the
+// long rows runs in topk_tail_kernel (64 union entries per thread would
+// crowd this kernel's registers).
+template <typename T, int DI, int HI, int UCAP>
+__global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
+  __shared__ uint32_t keys[kChunk];
+  __shared__ int32_t pages[kChunk];
+  __shared__ LongShared ls;
+  __shared__ SelShared sh;
+  __shared__ uint32_t flag;
+  const int rl = blockIdx.y, row = t.row0 + rl, c = blockIdx.x;
+  const RowPlan p(t, row);
+  if (t.pool_kidx != nullptr && p.n >= 1 && c == (p.n - 1) / kChunk) {
+    // the row's newest complete block, pooled by the workgroup whose chunk
+    // scores it, before the scores: published with an agent-scope release
+    // so that the row's tail, in whichever workgroup arrives last, reads it
+    constexpr int G = DI / Vec<T>::N;
+    if (threadIdx.x < G) {
+      pool_part<T, DI>(t.idx.pm, static_cast<const T*>(t.pool_kidx),
+                       static_cast<T*>(const_cast<void*>(t.idx.kbar)), p.seq, p.n - 1,
+                       threadIdx.x);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+    __syncthreads();
+  }
+  int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
+  if (p.n <= t.top_k) {
+    if (c == 0) write_all(sel_row, t.n_sel, row, p.n, t.top_k);
+    return;
+  }
+  const bool direct = p.n <= kDirectCap;
+  const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
+  if (direct && given) {  // every score is stored already: one workgroup
+    if (c != 0) return;
+    select_direct(ScoreKeys{given}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    return;
+  }
+  if (c >= p.W) return;
+  const int c0 = c * kChunk;
+  uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
+  const bool keep = !given && (direct || t.materialize);
+  if (given) {
+    for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
+      keys[i] = (c0 + i < p.n) ? score_key(given[c0 + i]) : 0u;
+    __syncthreads();
+  } else {
+    typename RowQuery<T, DI, HI>::type iq;
+    load_row_query<T, DI, HI>(iq, t.idx, row);
+    chunk_scores<T, DI, HI>(t.idx, p.seq, p.n, c0, iq, pages, keys);
+    if (keep) {
+      for (int i = threadIdx.x; i < kChunk && c0 + i < p.n; i += blockDim.x)
+        st_agent(ws_row + c0 + i, keys[i]);
+    }
+  }
+  constexpr bool OWN_TAIL = UCAP <= kUnionCapM;  // the tail runs here
+  uint64_t* tops = t.tops + (int64_t)rl * UCAP;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  if (!direct) {
+    // per-wave top-jw (key, id) pairs of this chunk, best first (key 0 =
+    // nothing left)
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = keys[wave * 256 + lane + 64 * i];
+    uint64_t* dst = tops + (c * kSelWaves + wave) * p.jw;
+    for (int j = 0; j < p.jw; ++j) {
+      const uint32_t lm = max(max(v[0], v[1]), max(v[2], v[3]));
+      const uint32_t wm = wave_max_u32(lm);
+      const uint64_t b = ballot(lm == wm);
+      if (lane == (int)(__ffsll((unsigned long long)b) - 1)) {
+        int hit = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+          if (v[i] == wm) hit = i;
+        const uint32_t id = (uint32_t)(c0 + wave * 256 + lane + 64 * hit);
+        st_agent(dst + j, ((uint64_t)id << 32) | wm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i == hit) v[i] = 0u;
+      }
+    }
+  }
+  if (!OWN_TAIL && !direct) return;  // the tail follows in topk_tail_kernel
+  if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
+  if (direct) {
+    select_direct(KeyArray{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    return;
+  }
+
+  // ---- last chunk of a long row
+  if constexpr (OWN_TAIL) {
+    const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+    const int nw = p.W * kSelWaves;
+    constexpr int E = UCAP / kSelThreads;
+    switch (p.jw) {
+      case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      default:
+        if constexpr (E >= 32)
+          long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
+        break;
+    }
+  }
+}
+
+// The tail of the long rows of a large selection, after topk_kernel has
+// published every chunk's per-wave tops: one workgroup per row.
+template <typename T, int DI>
+__global__ void __launch_bounds__(256) topk_tail_kernel(TopkArgs t) {
+  __shared__ LongShared ls;
+  __shared__ SelShared sh;
+  const int rl = blockIdx.x, row = t.row0 + rl;
+  const RowPlan p(t, row);
+  if (p.n <= t.top_k || p.n <= kDirectCap) return;  // done by topk_kernel
+  int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
+  const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
+  uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
+  const bool keep = !given && t.materialize;
+  const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+  const uint64_t* tops = t.tops + (int64_t)rl * kUnionCapL;
+  const int nw = p.W * kSelWaves;
+  constexpr int E = kUnionCapL / kSelThreads;
+  switch (p.jw) {
+    case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    default: long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+  }
+}
+
+// Launches the top-k kernels of one row batch for element type T and
+// indexer dimension DI; the compile-time head count is the real count
+// rounded up to 2, 4 or 8 (padding heads carry zero weight).
+template <typename T, int DI, int HI>
+static void launch_topk(const TopkArgs& t, int rows, hipStream_t st) {
+  dim3 grid((unsigned)t.w_max, (unsigned)rows);
+  if (t.ucap == kUnionCapL) {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapL>), grid, dim3(256), 0, st, t);
+    hipLaunchKernelGGL((topk_tail_kernel<T, DI>), dim3((unsigned)rows), dim3(256), 0, st, t);
+  } else if (t.ucap == kUnionCapM) {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapM>), grid, dim3(256), 0, st, t);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCap>), grid, dim3(256), 0, st, t);
+  }
+}
+
+template <typename T, int DI>
+void launch_topk_typed(const TopkArgs& t, int rows, hipStream_t st) {
+  if (t.idx.hi <= 2) launch_topk<T, DI, 2>(t, rows, st);
+  else if (t.idx.hi <= 4) launch_topk<T, DI, 4>(t, rows, st);
+  else launch_topk<T, DI, 8>(t, rows, st);
+}
+
+}  // namespace qsa

@@ -1,0 +1,6 @@
+// Top-k kernels for float32 caches with indexer dimension 16.
+#include "topk.hpp"
+
+namespace qsa {
+template void launch_topk_typed<float, 16>(const TopkArgs& t, int rows, hipStream_t st);
+}  // namespace qsa
