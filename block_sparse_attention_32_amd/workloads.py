@@ -12,7 +12,12 @@ workloads they discuss, see the design notes):
   clipped to [-4, 4], with x ~ N(0, 1) for keys and x ~ N(0, 1) + s_seq for
   queries, where s_seq in {-1, +1}^Di is one seeded direction per sequence.
   On this grid every float32 sum and product of the indexer is exact, so any
-  summation order gives the same scores bit for bit.
+  summation order gives the same scores bit for bit.  The shared direction
+  makes the planted needles win for every query; it also makes the rows of a
+  sequence prefer some of the same blocks (about 30 % of two rows'
+  selections coincide at 1M context).  Workloads with direction_scale 0
+  draw x ~ N(0, 1) alone: their selections are independent across rows (the
+  needles are then not guaranteed to be selected).
 * Head weights w = (round(15 u) + 1) / 16 with u ~ U(0, 1): multiples of
   1/16 in [1/16, 1], never zero.
 * Needle blocks: all 4 indexer keys of a 4-token span equal 3 * s_seq, which
@@ -58,6 +63,7 @@ class Workload:
     hidden: int = 0         # hidden size of the indexer projections ("project")
     seed: int = 0
     block: int = 4          # tokens per pooled block (1: token-granular selection)
+    direction_scale: float = 1.0  # weight of the sequence direction in q_idx
 
     @property
     def torch_dtype(self):
@@ -110,6 +116,13 @@ WORKLOADS = {
         name="prefill_1m", mode="prefill", dtype="bf16", n_seqs=1, n_ctx=0,
         n_new=1048576, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
         n_needles=32, chunk=32768, seed=1005),
+    # the same prefill with indexer queries that share no direction: rows
+    # select independently of each other (no reuse of selected blocks
+    # across the rows of a chunk)
+    "prefill_1m_indep": Workload(
+        name="prefill_1m_indep", mode="prefill", dtype="bf16", n_seqs=1, n_ctx=0,
+        n_new=1048576, hq=16, hkv=2, d=128, hi=4, di=64, top_k=512,
+        n_needles=32, chunk=32768, seed=1005, direction_scale=0.0),
     # token-granular selection (block size 1) with the same 2,048-token
     # budget, on the same inputs as the block workloads they are named after
     "prefill_8k_at_128k_tok": Workload(
@@ -245,7 +258,7 @@ def make_queries(wl: Workload, cache: Cache, seq_id, pos, device="cpu",
     q = torch.randn((n, wl.hq, wl.d), generator=g, device=device).to(dt)
     noise = torch.randn((n, wl.hi, wl.di), generator=g, device=device)
     direc = cache.direction.to(device)[seq_id.long()]            # [n, Di]
-    q_idx = grid8(noise + direc[:, None, :]).to(dt)
+    q_idx = grid8(noise + wl.direction_scale * direc[:, None, :]).to(dt)
     u = torch.rand((n, wl.hi), generator=g, device=device)
     w = (torch.round(u * 15.0) + 1.0) / 16.0
     return Queries(seq_id=seq_id.contiguous(), pos=pos.contiguous(),

@@ -242,7 +242,11 @@ qsa_status qsa_index_project(const qsa_cache *c, const qsa_queries *qm,
  *         U {B*(pos[s]/B) .. pos[i]}
  * sel_of[i] = i gives exactly qsa_attn_decode's result.  sel_of: [T] device
  * int32; rows outside the limits above are clamped to them (their result
- * is unspecified).  ws: qsa_workspace_size(QSA_OP_ATTN_DECODE_SHARED, ...). */
+ * is unspecified).  sel and n_sel must hold all T rows ([T][top_k] and
+ * [T]), also those of rows that reuse another row's selection: every row's
+ * own entries are read (and ignored when sel_of[i] != i), so that the reads
+ * of a row start together.  ws: qsa_workspace_size(QSA_OP_ATTN_DECODE_SHARED,
+ * ...). */
 qsa_status qsa_attn_decode_shared(const qsa_cache *c, const qsa_queries *qm,
                                   const void *q, int32_t n_q_heads,
                                   const int32_t *sel, const int32_t *n_sel,
