@@ -16,9 +16,13 @@
 //     the tile's V rows.  A product with a ones operand sums the
 //     numerators (the softmax denominator) on the matrix core as well.
 //
-// Workgroups: 4 waves per (row, split).  With n_splits > 1 (the SPLIT
-// instances) the split partials go to the workspace and the last split of
-// the row merges them.
+// Workgroups: the SPLIT instances (few rows) run 8 waves per (row, split),
+// waves w and w + Hkv on the same KV head; the split partials go to the
+// workspace and the last split of the row merges them.  The per-row
+// instances (many rows) run 4 waves per (row, KV head): workgroup
+// row * Hkv + head, so that with the round-robin placement of workgroups on
+// the 8 XCDs (Hkv dividing 8) every XCD serves one KV head only, and its L2
+// holds twice as many blocks of that head as it would of both.
 #include <type_traits>
 
 #include "attention.hpp"
@@ -186,9 +190,12 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int l = lane_id(), g = l / 16, c16 = l % 16;
   const int hkv = a.hkv, hq = a.hq, G = hq / hkv;
-  const int wph = NW / hkv;  // waves per KV head
-  const int hk = w % hkv, wsub = w / hkv;
-  const int row = blockIdx.y, split = blockIdx.x;
+  // one KV head per workgroup (per-row instances) or Hkv of them (SPLIT)
+  const int wph = SPLIT ? NW / hkv : NW;  // waves per KV head
+  const int hk = SPLIT ? w % hkv : (int)(blockIdx.x % (unsigned)hkv);
+  const int wsub = SPLIT ? w / hkv : w;
+  const int row = SPLIT ? (int)blockIdx.y : (int)(blockIdx.x / (unsigned)hkv);
+  const int split = SPLIT ? (int)blockIdx.x : 0;
 
   // the reads that depend on the row index alone, issued together so that
   // their latencies overlap: sequence, position, selection length, and the
@@ -454,18 +461,20 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   }
   __syncthreads();
   bf16_t* orow = static_cast<bf16_t*>(a.out) + (int64_t)row * hq * D;
-  // combine the waves of each KV head: thread = (head, its dims)
-  const MergeLane<D, NT> lane(hq);
+  // combine the waves of each KV head: thread = (head, its dims); lane.h is
+  // the query head (SPLIT) or the head within this workgroup's group
+  const MergeLane<D, NT> lane(SPLIT ? hq : G);
   constexpr int ND = MergeLane<D, NT>::ND;
   if (lane.on) {
-    const int hk_ = lane.h / G, hh = lane.h % G;
+    const int hk_ = SPLIT ? lane.h / G : 0, hh = SPLIT ? lane.h % G : lane.h;
+    const int wstride = SPLIT ? hkv : 1;  // wave j of the head: hk_ + j * wstride
     float M = -INFINITY;
-    for (int j = 0; j < wph; ++j) M = fmaxf(M, mrg[((hk_ + j * hkv) * 16 + hh) * (D + 2) + D]);
+    for (int j = 0; j < wph; ++j) M = fmaxf(M, mrg[((hk_ + j * wstride) * 16 + hh) * (D + 2) + D]);
     float L = 0.0f, O[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) O[i] = 0.0f;
     for (int j = 0; j < wph; ++j) {
-      const float* o = mrg + ((hk_ + j * hkv) * 16 + hh) * (D + 2);
+      const float* o = mrg + ((hk_ + j * wstride) * 16 + hh) * (D + 2);
       const float f = (o[D] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(o[D] - M);
       L = fmaf(o[D + 1], f, L);
 #pragma unroll
@@ -473,8 +482,9 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     }
     if constexpr (!SPLIT) {
       const float inv = 1.0f / L;
+      bf16_t* oh = orow + (hk * G + lane.h) * D + lane.d0;
 #pragma unroll
-      for (int i = 0; i < ND; ++i) orow[lane.h * D + lane.d0 + i] = f32_to_bf16(O[i] * inv);
+      for (int i = 0; i < ND; ++i) oh[i] = f32_to_bf16(O[i] * inv);
     } else {
       // partials are read by another workgroup: agent-scope stores, 8 bytes
       // at a time
@@ -497,8 +507,10 @@ bool attn_mfma_supported(int dtype, int hq, int hkv, int d) {
 }
 
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st) {
-  dim3 grid((unsigned)a.n_splits, (unsigned)n_rows);
   const bool split = a.n_splits > 1;
+  // SPLIT: (split, row); per row: one workgroup per (row, KV head)
+  const dim3 grid = split ? dim3((unsigned)a.n_splits, (unsigned)n_rows)
+                          : dim3((unsigned)n_rows * (unsigned)a.hkv);
   const bool wide = a.n_slots * a.hkv * d * 2 > kNarrowCacheBytes;
 #define QSA_ATTN_LAUNCH(DD, DN, SP, WD) \
   hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD>), grid, dim3(attn_waves<SP>() * 64), 0, \
