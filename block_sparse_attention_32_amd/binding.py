@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqsa.so")
+# QSA_LIB selects another build of the same library (the sanitized host
+# build the ABI tests run against); the in-tree libqsa.so otherwise
+LIB_PATH = os.environ.get("QSA_LIB") or os.path.join(_PKG, "libqsa.so")
 
 QSA_BLOCK = 4
 QSA_MAX_BLOCK = 16
