@@ -78,7 +78,7 @@ qsa_status launched() {
 struct TopkPlan {
   int rows, w_max, materialize, ucap;
   int64_t ws_ld;
-  size_t off_ctr, off_tops, off_scores, total;
+  size_t off_ctr, off_tops, off_nxt, off_scores, total;
 };
 
 // MFMA prefill indexer plan (fused mode, many rows)
@@ -123,6 +123,7 @@ TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm, int top_k) {
   size_t o = 0;
   p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
   p.off_tops = o;   o = align256(o + (size_t)p.rows * p.ucap * 8);
+  p.off_nxt = o;    o = align256(o + (size_t)p.rows * p.w_max * kChunkWaves * 4);
   p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
   p.total = o;
   return p;
@@ -385,6 +386,7 @@ static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const f
   t.ws_ld = p.ws_ld;
   t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);
   t.tops = reinterpret_cast<uint64_t*>(base + p.off_tops);
+  t.nxt = reinterpret_cast<uint32_t*>(base + p.off_nxt);
   t.ucap = p.ucap;
   t.pool_kidx = pool_newest ? c->kidx : nullptr;
   for (int r0 = 0; r0 < qm->n_rows; r0 += p.rows) {

@@ -8,6 +8,7 @@
 namespace qsa {
 
 constexpr int kChunk = 1024;        // candidate blocks per workgroup (4 per thread)
+constexpr int kChunkWaves = 4;      // waves of a top-k workgroup (one run of 256 candidates each)
 constexpr int kDirectCap = 8192;    // rows with <= this many candidates select in one pass
 constexpr int kUnionCap = 4096;     // (key, id) pairs of the per-wave tops of one row
 constexpr int kLargeTopk = 512;     // larger selections use the wider unions below
@@ -89,6 +90,7 @@ struct TopkArgs {
   uint32_t* cnt;         // [R] arrival counters
   int ucap;              // union capacity per row (union_cap)
   uint64_t* tops;        // [R][ucap] (block id << 32 | key)
+  uint32_t* nxt;         // [R][w_max * 4] largest key of each wave not in its tops (0: none)
   const void* pool_kidx; // non-null: pool each row's newest complete block first
 };
 

@@ -97,15 +97,17 @@ __device__ __noinline__ void select_full(Get get, int n, int top_k, int32_t* sel
 // last chunk of the row to finish selects over all of them in LDS.
 //
 // Longer rows: each of the chunk's four waves publishes its jw largest
-// (key, id) pairs.  The last chunk takes tau = the k-th largest key of all
-// published pairs: tau is a key of the row, and at least k keys are >= tau,
-// so tau never exceeds the row's k-th largest key and every selected block
-// has key >= tau.  A wave whose jw-th published key is below tau has all of
-// its keys >= tau among its published pairs; only a wave whose jw-th key
-// reaches tau ("saturated", rare) is rescanned.  The survivors are gathered
+// (key, id) pairs, and the largest of its other keys.  The last chunk takes
+// tau = the k-th largest key of all published pairs: tau is a key of the
+// row, and at least k keys are >= tau, so tau never exceeds the row's k-th
+// largest key and every selected block has key >= tau.  A wave whose
+// largest unpublished key is below tau has all of its keys >= tau among its
+// published pairs; only a wave whose unpublished key reaches tau
+// ("saturated": at least jw + 1 of its keys reach tau, rare) is rescanned.  The survivors are gathered
 // wave by wave, ascending ids inside each wave, so they come out in
 // ascending id order, and the exact radix select + ordered emission of
 // select.hpp picks the k best with ties to the lower id.
+static_assert(kChunkWaves == kSelWaves, "a top-k workgroup's waves are its runs");
 constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
 constexpr int kWaveSel = 16;  // survivors per lane of the one-wave final select (1,024)
 
@@ -120,15 +122,17 @@ struct LongShared {
 
 // Tail of a long row (the last chunk to finish), JW keys per published run.
 // Thread t holds union entries [E t, E t + E) -- whole runs, E = union cap /
-// 256 -- in registers, loaded at once.  tau = the k-th largest union key
-// (low bits past two radix digits cleared); a run whose last published key
-// reaches tau is saturated and rescanned from the key source; the other
-// runs' survivors (key >= tau) are placed in id order straight from the
-// registers, each run's entries ranked by id (a run lists one wave's keys
-// best first).  Then the exact select among the survivors.
+// 256 -- in registers, loaded at once, with the largest unpublished key of
+// each of its runs (nxt).  tau = the k-th largest union key (low bits past
+// two radix digits cleared); a run whose unpublished key reaches tau is
+// saturated and rescanned from the key source; the other runs' survivors
+// (key >= tau) are placed in id order straight from the registers, each
+// run's entries ranked by id (a run lists one wave's keys best first).
+// Then the exact select among the survivors.
 template <int JW, int E, class Src>
-__device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, int nw, int n,
-                                          int top_k, int32_t* sel_row, int32_t* n_sel, int row,
+__device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops,
+                                          const uint32_t* nxt, int nw, int n, int top_k,
+                                          int32_t* sel_row, int32_t* n_sel, int row,
                                           LongShared& ls, SelShared& sh) {
   static_assert(JW <= E, "a thread holds whole runs");
   constexpr int R = E / JW;
@@ -137,10 +141,13 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
   const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t k[E];
   int32_t id[E];
+  uint32_t nx[R];  // largest unpublished key of each of this thread's runs
   {
     uint64_t v[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = e0 + i < un ? tops[e0 + i] : 0ull;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) nx[rr] = e0 + rr * JW < un ? nxt[e0 / JW + rr] : 0u;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       k[i] = (uint32_t)v[i];
@@ -159,8 +166,7 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops, 
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     si[rr] = 0xff;
-    const uint32_t last = k[rr * JW + JW - 1];
-    if (e0 + rr * JW < un && last >= tau && last != 0u) {
+    if (e0 + rr * JW < un && nx[rr] >= tau && nx[rr] != 0u) {
       const uint32_t sidx = atomicAdd(&ls.n_sat, 1u);
       if (sidx < (uint32_t)kMaxSat) {
         ls.sat_w[sidx] = e0 / JW + rr;
@@ -378,6 +384,10 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
           if (i == hit) v[i] = 0u;
       }
     }
+    // the largest key left: a bound of every unpublished key of the wave
+    const uint32_t rest = wave_max_u32(max(max(v[0], v[1]), max(v[2], v[3])));
+    if (lane == 0)
+      st_agent(t.nxt + (int64_t)rl * t.w_max * kSelWaves + c * kSelWaves + wave, rest);
   }
   if (!OWN_TAIL && !direct) return;  // the tail follows in topk_tail_kernel
   if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
@@ -391,15 +401,16 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
     const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
     const int nw = p.W * kSelWaves;
     constexpr int E = UCAP / kSelThreads;
+    const uint32_t* nxt = t.nxt + (int64_t)rl * t.w_max * kSelWaves;
     switch (p.jw) {
-      case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 1: long_tail<1, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 2: long_tail<2, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 4: long_tail<4, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 8: long_tail<8, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 16: long_tail<16, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
       default:
         if constexpr (E >= 32)
-          long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
+          long_tail<32, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
         break;
     }
   }
@@ -420,15 +431,16 @@ __global__ void __launch_bounds__(256) topk_tail_kernel(TopkArgs t) {
   const bool keep = !given && t.materialize;
   const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
   const uint64_t* tops = t.tops + (int64_t)rl * kUnionCapL;
+  const uint32_t* nxt = t.nxt + (int64_t)rl * t.w_max * kSelWaves;
   const int nw = p.W * kSelWaves;
   constexpr int E = kUnionCapL / kSelThreads;
   switch (p.jw) {
-    case 1: long_tail<1, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 2: long_tail<2, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 4: long_tail<4, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 8: long_tail<8, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 16: long_tail<16, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    default: long_tail<32, E>(src, tops, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 1: long_tail<1, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 2: long_tail<2, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 4: long_tail<4, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 8: long_tail<8, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 16: long_tail<16, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    default: long_tail<32, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
   }
 }
 
