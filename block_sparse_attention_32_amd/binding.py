@@ -34,8 +34,10 @@ SYMBOLS = (
     "qsa_topk_blocks_pool_newest", "qsa_attn_decode",
     "qsa_attn_decode_shared", "qsa_attn_prefill", "qsa_dense_attn_decode",
     "qsa_dense_attn_prefill",
-    "qsa_workspace_size", "qsa_status_string", "qsa_version",
+    "qsa_workspace_size", "qsa_status_string", "qsa_version", "qsa_debug_take",
 )
+QSA_DEBUG_BAD_PAGE, QSA_DEBUG_BAD_ROW, QSA_DEBUG_BAD_SEL = 1, 2, 4
+DEBUG_LIB_PATH = os.path.join(_PKG, "libqsa_debug.so")
 
 
 class QsaError(RuntimeError):
@@ -91,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "qsa_dense_attn_decode": [P, P, P, I32, F, P, P, SZ, P],
             "qsa_dense_attn_prefill": [P, P, P, I32, F, P, P, SZ, P],
             "qsa_workspace_size": [I32, P, P, I32, I32],
+            "qsa_debug_take": [P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -193,6 +196,14 @@ def _call(name, *args):
     st = getattr(lib(), name)(*args)
     if st != 0:
         raise QsaError(name, st)
+
+
+def qsa_debug_take() -> int:
+    """Device-data check bits recorded by a debug build since the last call
+    (synchronises); raises QsaError on the release build."""
+    f = ctypes.c_uint32(0)
+    _call("qsa_debug_take", ctypes.byref(f))
+    return int(f.value)
 
 
 def qsa_workspace_size(op: int, cache: CacheView, queries: QueriesView,

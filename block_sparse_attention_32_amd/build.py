@@ -1,6 +1,9 @@
 """Builds libqsa.so (the HIP library) for gfx950 with hipcc, in-tree.
 
-Usage: python -m block_sparse_attention_32_amd.build [--verbose] [--incremental]
+Usage: python -m block_sparse_attention_32_amd.build [--verbose] [--incremental] [--debug]
+
+--debug builds libqsa_debug.so: the same sources with -DQSA_DEBUG (device
+data checks, see qsa_debug_take in include/qsa.h).
 
 --incremental recompiles only the sources whose object is older than the
 source or than any header of csrc/ and include/ (a full build otherwise).
@@ -20,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
+# the same sources with the device-data checks on (-DQSA_DEBUG)
+DEBUG_LIB = os.path.join(PKG, "libqsa_debug.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -57,12 +62,12 @@ def _headers_mtime() -> float:
     return max(os.path.getmtime(h) for h in hs)
 
 
-def _compile(src: str, verbose: bool, newest_dep: float = None) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, newest_dep: float = None, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, "debug" if debug else "", os.path.basename(src) + ".o")
     if newest_dep is not None and os.path.exists(obj) and \
             os.path.getmtime(obj) > max(newest_dep, os.path.getmtime(src)):
         return obj
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DQSA_DEBUG"] if debug else []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,25 +78,29 @@ def _compile(src: str, verbose: bool, newest_dep: float = None) -> str:
     return obj
 
 
-def build(verbose: bool = False, incremental: bool = False) -> str:
-    """Compile every csrc/*.hip for gfx950 and link libqsa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, incremental: bool = False, debug: bool = False) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libqsa.so (debug:
+    libqsa_debug.so with -DQSA_DEBUG); returns its path."""
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     dep = _headers_mtime() if incremental else None
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, dep), srcs))
-    stale = set(os.listdir(BUILD)) - {os.path.basename(o) for o in objs}
+        objs = list(ex.map(lambda s: _compile(s, verbose, dep, debug), srcs))
+    stale = set(os.listdir(out_dir)) - {os.path.basename(o) for o in objs}
     for f in stale:  # objects of removed sources
         if f.endswith(".hip.o"):
-            os.remove(os.path.join(BUILD, f))
-    tmp = LIB + ".tmp"
+            os.remove(os.path.join(out_dir, f))
+    lib = DEBUG_LIB if debug else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv, incremental="--incremental" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, incremental="--incremental" in sys.argv,
+                debug="--debug" in sys.argv))

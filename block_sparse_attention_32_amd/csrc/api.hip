@@ -4,11 +4,24 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "attention.hpp"
 #include "project.hpp"
 #include "index.hpp"
 
 using namespace qsa;
+
+#ifdef QSA_DEBUG
+namespace qsa {
+// the error-word readers of every translation unit (registered at load)
+static std::vector<uint32_t (*)()>& debug_units() {
+  static std::vector<uint32_t (*)()> units;
+  return units;
+}
+void debug_register(uint32_t (*take)()) { debug_units().push_back(take); }
+}  // namespace qsa
+#endif
 
 namespace {
 
@@ -65,6 +78,7 @@ PageMap page_map(const qsa_cache* c) {
   pm.max_pages = c->max_pages_per_seq;
   pm.page_shift = log2i(c->page_size);
   pm.blk_shift = log2i(cache_block(c));
+  pm.n_pages = c->n_pages;
   return pm;
 }
 
@@ -520,6 +534,18 @@ const char* qsa_status_string(qsa_status s) {
   }
 }
 
-int32_t qsa_version(void) { return (0 << 16) | 1; }
+int32_t qsa_version(void) { return (0 << 16) | 2; }
+
+qsa_status qsa_debug_take(uint32_t* flags) {
+  if (flags == nullptr) return QSA_ERR_INVALID_ARG;
+  *flags = 0u;
+#ifdef QSA_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return QSA_ERR_HIP;
+  for (auto take : debug_units()) *flags |= take();
+  return QSA_OK;
+#else
+  return QSA_ERR_UNSUPPORTED;
+#endif
+}
 
 }  // extern "C"

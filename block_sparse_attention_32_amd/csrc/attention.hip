@@ -41,8 +41,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_kernel(AttnArgs a) {
   T* vs = reinterpret_cast<T*>(smem + L.v);                   // [TT][hkv][D]
   __shared__ uint32_t flag;
 
-  const int seq = min(max(a.seq_id[row], 0), a.n_seqs - 1);
-  const int t = min(max(a.pos[row], 0), a.max_pos);
+  const int seq = clamp_flag(a.seq_id[row], 0, a.n_seqs - 1, QSA_DEBUG_BAD_ROW);
+  const int t = clamp_flag(a.pos[row], 0, a.max_pos, QSA_DEBUG_BAD_ROW);
   // n_sel is clamped to [0, top_k]; selected ids the row may not attend are
   // skipped
   const RowList rl(a, row, t, DENSE, DENSE ? 0 : a.n_sel[row]);

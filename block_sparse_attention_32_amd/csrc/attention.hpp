@@ -55,12 +55,12 @@ struct RowList {
     b_own = t >> bs;
     int rs = row;
     b_sel = b_own;
-    n_list = dense ? b_own : min(max(n_sel_row, 0), a.top_k);
+    n_list = dense ? b_own : clamp_flag(n_sel_row, 0, a.top_k, QSA_DEBUG_BAD_SEL);
     if (!dense && a.sel_of != nullptr) {
-      rs = min(max(a.sel_of[row], 0), a.n_rows - 1);
+      rs = clamp_flag(a.sel_of[row], 0, a.n_rows - 1, QSA_DEBUG_BAD_SEL);
       const int ts = min(max(a.pos[rs], 0), a.max_pos);
       b_sel = max(min(ts >> bs, b_own), b_own - (((QSA_MAX_SHARED_LAG - 1) >> bs) + 1));
-      if (rs != row) n_list = min(max(a.n_sel[rs], 0), a.top_k);
+      if (rs != row) n_list = clamp_flag(a.n_sel[rs], 0, a.top_k, QSA_DEBUG_BAD_SEL);
     }
     own_sel = rs == row;
     n_bridge = b_own - b_sel;
@@ -75,6 +75,7 @@ struct RowList {
     }
     const int b = dense ? e : sel[e];
     ok = b >= 0 && b < b_sel;
+    if (!ok && own_sel) debug_flag(QSA_DEBUG_BAD_SEL);
     return b;
   }
 };

@@ -207,8 +207,8 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int nsel_raw = DENSE ? 0 : a.n_sel[row];
   const int32_t pre =
       DENSE ? -1 : a.sel[(int64_t)row * a.top_k + min(e_beg + (int)threadIdx.x, a.top_k - 1)];
-  const int seq = min(max(sid_raw, 0), a.n_seqs - 1);
-  const int t = min(max(pos_raw, 0), a.max_pos);
+  const int seq = clamp_flag(sid_raw, 0, a.n_seqs - 1, QSA_DEBUG_BAD_ROW);
+  const int t = clamp_flag(pos_raw, 0, a.max_pos, QSA_DEBUG_BAD_ROW);
   const RowList rl(a, row, t, DENSE, nsel_raw);
   const int b_own = rl.b_own;
   const int n_entries = rl.e_own + 1;
@@ -275,6 +275,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
         if (!DENSE && rl.own_sel && cb == e_beg && i0 == 0 && E < rl.n_list) {
           b = pre;
           ok = b >= 0 && b < rl.b_sel;
+          if (!ok) debug_flag(QSA_DEBUG_BAD_SEL);
         } else {
           b = rl.block(E, DENSE, ok);
         }

@@ -78,6 +78,59 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---------------------------------------------------------------- debug checks
+
+// Built with -DQSA_DEBUG (libqsa_debug.so), the kernels check the device data
+// the host cannot see: a page id outside [0, n_pages), a sequence id or
+// position outside its range, and a selection length or selected id a row
+// may not use.  Each such value sets a bit of a per-translation-unit error
+// word (qsa_debug_take reports and clears them) and is replaced by one that
+// keeps every access inside the caller's buffers (page 0; the clamped
+// sequence id or position; the selection entry skipped), the same
+// replacement the release build makes for everything but page ids.
+// Without QSA_DEBUG the checks compile to nothing.
+#ifdef QSA_DEBUG
+static __device__ uint32_t g_debug_flags;  // this translation unit's error bits
+__device__ __forceinline__ void debug_flag(uint32_t bit) { atomicOr(&g_debug_flags, bit); }
+void debug_register(uint32_t (*take)());   // api.hip: the units' readers
+namespace {
+uint32_t debug_take_unit() {
+  uint32_t v = 0, z = 0;
+  (void)hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof v, 0, hipMemcpyDeviceToHost);
+  (void)hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &z, sizeof z, 0, hipMemcpyHostToDevice);
+  return v;
+}
+struct DebugUnit {
+  DebugUnit() { debug_register(&debug_take_unit); }
+} debug_unit_registered;
+}  // namespace
+#else
+__device__ __forceinline__ void debug_flag(uint32_t) {}
+#endif
+
+// page id read from a block table: checked in debug builds
+__device__ __forceinline__ int32_t checked_page(int32_t page, int64_t n_pages) {
+#ifdef QSA_DEBUG
+  if ((uint64_t)(uint32_t)page >= (uint64_t)n_pages) {
+    debug_flag(QSA_DEBUG_BAD_PAGE);
+    return 0;
+  }
+#else
+  (void)n_pages;
+#endif
+  return page;
+}
+
+// v clamped to [lo, hi]; in debug builds a value outside sets `bit`
+__device__ __forceinline__ int clamp_flag(int v, int lo, int hi, uint32_t bit) {
+#ifdef QSA_DEBUG
+  if (v < lo || v > hi) debug_flag(bit);
+#else
+  (void)bit;
+#endif
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
 // ---------------------------------------------------------------- paging
 
 struct PageMap {
@@ -85,18 +138,23 @@ struct PageMap {
   int32_t max_pages;
   int32_t page_shift;     // log2(page_size)
   int32_t blk_shift;      // log2(tokens per pooled block)
+  int64_t n_pages;        // pages in the pool (debug builds check page ids)
+  // physical page of logical page i of sequence seq
+  __device__ __forceinline__ int32_t page(int seq, int i) const {
+    return checked_page(table[(int64_t)seq * max_pages + i], n_pages);
+  }
   __device__ __forceinline__ int64_t token_slot(int seq, int tok) const {
     // global token-row index: page * page_size + slot
-    int32_t page = table[(int64_t)seq * max_pages + (tok >> page_shift)];
-    return ((int64_t)page << page_shift) + (tok & ((1 << page_shift) - 1));
+    int32_t pg = page(seq, tok >> page_shift);
+    return ((int64_t)pg << page_shift) + (tok & ((1 << page_shift) - 1));
   }
   // log2(pooled blocks per page)
   __device__ __forceinline__ int bpp_shift() const { return page_shift - blk_shift; }
   // row index of block b of sequence seq in the pooled-key array
   __device__ __forceinline__ int64_t block_slot(int seq, int b) const {
     const int sh = bpp_shift();
-    int32_t page = table[(int64_t)seq * max_pages + (b >> sh)];
-    return ((int64_t)page << sh) + (b & ((1 << sh) - 1));
+    int32_t pg = page(seq, b >> sh);
+    return ((int64_t)pg << sh) + (b & ((1 << sh) - 1));
   }
 };
 

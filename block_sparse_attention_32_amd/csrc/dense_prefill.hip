@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(kFThreads) dense_flash_kernel(AttnArgs a, int 
   for (int i = threadIdx.x; i < TR; i += blockDim.x) {
     const int row = r0 + i;
     const bool ok = row < n_rows;
-    ft.seq[i] = ok ? min(max(a.seq_id[row], 0), a.n_seqs - 1) : -1;
-    ft.pos[i] = ok ? min(max(a.pos[row], 0), a.max_pos) : -1;
+    ft.seq[i] = ok ? clamp_flag(a.seq_id[row], 0, a.n_seqs - 1, QSA_DEBUG_BAD_ROW) : -1;
+    ft.pos[i] = ok ? clamp_flag(a.pos[row], 0, a.max_pos, QSA_DEBUG_BAD_ROW) : -1;
     ft.done[i] = ok ? 0 : 1;
   }
   __syncthreads();

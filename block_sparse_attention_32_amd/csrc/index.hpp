@@ -66,12 +66,10 @@ struct IdxArgs {
   int n_seqs;            // seq_id is clamped to [0, n_seqs)
   int max_pos;           // pos is clamped to [0, max_pos]
   __device__ __forceinline__ int seq_of(int row) const {
-    int s = seq_id[row];
-    return s < 0 ? 0 : (s >= n_seqs ? n_seqs - 1 : s);
+    return clamp_flag(seq_id[row], 0, n_seqs - 1, QSA_DEBUG_BAD_ROW);
   }
   __device__ __forceinline__ int pos_of(int row) const {
-    int t = pos[row];
-    return t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    return clamp_flag(pos[row], 0, max_pos, QSA_DEBUG_BAD_ROW);
   }
 };
 

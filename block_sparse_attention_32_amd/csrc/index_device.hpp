@@ -141,8 +141,7 @@ __device__ __forceinline__ void stage_pages(const PageMap& pm, int seq, int c0, 
   const int first = c0 >> pm.bpp_shift();
   const int last_b = min(c0 + kChunk, n) - 1;
   const int cnt = (last_b >> pm.bpp_shift()) - first + 1;
-  const int32_t* row = pm.table + (int64_t)seq * pm.max_pages + first;
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) pages[i] = row[i];
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) pages[i] = pm.page(seq, first + i);
   __syncthreads();
 }
 

@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
           const int b = b0 + vi / Gm::VPR, part = vi % Gm::VPR;
           v[j] = u32x4_t{0u, 0u, 0u, 0u};
           if (b < n_hi) {
-            const int32_t pg = a.idx.pm.table[tbase + (b >> bpp_sh)];
+            const int32_t pg = checked_page(a.idx.pm.table[tbase + (b >> bpp_sh)], a.idx.pm.n_pages);
             const int64_t slot = ((int64_t)pg << bpp_sh) + (b & ((1 << bpp_sh) - 1));
             v[j] = *reinterpret_cast<const u32x4_t*>(kbar + slot * DI + part * 8);
           }

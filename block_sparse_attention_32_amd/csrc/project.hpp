@@ -20,12 +20,10 @@ struct ProjArgs {
   bf16_t* kidx;          // paged cache rows [slot][nk]
   float* w;              // [T][Hi]
   __device__ __forceinline__ int seq_of(int row) const {
-    const int s = seq_id[row];
-    return s < 0 ? 0 : (s >= n_seqs ? n_seqs - 1 : s);
+    return clamp_flag(seq_id[row], 0, n_seqs - 1, QSA_DEBUG_BAD_ROW);
   }
   __device__ __forceinline__ int pos_of(int row) const {
-    const int t = pos[row];
-    return t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    return clamp_flag(pos[row], 0, max_pos, QSA_DEBUG_BAD_ROW);
   }
 };
 

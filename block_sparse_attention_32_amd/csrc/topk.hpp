@@ -49,6 +49,7 @@ struct RowKeys {
   const T* qrow;     // the row's q_idx, [hi][DI]
   const float* wrow; // the row's head weights
   const int32_t* pages;  // the sequence's row of the page table
+  int64_t n_pages;       // pages in the pool
   int hi, bsh;           // heads; log2(blocks per page)
   // (56 bytes: small enough to travel in registers to the out-of-line
   // selection routines)
@@ -57,12 +58,14 @@ struct RowKeys {
       : given(g), stored(st), kbar(static_cast<const T*>(t.idx.kbar)),
         qrow(static_cast<const T*>(t.idx.q_idx) + (int64_t)row * t.idx.hi * DI),
         wrow(t.idx.w + (int64_t)row * t.idx.hi),
-        pages(t.idx.pm.table + (int64_t)sq * t.idx.pm.max_pages), hi(t.idx.hi),
+        pages(t.idx.pm.table + (int64_t)sq * t.idx.pm.max_pages), n_pages(t.idx.pm.n_pages),
+        hi(t.idx.hi),
         bsh(t.idx.pm.bpp_shift()) {}
   __device__ __forceinline__ uint32_t operator()(int e) const {
     if (given != nullptr) return score_key(given[e]);
     if (stored != nullptr) return stored[e];
-    const int64_t slot = ((int64_t)pages[e >> bsh] << bsh) + (e & ((1 << bsh) - 1));
+    const int64_t slot =
+        ((int64_t)checked_page(pages[e >> bsh], n_pages) << bsh) + (e & ((1 << bsh) - 1));
     const T* p = kbar + slot * DI;
     float s = 0.0f;
     for (int h = 0; h < hi; ++h) {

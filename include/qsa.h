@@ -273,6 +273,24 @@ size_t qsa_workspace_size(int32_t op, const qsa_cache *c,
                           const qsa_queries *qm, int32_t n_q_heads,
                           int32_t top_k);
 
+/* Debug builds (libqsa_debug.so, compiled with -DQSA_DEBUG): the kernels
+ * check the device data the host cannot -- page ids read from block_table,
+ * sequence ids and positions, selection lengths and selected ids -- and
+ * replace an out-of-range value with one that keeps every access inside
+ * the caller's buffers (page 0; the clamped id or position; the selection
+ * entry skipped), recording what they saw in these bits: */
+#define QSA_DEBUG_BAD_PAGE 1u /* a block_table entry outside [0, n_pages)         */
+#define QSA_DEBUG_BAD_ROW  2u /* seq_id outside [0, n_seqs) or pos outside
+                                 [0, max_pos]                                      */
+#define QSA_DEBUG_BAD_SEL  4u /* n_sel outside [0, top_k], a row's selected id
+                                 outside [0, pos/B), or sel_of outside [0, T)     */
+/* qsa_debug_take: waits for the device (hipDeviceSynchronize), ORs the bits
+ * recorded since the last call into *flags (host) and clears them.  For
+ * debugging only: it synchronises.  The release build (libqsa.so) records
+ * nothing: *flags = 0 and QSA_ERR_UNSUPPORTED.  QSA_ERR_INVALID_ARG for a
+ * null flags. */
+qsa_status qsa_debug_take(uint32_t *flags);
+
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -167,3 +167,14 @@ def test_top_k_limit(libqsa):
     at = libqsa.qsa_attn_decode
     wsa = libqsa.qsa_workspace_size(B.QSA_OP_ATTN_DECODE, R(c), R(q), 16, 2048)
     assert at(R(c), R(q), 8, 16, 8, 8, 2049, f(0.1), 8, 8, wsa, None) == -1
+
+
+def test_release_build_has_no_debug_checks(libqsa):
+    """qsa_debug_take reports QSA_ERR_UNSUPPORTED (and zero flags) on the
+    release build, and rejects a null flags pointer."""
+    f = ctypes.c_uint32(7)
+    want = -2 if "debug" not in os.path.basename(B.LIB_PATH) else 0
+    assert libqsa.qsa_debug_take(ctypes.byref(f)) == want
+    assert f.value == 0
+    assert libqsa.qsa_debug_take(None) == -1
+

@@ -572,25 +572,53 @@ def test_e2e_mtp_step(gpu, n_ctx):
         assert err <= TOL[wl.dtype], f"row {i} t={pos[i]} err={err}"
 
 
+def _assert_needles_selected(pb, st, rows):
+    """Every planted needle a row can see (block id below its own block) is
+    among its selected blocks (the depth-recall property the pages report
+    for a QSA patch)."""
+    _, sel, n = sel_rows(st.sel, st.n_sel)
+    for i in rows:
+        b_own = pb.pos_list[i] // pb.wl.block
+        want = {b for b in pb.cache.needles[pb.seq_id_list[i]] if b < b_own}
+        missing = want - set(sel[i, : n[i]].tolist())
+        assert not missing, f"row {i} t={pb.pos_list[i]}: needles {sorted(missing)} not selected"
+
+
 def test_e2e_prefill_8k_at_128k(gpu):
+    """The 8,192-row chunk at 128K: every 8th row and the last eight rows
+    (both ends, every t mod 4) against the oracle, selection bit for bit and
+    outputs within tolerance; every needle selected by every checked row."""
     _say("e2e prefill_8k_at_128k")
     wl = WL["prefill_8k_at_128k"]
     pb = Problem(wl, gpu)
     pb.pool_all()
     T = len(pb.pos_list)
-    check = sorted(set([0, 1, 2, 3, T - 1, T - 2] + list(range(5, T, 181))))
-    _e2e(pb, check)
+    check = sorted(set(list(range(0, T, 8)) + list(range(1, 4)) + list(range(T - 8, T))))
+    assert len(check) >= 1024
+    st, worst = _e2e(pb, check)
+    _assert_needles_selected(pb, st, check)
+    _say(f"  {len(check)} rows, max err {worst:.3g}")
 
 
-@pytest.mark.parametrize("chunk", [0, 31])
+@pytest.mark.parametrize("chunk", [0, 1, 16, 31])
 def test_e2e_prefill_1m_chunk(gpu, chunk):
+    """Chunks of the 1M prefill at full size: the first and last eight rows
+    of the chunk (every t mod 4 at both edges), rows up to t = 2,051 in the
+    first chunk (selection covering the whole context), and rows spread over
+    the chunk; selection bit for bit, outputs within tolerance, needles
+    selected."""
     _say(f"e2e prefill_1m chunk {chunk}")
     wl = WL["prefill_1m"]
     pb = Problem(wl, gpu, chunk_index=chunk)
     pb.pool_all()
     T = len(pb.pos_list)
-    check = sorted(set([0, 1, 2, 3, 2047, 2048, 2051, T - 1] + list(range(11, T, 1531))))
-    _e2e(pb, check)
+    check = list(range(8)) + list(range(T - 8, T)) + list(range(13, T, 1367))
+    if chunk == 0:
+        check += [2046, 2047, 2048, 2049, 2050, 2051, 2052]
+    check = sorted(set(check))
+    st, worst = _e2e(pb, check)
+    _assert_needles_selected(pb, st, check)
+    _say(f"  {len(check)} rows, max err {worst:.3g}")
 
 
 def test_chunked_prefill_overlap_matches_serial(gpu):

@@ -74,15 +74,30 @@ def test_pool_newest_decode_workloads(gpu, name):
     _check(pb, sel, n_sel, pooled)
 
 
-@pytest.mark.parametrize("rows", [5, 80], ids=["chunked", "matrix-core"])
-def test_pool_newest_positions(gpu, rows):
+_BASE = [0, 3, 4, 5, 2047, 2048, 2049, 2052, 9000, 9001, 19996, 19997, 19998, 19999, 20000]
+_POSITIONS = {
+    # few rows, none past the budget (every row takes all its candidates)
+    "chunked": sorted(_BASE[:5]),
+    # few rows of one sequence, all past the budget: the chunked top-k
+    # pools each row's newest block in the workgroup that scores it while
+    # the other rows' workgroups score that block too (it is pooled already,
+    # as the call requires, and is rewritten with identical values); only
+    # the newest block of the furthest rows (20000, 19999 share none) is
+    # poisoned first
+    "chunked-long": [2052, 3001, 5000, 9001, 19999, 19999, 20000],
+    # 80 rows: the matrix-core path
+    "matrix-core": sorted((_BASE * 6)[:80]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_POSITIONS))
+def test_pool_newest_positions(gpu, case):
     """Rows of one sequence at positions around block edges, including
     positions with no complete block (pos < 4) and rows sharing their
     newest block; 80 rows take the matrix-core path."""
-    _say(f"pool newest positions rows={rows}")
+    _say(f"pool newest positions {case}")
     wl = WL["decode_8x32k"].replace(n_ctx=20000, n_seqs=1, seed=91)
-    base = [0, 3, 4, 5, 2047, 2048, 2049, 2052, 9000, 9001, 19996, 19997, 19998, 19999, 20000]
-    pos = sorted((base * 6)[:rows])
+    pos = _POSITIONS[case]
     pb = Problem(wl, gpu, [0] * len(pos), pos)
     pb.pool_all()
     pooled = _poison_newest(pb)
