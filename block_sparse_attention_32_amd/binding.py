@@ -35,7 +35,9 @@ SYMBOLS = (
     "qsa_attn_decode_shared", "qsa_attn_prefill", "qsa_dense_attn_decode",
     "qsa_dense_attn_prefill",
     "qsa_workspace_size", "qsa_status_string", "qsa_version", "qsa_debug_take",
+    "qsa_attn_decode_noalloc",
 )
+QSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 QSA_DEBUG_BAD_PAGE, QSA_DEBUG_BAD_ROW, QSA_DEBUG_BAD_SEL = 1, 2, 4
 DEBUG_LIB_PATH = os.path.join(_PKG, "libqsa_debug.so")
 
@@ -94,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "qsa_dense_attn_prefill": [P, P, P, I32, F, P, P, SZ, P],
             "qsa_workspace_size": [I32, P, P, I32, I32],
             "qsa_debug_take": [P],
+            "qsa_attn_decode_noalloc": [P, P, P, I32, P, P, I32, F, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -295,6 +298,16 @@ def qsa_index_project(cache, queries, x, wq, wk, ww, q_idx, w, kidx_out=None, st
 
 def qsa_attn_decode(cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream=None):
     _attn("qsa_attn_decode", cache, queries, q, sel, n_sel, top_k, scale, out, ws, stream)
+
+
+def qsa_attn_decode_noalloc(cache, queries, q, sel, n_sel, top_k, scale, out, stream=None):
+    """qsa_attn_decode on the library's static scratch (no workspace)."""
+    _check(q, "q", cache.dtype, cache.device)
+    _check(out, "out", cache.dtype, cache.device)
+    _check(sel, "sel", torch.int32, cache.device)
+    _check(n_sel, "n_sel", torch.int32, cache.device)
+    _call("qsa_attn_decode_noalloc", cache.ref, queries.ref, _ptr(q), int(q.shape[1]), _ptr(sel),
+          _ptr(n_sel), int(top_k), ctypes.c_float(scale), _ptr(out), _stream(stream))
 
 
 def qsa_attn_decode_shared(cache, queries, q, sel, n_sel, sel_of, top_k, scale, out, ws,

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "attention.hpp"
@@ -203,10 +204,46 @@ AttnPlan attn_plan(int op, const qsa_cache* c, const qsa_queries* qm, int hq, in
   return p;
 }
 
+// ------------------------------------------------------------- static scratch
+
+// The workspace of qsa_attn_decode_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: each device's address is looked up once,
+// with that device current, and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* scratch_addr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+std::once_flag scratch_once[kMaxDevices];
+
+// the current device's copy of `scratch`
+qsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_addr[dev] = p;
+  });
+  if (scratch_err[dev] != hipSuccess || scratch_addr[dev] == nullptr) return QSA_ERR_HIP;
+  *out = scratch_addr[dev];
+  return QSA_OK;
+}
+
+// zeroes n 32-bit words (a kernel, not a memset, so that graph capture
+// records a kernel node)
+__global__ void __launch_bounds__(256) clear_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, const void* q,
                             int32_t hq, const int32_t* sel, const int32_t* n_sel,
                             int32_t top_k, float scale, void* out, void* ws, size_t ws_bytes,
-                            void* stream, const int32_t* sel_of = nullptr) {
+                            void* stream, const int32_t* sel_of = nullptr,
+                            bool use_scratch = false) {
   qsa_status st = check_cache(c);
   if (st != QSA_OK) return st;
   if ((st = check_queries(c, qm)) != QSA_OK) return st;
@@ -221,6 +258,22 @@ qsa_status attention_common(int op, const qsa_cache* c, const qsa_queries* qm, c
   if (c->k == nullptr || c->v == nullptr) return QSA_ERR_INVALID_ARG;
   const AttnPlan p = attn_plan(op, c, qm, hq, top_k);
   if (p.tile < 4) return QSA_ERR_UNSUPPORTED;
+  if (use_scratch) {
+    // the static scratch replaces the caller's workspace
+    if (p.total > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_WORKSPACE;
+    if (qm->n_rows == 0) return QSA_OK;
+    if ((st = scratch_for_current_device(&ws)) != QSA_OK) return st;
+    ws_bytes = QSA_NOALLOC_SCRATCH_BYTES;
+    if (p.splits > 1) {
+      // the arrival counters start at zero (the array keeps the last
+      // call's contents)
+      hipLaunchKernelGGL(clear_words, dim3((unsigned)((qm->n_rows + 255) / 256)), dim3(256), 0,
+                         as_stream(stream),
+                         reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_cnt),
+                         qm->n_rows);
+      if ((st = launched()) != QSA_OK) return st;
+    }
+  }
   if (p.total > 0 && (ws == nullptr || ws_bytes < p.total)) return QSA_ERR_WORKSPACE;
   if (qm->n_rows == 0) return QSA_OK;
   AttnArgs a;
@@ -434,6 +487,13 @@ qsa_status qsa_attn_decode(const qsa_cache* c, const qsa_queries* qm, const void
                            void* stream) {
   return attention_common(QSA_OP_ATTN_DECODE, c, qm, q, n_q_heads, sel, n_sel, top_k, scale,
                           out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_attn_decode_noalloc(const qsa_cache* c, const qsa_queries* qm, const void* q,
+                                   int32_t n_q_heads, const int32_t* sel, const int32_t* n_sel,
+                                   int32_t top_k, float scale, void* out, void* stream) {
+  return attention_common(QSA_OP_ATTN_DECODE, c, qm, q, n_q_heads, sel, n_sel, top_k, scale,
+                          out, nullptr, 0, stream, nullptr, true);
 }
 
 qsa_status qsa_index_project(const qsa_cache* c, const qsa_queries* qm, const void* x,

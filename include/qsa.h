@@ -213,6 +213,26 @@ qsa_status qsa_attn_prefill(const qsa_cache *c, const qsa_queries *qm,
                             int32_t top_k, float scale, void *out, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* qsa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation): computes exactly what qsa_attn_decode computes, with
+ * the same kernels, using a static scratch array of
+ * QSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  It calls no hipMalloc/hipFree.  Arguments,
+ * layouts and errors as qsa_attn_decode, plus QSA_ERR_WORKSPACE when the
+ * call's plan needs more than the scratch holds (never for head_dim <= 128
+ * and n_q_heads <= 16 on the matrix-core path, whose workgroups are capped
+ * at 1,024), QSA_ERR_HIP when the scratch's address cannot be obtained.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from different threads) race and must be
+ * serialised by the caller. */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+qsa_status qsa_attn_decode_noalloc(const qsa_cache *c, const qsa_queries *qm,
+                                   const void *q, int32_t n_q_heads,
+                                   const int32_t *sel, const int32_t *n_sel,
+                                   int32_t top_k, float scale, void *out,
+                                   void *stream);
+
 /* Indexer projections (the input side of the learned indexer the
  * keieiax.jp glossary describes in section 4トークンずつまとめて; the pages
  * print no projection, so these are plain linear maps, no bias).  For every

@@ -178,3 +178,16 @@ def test_release_build_has_no_debug_checks(libqsa):
     assert f.value == 0
     assert libqsa.qsa_debug_take(None) == -1
 
+
+def test_noalloc_decode_validates_before_launch(libqsa):
+    """The no-allocation decode rejects invalid arguments on the host, like
+    qsa_attn_decode (no GPU work happens on these paths)."""
+    c, q = _cache(), _rows()
+    f = libqsa.qsa_attn_decode_noalloc
+    F = ctypes.c_float
+    assert f(None, R(q), 8, 16, 8, 8, 512, F(0.1), 8, None) == -1          # no cache
+    assert f(R(c), R(q), None, 16, 8, 8, 512, F(0.1), 8, None) == -1      # no q
+    assert f(R(c), R(q), 8, 16, None, 8, 512, F(0.1), 8, None) == -1      # no sel
+    assert f(R(c), R(q), 8, 16, 8, 8, 0, F(0.1), 8, None) == -1           # top_k < 1
+    assert f(R(c), R(q), 8, 15, 8, 8, 512, F(0.1), 8, None) == -1         # Hq % Hkv
+    assert f(R(c), R(q), 8, 16, 8, 8, 512, F(0.0), 8, None) == -1         # scale <= 0
