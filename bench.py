@@ -80,10 +80,12 @@ class Timer:
 
 # ------------------------------------------------------------------ decode
 
-def run_decode(wl, steps: int, warmup: int, dev, dense: bool = True):
+def run_decode(wl, steps: int, warmup: int, dev, dense: bool = True, graph: bool = False):
     """One step = pool the newest complete block, fused indexer scores and
     exact top-k (one call: the block is pooled by the top-k workgroup that
-    scores it) -> split-K sparse attention, for one query row per sequence."""
+    scores it) -> split-K sparse attention, for one query row per sequence.
+    With graph the step's two calls are captured once in a HIP graph and the
+    timed steps replay it (the per-call event times stay eager calls)."""
     from block_sparse_attention_32_amd import pipeline as P
     log(f"[bench] drawing {wl.name} cache on {dev}")
     cache = W.make_cache(wl, device=dev)
@@ -96,10 +98,25 @@ def run_decode(wl, steps: int, warmup: int, dev, dense: bool = True):
     P.pool_all(cv, wl.n_seqs, n_blocks, dev)               # set-up, untimed
     step = P.QsaStep(cv, rows, qs.q, qs.q_idx, qs.w, wl.top_k, wl.scale, "decode")
 
-    def one(timer=None):
+    def eager(timer=None):
         call = timer.wrap if timer else (lambda name, fn, *a, **k: fn(*a, **k))
         call("topk", step.select_pooling_newest)   # pools, scores and selects
         call("attn", step.attend)
+
+    one = eager
+    if graph:
+        eager()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            eager()
+        torch.cuda.synchronize()
+
+        def one(timer=None):
+            if timer is not None:
+                eager(timer)
+            else:
+                g.replay()
 
     wall, kern = _timed(one, steps, warmup)
     n_sel = step.n_sel.cpu().numpy()
@@ -123,7 +140,7 @@ def run_decode(wl, steps: int, warmup: int, dev, dense: bool = True):
         dense_ms = _dense_time(ds.run, max(5, steps // 4))
     ctx = {"rows": rows.n_rows, "cache": cache, "qs": qs, "pos": pos, "launches": 1,
            "dense_ms": dense_ms, "dense_note": "split-K flash-decode over all tokens",
-           "step": step}
+           "step": step, "graph": graph}
     return wall, kern, work, ctx
 
 
@@ -760,7 +777,8 @@ def measure(wl, steps, warmup, args, dev, cpu=True, dense=True, memory=True):
     elif wl.mode == "mtp":
         wall, timer, work, ctx = run_mtp(wl, steps, warmup, dev, dense=dense)
     elif decode:
-        wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=dense)
+        wall, timer, work, ctx = run_decode(wl, steps, warmup, dev, dense=dense,
+                                            graph=args.graph)
     else:
         wall, timer, work, ctx = run_prefill(wl, steps, warmup, dev, dense=dense,
                                              overlap=args.overlap)
@@ -778,7 +796,8 @@ def measure(wl, steps, warmup, args, dev, cpu=True, dense=True, memory=True):
            "chunk": (wl.chunk or wl.n_new) if not decode else None,
            "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "idx_heads": wl.hi, "idx_dim": wl.di,
            "top_k": wl.top_k, "block_tokens": wl.block, "page_size": wl.page_size,
-           "direction_scale": wl.direction_scale, "parallelism": "single-gpu"}
+           "direction_scale": wl.direction_scale, "parallelism": "single-gpu",
+           "hip_graph": bool(ctx.get("graph", False))}
     step_ms = timer.step_ms
     rec = {
         "value": round(value, 1), "unit": "query-tokens/s", "steps": steps, "warmup": warmup,
@@ -853,6 +872,8 @@ def main():
                          f"{HEADLINE})")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-GQA comparison")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: replay the step from a HIP graph (captured once)")
     ap.add_argument("--overlap", action="store_true",
                     help="prefill: run each chunk's attention on a second stream, beside the "
                          "next chunk's selection (per-kernel times then overlap)")
