@@ -83,70 +83,94 @@ __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint
 __device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 // Merge of a row's split partials, run by the last split workgroup after its
-// acquire.  Each thread keeps a running (M, L, O[ND]) for its head and dims;
-// the partials of the next kMergeBatch splits are loaded while the current
-// batch is folded in.
+// acquire.  Each thread keeps a running (M, L, O[ND]) for its head and dims.
+// Per batch of kMergeBatch splits, lane j of a head's LPH threads loads the
+// (m, l) pair of split j once and the group shares it by lane shuffles,
+// each thread loads its ND floats of every split in one or two 16-byte
+// loads, and the next batch's loads are in flight while the current batch
+// is folded in.
 template <int D, int NT>
 __device__ void merge_splits(const AttnArgs& a, int row, bf16_t* orow) {
   constexpr int ND = MergeLane<D, NT>::ND;
-  constexpr int NV = ND / 2;  // 8-byte loads per split
-  // splits whose partials are in flight together
-  constexpr int kMergeBatch = ND >= 4 ? 64 / ND : 16;
+  constexpr int LPH = MergeLane<D, NT>::LPH;
+  constexpr int NV = ND / 4 > 0 ? ND / 4 : 1;  // 16-byte loads per split (8-byte if ND == 2)
+  constexpr int kMergeBatch = 16;
+  static_assert(LPH >= kMergeBatch, "a head's threads hold one batch of (m, l) pairs");
+  static_assert(ND == 2 || ND % 4 == 0, "dims per thread");
   const MergeLane<D, NT> ml(a.hq);
-  if (!ml.on) return;
+  if (!ml.on) return;  // whole head groups leave together
   const int S = a.n_splits, hq = a.hq;
+  const int j = (int)threadIdx.x % LPH;                  // lane within the head's group
+  const int gbase = (lane_id() / LPH) * LPH;             // the group's first lane
   const int64_t rb = (int64_t)row * S * hq;
   const uint64_t* pml = reinterpret_cast<const uint64_t*>(a.part_ml) + rb + ml.h;
-  const uint64_t* pacc = reinterpret_cast<const uint64_t*>(a.part_acc + (rb + ml.h) * D + ml.d0);
-  const int64_t acc_step = (int64_t)hq * D / 2;  // uint64 per split
+  const float* pacc = a.part_acc + (rb + ml.h) * D + ml.d0;
+  const int64_t acc_step = (int64_t)hq * D;  // floats per split
   float M = -INFINITY, L = 0.0f, O[ND];
 #pragma unroll
-  for (int j = 0; j < ND; ++j) O[j] = 0.0f;
-  uint64_t cm[kMergeBatch], cv[kMergeBatch][NV];
+  for (int q = 0; q < ND; ++q) O[q] = 0.0f;
+  uint64_t cm;              // (m, l) of split s0 + j of the batch
+  float cv[kMergeBatch][ND];
   auto load = [&](int s0) {
+    cm = (j < kMergeBatch && s0 + j < S) ? pml[(int64_t)(s0 + j) * hq] : pack2(-INFINITY, 0.0f);
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const bool ok = s0 + u < S;
-      cm[u] = ok ? pml[(int64_t)(s0 + u) * hq] : pack2(-INFINITY, 0.0f);
+      const float* src = pacc + (int64_t)(s0 + u) * acc_step;
+      if constexpr (ND == 2) {
+        const float2 v = ok ? *reinterpret_cast<const float2*>(src) : make_float2(0.f, 0.f);
+        cv[u][0] = v.x;
+        cv[u][1] = v.y;
+      } else {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) cv[u][j] = ok ? pacc[(s0 + u) * acc_step + j] : 0ull;
+        for (int q = 0; q < NV; ++q) {
+          const float4 v = ok ? *reinterpret_cast<const float4*>(src + 4 * q)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+          cv[u][4 * q] = v.x;
+          cv[u][4 * q + 1] = v.y;
+          cv[u][4 * q + 2] = v.z;
+          cv[u][4 * q + 3] = v.w;
+        }
+      }
     }
   };
   load(0);
   for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
-    uint64_t bm[kMergeBatch], bv[kMergeBatch][NV];
+    const uint64_t bm_own = cm;
+    float bv[kMergeBatch][ND];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < ND; ++q) bv[u][q] = cv[u][q];
+    if (s0 + kMergeBatch < S) load(s0 + kMergeBatch);
+    // the batch's (m, l) pairs, from the lanes that loaded them
+    float bm[kMergeBatch], bl[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      bm[u] = cm[u];
-#pragma unroll
-      for (int j = 0; j < NV; ++j) bv[u][j] = cv[u][j];
+      bm[u] = __shfl(lo_f(bm_own), gbase + u);
+      bl[u] = __shfl(hi_f(bm_own), gbase + u);
     }
-    if (s0 + kMergeBatch < S) load(s0 + kMergeBatch);
     float Mc = M;
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) Mc = fmaxf(Mc, lo_f(bm[u]));
+    for (int u = 0; u < kMergeBatch; ++u) Mc = fmaxf(Mc, bm[u]);
     if (Mc == -INFINITY) continue;  // nothing attended yet
     const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
     L *= rs;
 #pragma unroll
-    for (int j = 0; j < ND; ++j) O[j] *= rs;
+    for (int q = 0; q < ND; ++q) O[q] *= rs;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float mu = lo_f(bm[u]);
-      const float f = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - Mc);
-      L = fmaf(hi_f(bm[u]), f, L);
+      const float f = (bm[u] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(bm[u] - Mc);
+      L = fmaf(bl[u], f, L);
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        O[2 * j] = fmaf(lo_f(bv[u][j]), f, O[2 * j]);
-        O[2 * j + 1] = fmaf(hi_f(bv[u][j]), f, O[2 * j + 1]);
-      }
+      for (int q = 0; q < ND; ++q) O[q] = fmaf(bv[u][q], f, O[q]);
     }
     M = Mc;
   }
   const float inv = 1.0f / L;
   bf16_t* o = orow + ml.h * D + ml.d0;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) o[j] = f32_to_bf16(O[j] * inv);
+  for (int q = 0; q < ND; ++q) o[q] = f32_to_bf16(O[q] * inv);
 }
 
 // K/V row offsets are kept as 32-bit byte offsets while both arrays are
