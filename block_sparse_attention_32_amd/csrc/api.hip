@@ -27,7 +27,6 @@ void debug_register(uint32_t (*take)()) { debug_units().push_back(take); }
 namespace {
 
 constexpr int kRowBatch = 4096;              // top-k rows per launch pair
-constexpr size_t kMaterializeBytes = 1u << 30;  // long rows keep scores below this
 constexpr int kTargetSplitWgs = 256;         // decode (generic kernel): workgroups over all rows
 constexpr int kMinEntriesPerSplit = 8;
 constexpr int64_t kMaxSplitWgs = 1024;       // decode (MFMA kernel): workgroup cap
@@ -91,7 +90,7 @@ qsa_status launched() {
 // ------------------------------------------------------------- top-k plan
 
 struct TopkPlan {
-  int rows, w_max, materialize, ucap;
+  int rows, w_max, ucap;
   int64_t ws_ld;
   size_t off_ctr, off_tops, off_nxt, off_scores, total;
 };
@@ -107,8 +106,9 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
   p.rows = qm->n_rows < kPRowBatch ? qm->n_rows : kPRowBatch;
   if (p.rows < 1) p.rows = 1;
   const int tiles = (p.rows + kPQT - 1) / kPQT;
-  // enough workgroups for four per CU
-  int sp = (1024 + tiles - 1) / tiles;
+  // enough workgroups for two per CU (the scoring kernel's 128 VGPRs per
+  // lane allow two of its 8-wave workgroups on a CU)
+  int sp = (512 + tiles - 1) / tiles;
   p.splits = sp < 1 ? 1 : (sp > kPMaxSplits ? kPMaxSplits : sp);
   size_t o = 0;
   p.off_uni = o;     o = align256(o + (size_t)p.rows * kPUnion * 4);
@@ -132,9 +132,10 @@ TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm, int top_k) {
   const int batch = kRowBatch * kUnionCap / p.ucap;
   p.rows = qm->n_rows < batch ? qm->n_rows : batch;
   if (p.rows < 1) p.rows = 1;
+  // rows of at most kDirectCap candidates keep their keys for the exact
+  // select; longer rows keep none (a rare rescan recomputes its keys)
   const int64_t full = (int64_t)p.w_max * kChunk;
-  p.materialize = (size_t)p.rows * (size_t)full * 4 <= kMaterializeBytes;
-  p.ws_ld = p.materialize ? full : (full < kDirectCap ? full : kDirectCap);
+  p.ws_ld = full < kDirectCap ? full : kDirectCap;
   size_t o = 0;
   p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
   p.off_tops = o;   o = align256(o + (size_t)p.rows * p.ucap * 8);
@@ -448,7 +449,6 @@ static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const f
   t.sel = sel;
   t.n_sel = n_sel;
   t.w_max = p.w_max;
-  t.materialize = p.materialize;
   t.ws_scores = reinterpret_cast<float*>(base + p.off_scores);
   t.ws_ld = p.ws_ld;
   t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);

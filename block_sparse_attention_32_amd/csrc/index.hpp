@@ -82,8 +82,7 @@ struct TopkArgs {
   int32_t* sel;
   int32_t* n_sel;
   int w_max;             // chunks of the longest row
-  int materialize;       // long rows keep their scores in ws_scores
-  float* ws_scores;      // [R][ws_ld]
+  float* ws_scores;      // [R][ws_ld] keys of rows of at most kDirectCap candidates
   int64_t ws_ld;
   uint32_t* cnt;         // [R] arrival counters
   int ucap;              // union capacity per row (union_cap)

@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   if (c >= p.W) return;
   const int c0 = c * kChunk;
   uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
-  const bool keep = !given && (direct || t.materialize);
+  const bool keep = !given && direct;  // long rows publish tops only
   if (given) {
     for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
       keys[i] = (c0 + i < p.n) ? score_key(given[c0 + i]) : 0u;
@@ -430,9 +430,7 @@ __global__ void __launch_bounds__(256) topk_tail_kernel(TopkArgs t) {
   if (p.n <= t.top_k || p.n <= kDirectCap) return;  // done by topk_kernel
   int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
   const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
-  uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
-  const bool keep = !given && t.materialize;
-  const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+  const RowKeys<T, DI> src(given, nullptr, t, row, p.seq);
   const uint64_t* tops = t.tops + (int64_t)rl * kUnionCapL;
   const uint32_t* nxt = t.nxt + (int64_t)rl * t.w_max * kSelWaves;
   const int nw = p.W * kSelWaves;
