@@ -98,7 +98,8 @@ struct TopkPlan {
 // MFMA prefill indexer plan (fused mode, many rows)
 struct PidxPlan {
   int rows, splits;
-  size_t off_uni, off_tau, off_tstride, off_rstride, off_surv, off_scnt, off_done, total;
+  size_t off_uni, off_tau, off_tstride, off_rstride, off_surv, off_scnt, off_done, off_fbcnt,
+      off_fblist, total;
 };
 
 PidxPlan pidx_plan(const qsa_queries* qm) {
@@ -118,6 +119,8 @@ PidxPlan pidx_plan(const qsa_queries* qm) {
   p.off_surv = o;    o = align256(o + (size_t)p.rows * kPSurvCap * 8);
   p.off_scnt = o;    o = align256(o + (size_t)p.rows * p.splits * 4);
   p.off_done = o;    o = align256(o + (size_t)p.rows * 4);
+  p.off_fbcnt = o;   o = align256(o + 2 * 4);
+  p.off_fblist = o;  o = align256(o + (size_t)p.rows * 4);
   p.total = o;
   return p;
 }
@@ -417,6 +420,8 @@ static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const f
     a.surv = reinterpret_cast<uint64_t*>(base + pp.off_surv);
     a.surv_cnt = reinterpret_cast<uint32_t*>(base + pp.off_scnt);
     a.done = reinterpret_cast<uint32_t*>(base + pp.off_done);
+    a.fb_cnt = reinterpret_cast<uint32_t*>(base + pp.off_fbcnt);
+    a.fb_list = reinterpret_cast<int32_t*>(base + pp.off_fblist);
     a.sel = sel;
     a.n_sel = n_sel;
     if (pool_newest) {

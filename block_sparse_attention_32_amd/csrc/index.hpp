@@ -115,9 +115,12 @@ struct PIdxArgs {
   uint64_t* surv;            // [rows][splits][kPSurvCap / splits] (block << 32 | score bits)
   uint32_t* surv_cnt;        // [rows][splits]
   uint32_t* done;            // [rows] set by the one-wave select, cleared by the fallback
+  uint32_t* fb_cnt;          // [2] rows listed for the exact fallback; its arrival counter
+  int32_t* fb_list;          // [rows] those rows (batch-local index)
   int32_t* sel;
   int32_t* n_sel;
 };
+constexpr int kPFallbackWgs = 64;  // workgroups of the fallback kernel (they loop over its list)
 
 bool pidx_supported(int dtype, int di, int hi);
 void run_pidx(const PIdxArgs& a, int di, hipStream_t st);

@@ -27,11 +27,13 @@
 //       score bits) appended per (row, split) in block order;
 //   P4  per row: survivors gathered in block order -> exact radix select and
 //       ordered emission (select.hpp); a row whose survivors overflowed its
-//       slots, or number fewer than k, falls back to an exact select over
-//       recomputed keys.
+//       slots, or number fewer than k, is listed for the exact fallback:
+//       one streaming pass over its pooled keys keeps every key at or above
+//       a guaranteed lower bound of the k-th (from its union), then the same
+//       exact select.
 #include <type_traits>
 
-#include "index.hpp"
+#include "index_device.hpp"
 #include "select.hpp"
 
 namespace qsa {
@@ -511,14 +513,129 @@ __global__ void __launch_bounds__(256) pidx_select_kernel(PIdxArgs a) {
     emit_regs<EPT>(key, id, (int)m, thr, r, sel_row, a.top_k, sh);
   } else {
     // survivors overflowed their slots or the select's LDS, or the sampled
-    // threshold kept fewer than k: exact select over every candidate
-    const PRecomputed<DI> get{&a, row, a.idx.seq_of(row)};
-    uint32_t thr;
-    int r;
-    radix_kth(get, n, a.top_k, sh, thr, r);
-    emit_topk(get, IdSelf{}, n, thr, r, sel_row, a.top_k, sh);
+    // threshold kept fewer than k: the row is listed for the exact
+    // fallback (pidx_fallback_kernel)
+    if (threadIdx.x == 0) {
+      const uint32_t i = atomicAdd(a.fb_cnt, 1u);
+      a.fb_list[i] = rl;
+    }
+    return;
   }
   if (threadIdx.x == 0) a.n_sel[row] = a.top_k;
+}
+
+// LDS of the exact fallback: one chunk of recomputed keys and its pages.
+struct FallbackShared {
+  uint32_t keys[kChunk];
+  int32_t pages[kChunk];
+  uint32_t wcnt[kSelWaves];
+};
+
+// The exact fallback of one row.  tau_low = the k-th largest key of the
+// row's union of group maxima is a lower bound of the row's k-th key (the
+// union holds distinct keys of the row, so at least k keys reach it).  One
+// streaming pass recomputes the row's keys chunk by chunk with the decode
+// indexer's vector path (chunk_scores: same exact scores), keeps the keys
+// >= tau_low with their block ids in block order -- in the row's own
+// survivor region, free once the row is listed -- and the exact radix
+// select and ordered emission pick the k best.  Returns false (nothing
+// written) when more keys reach tau_low than the region holds.
+template <int DI>
+__device__ bool fallback_row(const PIdxArgs& a, int rl, int row, int n, int32_t* sel_row,
+                             FallbackShared& fs, SelShared& sh) {
+  const int seq = a.idx.seq_of(row);
+  const int s = max(a.row_stride[rl], 1);
+  const int n_groups = (n + kPGrp - 1) / kPGrp;
+  const int un = min(kPUnion, ((n_groups + s - 1) / s) * 16);
+  uint32_t tau = 1u;  // a union smaller than k bounds nothing: every key is kept
+  if (un >= a.top_k) {
+    constexpr int EPT = kPUnion / kSelThreads;
+    const uint32_t* src = a.uni + (int64_t)rl * kPUnion + threadIdx.x * EPT;
+    uint32_t key[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) key[i] = src[i];
+    int r;
+    bool resolved;
+    radix_kth_regs<EPT>(key, un, a.top_k, sh, tau, r, resolved);
+    tau = max(tau, 1u);
+  }
+  // candidate (key, id) list in the row's survivor region: keys, then ids
+  const int cap = min(kPSelCap, a.splits * (kPSurvCap / a.splits));
+  uint32_t* ck = reinterpret_cast<uint32_t*>(a.surv + (int64_t)rl * a.splits * (kPSurvCap / a.splits));
+  int32_t* cid = reinterpret_cast<int32_t*>(ck + cap);
+  typename RowQuery<bf16_t, DI, 4>::type iq;
+  load_row_query<bf16_t, DI, 4>(iq, a.idx, row);
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  int total = 0;
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    chunk_scores<bf16_t, DI, 4>(a.idx, seq, n, c0, iq, fs.pages, fs.keys);  // ends with a barrier
+    // wave w keeps keys [256 w, 256 w + 256) of the chunk, in order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      cnt += (uint32_t)__popcll(ballot(fs.keys[wave * 256 + 64 * j + lane] >= tau));
+    if (lane == 0) fs.wcnt[wave] = cnt;
+    __syncthreads();
+    int base = total, next = total;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      base += w < wave ? (int)fs.wcnt[w] : 0;
+      next += (int)fs.wcnt[w];
+    }
+    if (next > cap) return false;  // uniform: every thread sees the same counts
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = wave * 256 + 64 * j + lane;
+      const uint32_t kk = fs.keys[e];
+      const bool hit = kk >= tau;
+      const uint64_t m = ballot(hit);
+      if (hit) {
+        ck[base + (int)lanes_below(m)] = kk;
+        cid[base + (int)lanes_below(m)] = c0 + e;
+      }
+      base += (int)__popcll(m);
+    }
+    total = next;
+    __syncthreads();  // the chunk's LDS is reused by the next chunk
+  }
+  // the list was written by this workgroup's threads through memory
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  uint32_t thr;
+  int r;
+  radix_kth(KeyArray{ck}, total, a.top_k, sh, thr, r);
+  emit_topk(KeyArray{ck}, IdArray{cid}, total, thr, r, sel_row, a.top_k, sh);
+  return true;
+}
+
+// P4's exact fallback for the rows the select kernels listed: a fixed grid
+// of workgroups takes the listed rows in turn (the list is complete: the
+// select kernel finished before this launch).  A row whose candidates do
+// not fit its region takes the select over keys recomputed per pass.  The
+// last workgroup to finish clears the list's counter for the next call.
+template <int DI>
+__global__ void __launch_bounds__(256) pidx_fallback_kernel(PIdxArgs a) {
+  __shared__ FallbackShared fs;
+  __shared__ SelShared sh;
+  __shared__ uint32_t flag;
+  const uint32_t count = ld_agent(a.fb_cnt);
+  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+    const int rl = ld_agent(a.fb_list + i);
+    const int row = a.row0 + rl;
+    const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
+    int32_t* sel_row = a.sel + (int64_t)row * a.top_k;
+    if (!fallback_row<DI>(a, rl, row, n, sel_row, fs, sh)) {
+      const PRecomputed<DI> get{&a, row, a.idx.seq_of(row)};
+      uint32_t thr;
+      int r;
+      radix_kth(get, n, a.top_k, sh, thr, r);
+      emit_topk(get, IdSelf{}, n, thr, r, sel_row, a.top_k, sh);
+    }
+    if (threadIdx.x == 0) a.n_sel[row] = a.top_k;
+    __syncthreads();
+  }
+  if (arrive_last(a.fb_cnt + 1, gridDim.x, &flag) && threadIdx.x == 0) st_agent(a.fb_cnt, 0u);
 }
 
 bool pidx_supported(int dtype, int di, int hi) {
@@ -536,12 +653,14 @@ void run_pidx(const PIdxArgs& a, int di, hipStream_t st) {
     hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<64>), dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_fallback_kernel<64>), dim3(kPFallbackWgs), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<128>), dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pidx_fallback_kernel<128>), dim3(kPFallbackWgs), dim3(256), 0, st, a);
   }
 }
 

@@ -11,6 +11,16 @@ namespace qsa {
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
 
+// key and id sources of the selection routines: arrays in LDS or memory
+struct KeyArray {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
+};
+struct IdArray {
+  const int32_t* id;
+  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
+};
+
 struct SelShared {
   uint32_t hist[256];
   uint32_t wcnt[2][kSelWaves];

@@ -25,17 +25,9 @@ struct RowPlan {
 struct SelfId {
   __device__ __forceinline__ int32_t operator()(int e) const { return e; }
 };
-struct KeyArray {  // keys in LDS or global memory
-  const uint32_t* k;
-  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
-};
 struct ScoreKeys {  // keys of caller scores
   const float* s;
   __device__ __forceinline__ uint32_t operator()(int e) const { return score_key(s[e]); }
-};
-struct IdArray {
-  const int32_t* id;
-  __device__ __forceinline__ int32_t operator()(int e) const { return id[e]; }
 };
 
 // Key of candidate e of a row from whichever source the row has: caller

@@ -621,6 +621,41 @@ def test_e2e_prefill_1m_chunk(gpu, chunk):
     _say(f"  {len(check)} rows, max err {worst:.3g}")
 
 
+def test_e2e_prefill_1m_indep_chunk(gpu):
+    """The 1M prefill with independent selections (indexer queries without
+    the sequence direction), chunk 21 with the benchmark's queries: a few of
+    its rows keep fewer than k keys at the sampled threshold and take the
+    exact fallback.  Every one of the 32,768 rows' selections from the
+    matrix-core indexer equals the chunked VALU top-k's (run on batches of
+    63 rows), and sampled rows match the oracle (selection bit for bit,
+    outputs within tolerance)."""
+    ci = 21
+    _say(f"e2e prefill_1m_indep chunk {ci}")
+    wl = WL["prefill_1m_indep"]
+    seq_id, pos = W.prefill_rows(wl, ci)
+    pb = Problem(wl, gpu, seq_id, pos)
+    pb.qs = W.make_queries(wl, pb.cache, seq_id, pos, device=gpu, seed=wl.seed + 7919 + ci)
+    pb.rows = B.QueriesView(pb.qs.seq_id, pb.qs.pos, max(pos))
+    pb.pool_all()
+    T = len(pos)
+    _, worst = _e2e(pb, sorted(set(list(range(8)) + list(range(T - 8, T)) +
+                                  list(range(29, T, 2039)))))
+    st = pb.step("prefill")            # the matrix-core indexer (all rows at once)
+    ref_sel = torch.full_like(st.sel, -7)
+    ref_n = torch.full_like(st.n_sel, -7)
+    for i in range(0, T, 63):
+        j = min(T, i + 63)
+        rows = B.QueriesView(pb.qs.seq_id[i:j], pb.qs.pos[i:j], max(pos[i:j]))
+        ws = B.workspace(B.QSA_OP_TOPK, pb.cv, rows, 0, wl.top_k)
+        B.qsa_topk_blocks(pb.cv, rows, wl.top_k, ref_sel[i:j], ref_n[i:j], ws,
+                          q_idx=pb.qs.q_idx[i:j], w=pb.qs.w[i:j])
+    torch.cuda.synchronize()
+    assert torch.equal(st.n_sel, ref_n)
+    bad = (st.sel != ref_sel).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"rows {bad[:10]} differ between the two indexers"
+    _say(f"  {T} rows equal; sampled max err {worst:.3g}")
+
+
 def test_chunked_prefill_overlap_matches_serial(gpu):
     """The two-stream chunked prefill (each chunk's attention beside the next
     chunk's selection) gives the serial schedule's results bit for bit, and
