@@ -140,7 +140,7 @@ TopkPlan topk_plan(const qsa_cache* c, const qsa_queries* qm, int top_k) {
   const int64_t full = (int64_t)p.w_max * kChunk;
   p.ws_ld = full < kDirectCap ? full : kDirectCap;
   size_t o = 0;
-  p.off_ctr = o;    o = align256(o + (size_t)p.rows * 4);
+  p.off_ctr = o;    o = align256(o + (size_t)p.rows * arrive_slots(p.w_max) * kCtrStride * 4);
   p.off_tops = o;   o = align256(o + (size_t)p.rows * p.ucap * 8);
   p.off_nxt = o;    o = align256(o + (size_t)p.rows * p.w_max * kChunkWaves * 4);
   p.off_scores = o; o = align256(o + (size_t)p.rows * p.ws_ld * 4);
@@ -457,6 +457,7 @@ static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const f
   t.ws_scores = reinterpret_cast<float*>(base + p.off_scores);
   t.ws_ld = p.ws_ld;
   t.cnt = reinterpret_cast<uint32_t*>(base + p.off_ctr);
+  t.ctr_slots = arrive_slots(p.w_max);
   t.tops = reinterpret_cast<uint64_t*>(base + p.off_tops);
   t.nxt = reinterpret_cast<uint32_t*>(base + p.off_nxt);
   t.ucap = p.ucap;

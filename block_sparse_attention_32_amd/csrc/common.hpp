@@ -269,4 +269,40 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   return last;
 }
 
+// Atomic adds to one address serialize (about 10 ns each here), so a
+// hand-off among many workgroups counts in two levels: member idx of n
+// first adds to the counter of its group of G members, and only the last
+// member of each group adds to the top counter.  ctr[0] is the top counter
+// and ctr[stride * (1 + g)] group g's, each on its own cache line.  Same
+// guarantees as arrive_last: every counter is reset by its last member,
+// and the one workgroup that gets true has seen every member's published
+// data (each member's stores completed before its add, and each group's
+// last member adds to the top counter after every add of its group).
+template <int G>
+__device__ __forceinline__ bool arrive_last_tree(uint32_t* ctr, int stride, uint32_t idx,
+                                                 uint32_t n, uint32_t* smem_flag) {
+  if (n <= (uint32_t)G) return arrive_last(ctr, n, smem_flag);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t g = idx / G;
+    const uint32_t members = min((uint32_t)G, n - g * G);
+    const uint32_t groups = (n + G - 1) / G;
+    uint32_t* gc = ctr + (int64_t)stride * (1 + g);
+    bool last = false;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        members - 1) {
+      st_agent(gc, 0u);
+      last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             groups - 1;
+      if (last) st_agent(ctr, 0u);
+    }
+    *smem_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool last = *smem_flag != 0u;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
 }  // namespace qsa

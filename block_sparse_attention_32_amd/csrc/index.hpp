@@ -19,6 +19,14 @@ constexpr int kSelCap = 4096;       // survivors gathered into LDS for the final
 constexpr int kMaxIdxHeads = 8;
 constexpr int kMaxJw = 16;
 constexpr int kMaxJwL = 32;         // per-wave tops of a large selection
+constexpr int kArriveGroup = 32;    // chunks per first-level arrival counter of a row
+constexpr int kCtrStride = 64;      // words between arrival counters (one 256-byte line each)
+
+// Arrival counters of one row of the top-k: one, or with more than
+// kArriveGroup chunks a top counter and one per group of kArriveGroup.
+__host__ __device__ inline int arrive_slots(int w_max) {
+  return w_max > kArriveGroup ? 1 + (w_max + kArriveGroup - 1) / kArriveGroup : 1;
+}
 
 // Per-wave top count: each wave of each chunk publishes its jw best
 // (key, id) pairs: the largest power of two that fits the call's union
@@ -84,7 +92,8 @@ struct TopkArgs {
   int w_max;             // chunks of the longest row
   float* ws_scores;      // [R][ws_ld] keys of rows of at most kDirectCap candidates
   int64_t ws_ld;
-  uint32_t* cnt;         // [R] arrival counters
+  uint32_t* cnt;         // [R][ctr_slots][kCtrStride] arrival counters (arrive_slots)
+  int ctr_slots;
   int ucap;              // union capacity per row (union_cap)
   uint64_t* tops;        // [R][ucap] (block id << 32 | key)
   uint32_t* nxt;         // [R][w_max * 4] largest key of each wave not in its tops (0: none)

@@ -222,4 +222,64 @@ __device__ __forceinline__ void chunk_scores(const IdxArgs& a, int seq, int n, i
   __syncthreads();
 }
 
+// Keys of the kRun blocks [b0, b0 + kRun) of one row, computed by the
+// calling wave alone into dst[0, kRun) (blocks >= n get key 0).  The lane
+// layout (G lanes per block, lane part = lane % G holding the same slice of
+// the query as in chunk_scores) and the arithmetic are chunk_scores', so
+// each key equals the one the chunked pass computed, bit for bit.  The
+// wave's own later LDS reads see dst; other waves need a barrier.
+constexpr int kRun = 256;
+template <typename T, int DI, int HI>
+__device__ __forceinline__ void run_scores(const IdxArgs& a, int seq, int n, int b0,
+                                           const typename RowQuery<T, DI, HI>::type& iq,
+                                           uint32_t* dst) {
+  constexpr bool kBf = std::is_same<T, bf16_t>::value;
+  constexpr int G = RowQuery<T, DI, HI>::G;
+  static_assert(kWave % G == 0, "a block's lanes lie in one wave");
+  constexpr int LPR = kBf ? 2 : 1;
+  constexpr int RPW = kWave / G;          // blocks per wave iteration
+  constexpr int NIT = kRun / RPW;
+  constexpr int U = NIT * LPR < 32 ? NIT : 32 / LPR;
+  const T* kbar = static_cast<const T*>(a.kbar);
+  const int lane = lane_id(), gi = lane / G, part = lane % G;
+#pragma unroll 1
+  for (int it0 = 0; it0 < NIT; it0 += U) {
+    uint4 raw[U][LPR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = b0 + (it0 + u) * RPW + gi;
+      if (b < n) {
+        const T* rowp = kbar + a.pm.block_slot(seq, b) * DI;
+        if constexpr (kBf) {
+          raw[u][0] = *reinterpret_cast<const uint4*>(rowp + 8 * part);
+          raw[u][LPR - 1] = *reinterpret_cast<const uint4*>(rowp + 8 * (part + G));
+        } else {
+          raw[u][0] = *reinterpret_cast<const uint4*>(rowp + 4 * part);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < LPR; ++j) raw[u][j] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s;
+      if constexpr (kBf) {
+        s = iq.score(raw[u][0], raw[u][LPR - 1]);
+      } else {
+        float x[4] = {__uint_as_float(raw[u][0].x), __uint_as_float(raw[u][0].y),
+                      __uint_as_float(raw[u][0].z), __uint_as_float(raw[u][0].w)};
+        s = iq.score(x);
+      }
+      const int i = (it0 + u) * RPW + gi;
+      if (part == 0) dst[i] = (b0 + i < n) ? score_key(s) : 0u;
+    }
+  }
+  // the wave's LDS operations complete in order; keep the compiler from
+  // moving the callers' reads above these writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace qsa

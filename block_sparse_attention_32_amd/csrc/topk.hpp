@@ -69,6 +69,31 @@ struct RowKeys {
   }
 };
 
+// Keys of run r of a long row (candidates [kRun r, kRun r + kRun), one
+// scoring wave's), produced by the calling wave into dst[0, kRun): from the
+// caller's scores, or recomputed with the scoring pass's own vector path
+// (run_scores), which gives the keys the tops were taken from, bit for bit.
+template <typename T, int DI, int HI>
+struct RunKeys {
+  const IdxArgs& idx;
+  const float* given;
+  const typename RowQuery<T, DI, HI>::type& iq;
+  int seq, n;
+  __device__ __forceinline__ void operator()(int r, uint32_t* dst) const {
+    const int b0 = r * kRun;
+    if (given != nullptr) {
+      const int lane = lane_id();
+#pragma unroll
+      for (int j = 0; j < kRun / kWave; ++j) {
+        const int e = b0 + kWave * j + lane;
+        dst[kWave * j + lane] = e < n ? score_key(given[e]) : 0u;
+      }
+    } else {
+      run_scores<T, DI, HI>(idx, seq, n, b0, iq, dst);
+    }
+  }
+};
+
 __device__ __forceinline__ void write_all(int32_t* sel_row, int32_t* n_sel, int row, int n,
                                           int top_k) {
   for (int j = threadIdx.x; j < top_k; j += blockDim.x) sel_row[j] = j < n ? j : -1;
@@ -103,6 +128,7 @@ __device__ __noinline__ void select_full(Get get, int n, int top_k, int32_t* sel
 // ascending id order, and the exact radix select + ordered emission of
 // select.hpp picks the k best with ties to the lower id.
 static_assert(kChunkWaves == kSelWaves, "a top-k workgroup's waves are its runs");
+static_assert(kChunk == kSelWaves * kRun, "a chunk is four runs; its keys[] holds four rescored runs");
 constexpr int kMaxSat = 64;  // saturated waves rescanned per row (else exact fallback)
 constexpr int kWaveSel = 16;  // survivors per lane of the one-wave final select (1,024)
 
@@ -120,15 +146,19 @@ struct LongShared {
 // 256 -- in registers, loaded at once, with the largest unpublished key of
 // each of its runs (nxt).  tau = the k-th largest union key (low bits past
 // two radix digits cleared); a run whose unpublished key reaches tau is
-// saturated and rescanned from the key source; the other runs' survivors
-// (key >= tau) are placed in id order straight from the registers, each
-// run's entries ranked by id (a run lists one wave's keys best first).
-// Then the exact select among the survivors.
-template <int JW, int E, class Src>
-__device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops,
-                                          const uint32_t* nxt, int nw, int n, int top_k,
-                                          int32_t* sel_row, int32_t* n_sel, int row,
-                                          LongShared& ls, SelShared& sh) {
+// saturated and rescanned: wave w rescores runs w, w + 4, ... into its
+// quarter of rk (kRun keys each) with run_keys, counts them, and -- when
+// there are at most four, so that each stays in LDS -- places them from
+// there (else it rescores them).  The other runs' survivors (key >= tau)
+// are placed in id order straight from the registers, each run's entries
+// ranked by id (a run lists one wave's keys best first).  Then the exact
+// select among the survivors; src (every key of the row) serves the rare
+// select over all keys.
+template <int JW, int E, class Src, class Run>
+__device__ __forceinline__ void long_tail(const Src& src, const Run& run_keys, uint32_t* rk,
+                                          const uint64_t* tops, const uint32_t* nxt, int nw,
+                                          int n, int top_k, int32_t* sel_row, int32_t* n_sel,
+                                          int row, LongShared& ls, SelShared& sh) {
   static_assert(JW <= E, "a thread holds whole runs");
   constexpr int R = E / JW;
   const int un = nw * JW;
@@ -172,17 +202,19 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops,
   __syncthreads();
   const int ns = (int)ls.n_sat;
   bool fits = ns <= kMaxSat;
-  // survivor counts of saturated runs (a run is one scoring wave's 256
-  // candidates; wave w of this workgroup counts runs w, w + 4, ..., its
-  // lanes reading 4 keys each, with no workgroup barrier per run)
+  const bool runs_kept = ns <= kSelWaves;  // each wave's one run stays in rk
+  uint32_t* my_rk = rk + wave * kRun;
+  // survivor counts of saturated runs (wave w counts runs w, w + 4, ...,
+  // with no workgroup barrier per run)
 #pragma unroll 1
   for (int i = wave; fits && i < ns; i += kSelWaves) {
-    const int e0 = ls.sat_w[i] * 256 + lane;
+    const int e0 = ls.sat_w[i] * kRun + lane;
+    run_keys(ls.sat_w[i], my_rk);
     uint32_t cw = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 64 * j;
-      cw += (uint32_t)__popcll(ballot(e < n && src(e) >= tau));
+    for (int j = 0; j < kRun / kWave; ++j) {
+      const int e = e0 + kWave * j;
+      cw += (uint32_t)__popcll(ballot(e < n && my_rk[kWave * j + lane] >= tau));
     }
     if (lane == 0) ls.sat_cnt[i] = cw;
   }
@@ -229,12 +261,13 @@ __device__ __forceinline__ void long_tail(const Src& src, const uint64_t* tops,
   // ...; a run's ids ascend with 64 j + lane)
 #pragma unroll 1
   for (int i = wave; fits && i < ns; i += kSelWaves) {
-    const int e0 = ls.sat_w[i] * 256 + lane;
+    const int e0 = ls.sat_w[i] * kRun + lane;
+    if (!runs_kept) run_keys(ls.sat_w[i], my_rk);
     uint32_t base = ls.sat_off[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 64 * j;
-      const uint32_t kk = e < n ? src(e) : 0u;
+    for (int j = 0; j < kRun / kWave; ++j) {
+      const int e = e0 + kWave * j;
+      const uint32_t kk = e < n ? my_rk[kWave * j + lane] : 0u;
       const bool hit = e < n && kk >= tau;
       const uint64_t m = ballot(hit);
       if (hit) {
@@ -340,12 +373,12 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   const int c0 = c * kChunk;
   uint32_t* ws_row = reinterpret_cast<uint32_t*>(t.ws_scores + (int64_t)rl * t.ws_ld);
   const bool keep = !given && direct;  // long rows publish tops only
+  typename RowQuery<T, DI, HI>::type iq;  // (also rescores saturated runs in the tail)
   if (given) {
     for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
       keys[i] = (c0 + i < p.n) ? score_key(given[c0 + i]) : 0u;
     __syncthreads();
   } else {
-    typename RowQuery<T, DI, HI>::type iq;
     load_row_query<T, DI, HI>(iq, t.idx, row);
     chunk_scores<T, DI, HI>(t.idx, p.seq, p.n, c0, iq, pages, keys);
     if (keep) {
@@ -385,56 +418,69 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
       st_agent(t.nxt + (int64_t)rl * t.w_max * kSelWaves + c * kSelWaves + wave, rest);
   }
   if (!OWN_TAIL && !direct) return;  // the tail follows in topk_tail_kernel
-  if (!arrive_last(t.cnt + rl, (uint32_t)p.W, &flag)) return;
+  if (!arrive_last_tree<kArriveGroup>(t.cnt + (int64_t)rl * t.ctr_slots * kCtrStride, kCtrStride,
+                                      (uint32_t)c, (uint32_t)p.W, &flag))
+    return;
   if (direct) {
     select_direct(KeyArray{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
     return;
   }
 
-  // ---- last chunk of a long row
+  // ---- last chunk of a long row (its scoring LDS, keys[], holds the
+  // rescored saturated runs)
   if constexpr (OWN_TAIL) {
     const RowKeys<T, DI> src(given, keep ? ws_row : nullptr, t, row, p.seq);
+    const RunKeys<T, DI, HI> rs{t.idx, given, iq, p.seq, p.n};
     const int nw = p.W * kSelWaves;
     constexpr int E = UCAP / kSelThreads;
     const uint32_t* nxt = t.nxt + (int64_t)rl * t.w_max * kSelWaves;
+#define QSA_LONG_TAIL(J) \
+  long_tail<J, E>(src, rs, keys, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh)
     switch (p.jw) {
-      case 1: long_tail<1, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 2: long_tail<2, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 4: long_tail<4, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 8: long_tail<8, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-      case 16: long_tail<16, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+      case 1: QSA_LONG_TAIL(1); break;
+      case 2: QSA_LONG_TAIL(2); break;
+      case 4: QSA_LONG_TAIL(4); break;
+      case 8: QSA_LONG_TAIL(8); break;
+      case 16: QSA_LONG_TAIL(16); break;
       default:
-        if constexpr (E >= 32)
-          long_tail<32, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh);
+        if constexpr (E >= 32) QSA_LONG_TAIL(32);
         break;
     }
+#undef QSA_LONG_TAIL
   }
 }
 
 // The tail of the long rows of a large selection, after topk_kernel has
 // published every chunk's per-wave tops: one workgroup per row.
-template <typename T, int DI>
+template <typename T, int DI, int HI>
 __global__ void __launch_bounds__(256) topk_tail_kernel(TopkArgs t) {
   __shared__ LongShared ls;
   __shared__ SelShared sh;
+  __shared__ uint32_t rk[kSelWaves * kRun];
   const int rl = blockIdx.x, row = t.row0 + rl;
   const RowPlan p(t, row);
   if (p.n <= t.top_k || p.n <= kDirectCap) return;  // done by topk_kernel
   int32_t* sel_row = t.sel + (int64_t)row * t.top_k;
   const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
+  typename RowQuery<T, DI, HI>::type iq;
+  if (!given) load_row_query<T, DI, HI>(iq, t.idx, row);
   const RowKeys<T, DI> src(given, nullptr, t, row, p.seq);
+  const RunKeys<T, DI, HI> rs{t.idx, given, iq, p.seq, p.n};
   const uint64_t* tops = t.tops + (int64_t)rl * kUnionCapL;
   const uint32_t* nxt = t.nxt + (int64_t)rl * t.w_max * kSelWaves;
   const int nw = p.W * kSelWaves;
   constexpr int E = kUnionCapL / kSelThreads;
+#define QSA_LONG_TAIL_L(J) \
+  long_tail<J, E>(src, rs, rk, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh)
   switch (p.jw) {
-    case 1: long_tail<1, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 2: long_tail<2, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 4: long_tail<4, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 8: long_tail<8, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    case 16: long_tail<16, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
-    default: long_tail<32, E>(src, tops, nxt, nw, p.n, t.top_k, sel_row, t.n_sel, row, ls, sh); break;
+    case 1: QSA_LONG_TAIL_L(1); break;
+    case 2: QSA_LONG_TAIL_L(2); break;
+    case 4: QSA_LONG_TAIL_L(4); break;
+    case 8: QSA_LONG_TAIL_L(8); break;
+    case 16: QSA_LONG_TAIL_L(16); break;
+    default: QSA_LONG_TAIL_L(32); break;
   }
+#undef QSA_LONG_TAIL_L
 }
 
 // Launches the top-k kernels of one row batch for element type T and
@@ -445,7 +491,7 @@ static void launch_topk(const TopkArgs& t, int rows, hipStream_t st) {
   dim3 grid((unsigned)t.w_max, (unsigned)rows);
   if (t.ucap == kUnionCapL) {
     hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapL>), grid, dim3(256), 0, st, t);
-    hipLaunchKernelGGL((topk_tail_kernel<T, DI>), dim3((unsigned)rows), dim3(256), 0, st, t);
+    hipLaunchKernelGGL((topk_tail_kernel<T, DI, HI>), dim3((unsigned)rows), dim3(256), 0, st, t);
   } else if (t.ucap == kUnionCapM) {
     hipLaunchKernelGGL((topk_kernel<T, DI, HI, kUnionCapM>), grid, dim3(256), 0, st, t);
   } else {

@@ -128,10 +128,14 @@ def test_topk_bit_exact(gpu, case, fused):
 
 @pytest.mark.parametrize("rows", [4, 64], ids=["4rows", "64rows"])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
-@pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190), (9000, 100)])
+@pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190), (2000, 5000),
+                                          (9000, 100)])
 def test_topk_ties_lower_id_wins(gpu, n_tied, first, fused, rows):
-    """Many blocks with identical top scores: the lowest ids win.  Large tie
-    groups overflow the survivor slots (exact fallback paths)."""
+    """Many blocks with identical top scores: the lowest ids win.  The tied
+    blocks fill whole runs of 256, whose waves saturate: up to four such
+    runs are rescored once and kept in LDS, 2,000 ties (eight runs) are
+    rescored again to be placed; 9,000 overflow the survivor slots (exact
+    fallback paths)."""
     _say(f"ties {n_tied} {first} fused={fused} rows={rows}")
     wl = MIXED.replace(n_ctx=80004)
     pos = [20000 * 4 + 1, 9000 * 4 + 3, 8000 * 4, 600 * 4 + 2] * (rows // 4)
