@@ -539,7 +539,8 @@ struct FallbackShared {
 // >= tau_low with their block ids in block order -- in the row's own
 // survivor region, free once the row is listed -- and the exact radix
 // select and ordered emission pick the k best.  Returns false (nothing
-// written) when more keys reach tau_low than the region holds.
+// written) when more keys reach tau_low than the region holds, or fewer
+// than k do.
 template <int DI>
 __device__ bool fallback_row(const PIdxArgs& a, int rl, int row, int n, int32_t* sel_row,
                              FallbackShared& fs, SelShared& sh) {
@@ -598,6 +599,10 @@ __device__ bool fallback_row(const PIdxArgs& a, int rl, int row, int n, int32_t*
     total = next;
     __syncthreads();  // the chunk's LDS is reused by the next chunk
   }
+  // the keys recomputed here come from the vector path, the bound from the
+  // matrix-core keys: on inputs where the two round differently, fewer than
+  // k keys may reach it (then the select over keys recomputed per pass)
+  if (total < a.top_k) return false;
   // the list was written by this workgroup's threads through memory
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
