@@ -118,10 +118,12 @@ __device__ __forceinline__ bool next_pass(TileMeta& tm) {
 }
 
 // sample stride of a pass: the largest power of two s <= kPMaxStride with
-// ceil(n_lo / 256 / s) * 16 >= 2 * top_k (or 1)
+// ceil(n_lo / 256 / s) * 16 >= top_k (or 1): the sampled union still holds
+// at least k maxima (a sparser sample leaves more rows short of k
+// survivors, which the exact fallback then serves)
 __device__ __forceinline__ int pass_stride(int n_lo, int top_k) {
   int s = 1;
-  while (s < kPMaxStride && ((n_lo + kPGrp * 2 * s - 1) / (kPGrp * 2 * s)) * 16 >= 2 * top_k)
+  while (s < kPMaxStride && ((n_lo + kPGrp * 2 * s - 1) / (kPGrp * 2 * s)) * 16 >= top_k)
     s *= 2;
   return s;
 }
