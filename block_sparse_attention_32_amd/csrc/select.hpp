@@ -131,6 +131,26 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, SelShared& sh, u
   return base + incl;
 }
 
+// The maxima of a and of b over the workgroup in one exchange.
+__device__ __forceinline__ void block_max2_u32(uint32_t& a, uint32_t& b, SelShared& sh) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  a = wave_max_u32(a);
+  b = wave_max_u32(b);
+  if (lane == 0) {
+    sh.wcnt[0][wave] = a;
+    sh.wcnt[1][wave] = b;
+  }
+  __syncthreads();
+  a = 0u;
+  b = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    a = max(a, sh.wcnt[0][w]);
+    b = max(b, sh.wcnt[1][w]);
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, SelShared& sh) {
   const int wave = threadIdx.x / kWave, lane = lane_id();
   v = wave_max_u32(v);
@@ -274,8 +294,9 @@ __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShar
       nmn = max(nmn, ~key[i]);
     }
   }
-  mx = block_max_u32(mx, sh);
-  const uint32_t mn = ~block_max_u32(nmn, sh);
+  sh.hist[threadIdx.x] = 0u;  // the first pass's histogram, cleared under the exchange below
+  block_max2_u32(mx, nmn, sh);
+  const uint32_t mn = ~nmn;
   if (mx == mn) {
     T = mx;
     r = k;
@@ -290,8 +311,10 @@ __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShar
   for (int pass = 0; pass < max_passes; ++pass) {
     const int shift = hi >= 7 ? hi - 7 : 0;
     const uint32_t dmask = (1u << (hi - shift + 1)) - 1u;
-    sh.hist[threadIdx.x] = 0u;
-    __syncthreads();
+    if (pass > 0) {
+      sh.hist[threadIdx.x] = 0u;
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       if (base_e + i < n && (key[i] & mask) == prefix)

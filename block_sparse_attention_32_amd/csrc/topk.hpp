@@ -169,10 +169,34 @@ __device__ __forceinline__ void long_tail(const Src& src, const Run& run_keys, u
   uint32_t nx[R];  // largest unpublished key of each of this thread's runs
   {
     uint64_t v[E];
+    if (e0 + E <= un) {
+      // whole runs in range (every thread of a full union): 16-byte loads,
+      // no per-entry tests (tops rows and the thread's E entries are 16-byte
+      // aligned, and so are the thread's R nxt words when R is 4)
+      typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+      const u64x2_t* tp = reinterpret_cast<const u64x2_t*>(tops + e0);
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = e0 + i < un ? tops[e0 + i] : 0ull;
+      for (int i = 0; i < E / 2; ++i) {
+        const u64x2_t t2 = tp[i];
+        v[2 * i] = t2.x;
+        v[2 * i + 1] = t2.y;
+      }
+      if constexpr (R == 4) {
+        const uint4 n4 = *reinterpret_cast<const uint4*>(nxt + e0 / JW);
+        nx[0] = n4.x;
+        nx[1] = n4.y;
+        nx[2] = n4.z;
+        nx[3] = n4.w;
+      } else {
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) nx[rr] = e0 + rr * JW < un ? nxt[e0 / JW + rr] : 0u;
+        for (int rr = 0; rr < R; ++rr) nx[rr] = nxt[e0 / JW + rr];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = e0 + i < un ? tops[e0 + i] : 0ull;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) nx[rr] = e0 + rr * JW < un ? nxt[e0 / JW + rr] : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       k[i] = (uint32_t)v[i];
