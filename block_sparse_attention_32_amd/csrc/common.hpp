@@ -246,6 +246,13 @@ __device__ __forceinline__ U ld_agent(const U* p) {
   return __hip_atomic_load(const_cast<U*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Each wave waits until its own memory operations have completed: its
+// agent-scope stores have then reached the level every XCD reads, before
+// the workgroup's arrival is counted.  (A workgroup-scope fence does not
+// wait for them, and a store and a later atomic may travel to different
+// memory channels.)
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
 // "Last workgroup" hand-off: every workgroup of a group calls this after
 // publishing its results with st_agent; exactly one (the last to arrive)
 // gets true.  Each wave first waits for its own stores to complete; the
@@ -254,6 +261,7 @@ __device__ __forceinline__ U ld_agent(const U* p) {
 // published data and can be issued back to back.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected,
                                             uint32_t* smem_flag) {
+  wait_own_stores();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -282,6 +290,7 @@ template <int G>
 __device__ __forceinline__ bool arrive_last_tree(uint32_t* ctr, int stride, uint32_t idx,
                                                  uint32_t n, uint32_t* smem_flag) {
   if (n <= (uint32_t)G) return arrive_last(ctr, n, smem_flag);
+  wait_own_stores();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
