@@ -111,6 +111,10 @@ namespace qsa {
 constexpr int kMfmaTileTok = 16;    // tokens per wave tile
 constexpr int kMfmaSplitEnt = 16;   // 4-token units per split and KV head (split-K decode)
 constexpr int kMfmaListTok = 2048;  // list tokens staged in LDS per pass
+// Many-row attention in pairs of rows: each row's list (selection and own
+// block) holds at most kPairHalf entries, their union at most kPairCap.
+constexpr int kPairHalf = 544;
+constexpr int kPairCap = 2 * kPairHalf;
 
 bool attn_mfma_supported(int dtype, int hq, int hkv, int d);
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st);

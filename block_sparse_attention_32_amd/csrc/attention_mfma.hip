@@ -185,7 +185,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 template <bool SPLIT>
 constexpr int attn_waves() { return SPLIT ? 8 : 4; }
 
-template <int D, bool DENSE, bool SPLIT, bool WIDE>
+template <int D, bool DENSE, bool SPLIT, bool WIDE, bool PAIR>
 __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     attn_mfma_kernel(AttnArgs a) {
   constexpr int NW = attn_waves<SPLIT>(), NT = NW * kWave;
@@ -209,6 +209,12 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   __shared__ __align__(16) unsigned char lds[kStage > kMerge ? kStage : kMerge];
   __shared__ int wcnt[NW];
   __shared__ uint32_t flag;
+  // PAIR: the union of the two rows' entry lists (block ids and which rows
+  // list them: bit 0 row A, bit 1 row B) and each staged token's visibility
+  // (the same bits)
+  __shared__ int32_t ublk[PAIR ? kPairCap : 1];
+  __shared__ uint8_t umem[PAIR ? kPairCap : 4];
+  __shared__ __align__(4) uint8_t tmask[PAIR ? kMfmaListTok : 4];
   // the wave index is uniform: read it once so that what derives from it
   // (the KV head, the wave's tiles, the cache base) stays scalar
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
@@ -218,8 +224,12 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int wph = SPLIT ? NW / hkv : NW;  // waves per KV head
   const int hk = SPLIT ? w % hkv : (int)(blockIdx.x % (unsigned)hkv);
   const int wsub = SPLIT ? w / hkv : w;
-  const int row = SPLIT ? (int)blockIdx.y : (int)(blockIdx.x / (unsigned)hkv);
+  const int row =
+      SPLIT ? (int)blockIdx.y : (int)(blockIdx.x / (unsigned)hkv) * (PAIR ? 2 : 1);
   const int split = SPLIT ? (int)blockIdx.x : 0;
+  // PAIR: rows row (A) and row + 1 (B, if present) share the workgroup
+  const int rowB = row + 1;
+  const bool hasB = PAIR && rowB < a.n_rows;
 
   // the reads that depend on the row index alone, issued together so that
   // their latencies overlap: sequence, position, selection length, and the
@@ -231,9 +241,14 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   const int nsel_raw = DENSE ? 0 : a.n_sel[row];
   const int32_t pre =
       DENSE ? -1 : a.sel[(int64_t)row * a.top_k + min(e_beg + (int)threadIdx.x, a.top_k - 1)];
+  const int sidB_raw = hasB ? a.seq_id[rowB] : 0;
+  const int posB_raw = hasB ? a.pos[rowB] : 0;
+  const int nselB_raw = hasB ? a.n_sel[rowB] : 0;
   const int seq = clamp_flag(sid_raw, 0, a.n_seqs - 1, QSA_DEBUG_BAD_ROW);
   const int t = clamp_flag(pos_raw, 0, a.max_pos, QSA_DEBUG_BAD_ROW);
   const RowList rl(a, row, t, DENSE, nsel_raw);
+  const int seqB = clamp_flag(sidB_raw, 0, a.n_seqs - 1, QSA_DEBUG_BAD_ROW);
+  const int tB = clamp_flag(posB_raw, 0, a.max_pos, QSA_DEBUG_BAD_ROW);
   const int b_own = rl.b_own;
   const int n_entries = rl.e_own + 1;
   const int e_end = min(n_entries, e_beg + a.eps);
@@ -252,12 +267,18 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   // this lane's B fragment of Q^T: head c16 of the group, dims 32 s + 8 g
   // .. +8 at step s (K uses the same order, so one load instruction reads
   // 64 contiguous bytes of each token row)
+  // (PAIR: columns G .. 2G - 1 hold row B's heads)
+  const bool colB = PAIR && c16 >= G;
+  const uint32_t colbit = !PAIR ? 0u : (c16 < G ? 1u : (c16 < 2 * G ? 2u : 0u));
   u32x4_t qf[KS];
   {
-    const bf16_t* qh = static_cast<const bf16_t*>(a.q) + ((int64_t)row * hq + hk * G + c16) * D;
+    const bool qok = c16 < G || (colB && c16 < 2 * G && hasB);
+    const int64_t qr = colB ? rowB : row;
+    const bf16_t* qh =
+        static_cast<const bf16_t*>(a.q) + (qr * hq + hk * G + (colB ? c16 - G : c16)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[s] = (c16 < G) ? ld16(qh + 32 * s + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+      qf[s] = qok ? ld16(qh + 32 * s + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
   }
   // Online softmax per head column.  Scores stay raw (q.k); the reference
   // maximum m is kept raw and as m * scale * log2(e), and moves only when a
@@ -281,166 +302,119 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
 
   // list token p -> its place in trow
   auto tslot = [](int p) { return (p >> 4) * 16 + ((p & 3) << 2) + ((p & 15) >> 2); };
-  for (int cb = e_beg; cb < e_end; cb += epp) {
-    const int nloc = min(e_end, cb + epp) - cb;
-    __syncthreads();
-    // Stage the valid entries of [cb, cb + nloc) at the front, in list
-    // order (a block-wide prefix count of the valid flags), so that every
-    // tile but the last holds only tokens to attend.  The own block is the
-    // last entry of the list, hence the last valid entry of its chunk.
-    int nv = 0;
-    for (int i0 = 0; i0 < nloc; i0 += NT) {
-      const int i = i0 + (int)threadIdx.x;
-      const int E = cb + i;
-      const bool own = (E == rl.e_own);
-      bool ok = i < nloc;
-      int b = b_own;
-      if (ok && !own) {
-        if (!DENSE && rl.own_sel && cb == e_beg && i0 == 0 && E < rl.n_list) {
-          b = pre;
-          ok = b >= 0 && b < rl.b_sel;
-          if (!ok) debug_flag(QSA_DEBUG_BAD_SEL);
-        } else {
-          b = rl.block(E, DENSE, ok);
-        }
-      }
-      const uint64_t bal = __ballot(ok);
-      if (l == 0) wcnt[w] = __popcll(bal);
-      __syncthreads();
-      int pos = nv + (int)lanes_below(bal), tot = nv;
+  int ntok = 0;  // tokens staged by the current pass
+  // A tile is 16 tokens, tile row 4i + j = entry i, token j.  The K and
+  // V rows of the wave's next tile are loaded while the current one is
+  // computed, both the same way: load i reads entry i, lane group g its
+  // token g, lane c16 its 16-byte chunk, so that 16 lanes read a whole
+  // row (whole cache lines; the MFMA operand order, 64 bytes of 16 rows
+  // per load, costs the vector cache about twice as much).  Every load
+  // reads a row present in the cache (masked tokens read the own block's
+  // first token).
+  auto load_tile = [&](int tile, u32x4_t (&kf)[4], u32x4_t (&vf)[4]) {
+    const u32x4_t tv = *reinterpret_cast<const u32x4_t*>(trow + tile * 16 + 4 * g);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const int c = wcnt[j];
-        pos += j < w ? c : 0;
-        tot += c;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (WIDE) {
+        const int64_t o = (int64_t)tv[i] * rowbytes + lane_c;
+        kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
+        vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
+      } else {
+        const uint32_t o = tv[i] + lane_c;
+        kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
+        vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
       }
-      if (ok) {
-        const int64_t r0 = a.pm.token_slot(seq, b << bs);
-        const int nt = own ? tail : nb;
-        const int p0 = pos << bs;
-        if (nb == 4) {  // QSA blocks: four stores, no loop
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int64_t r = j < nt ? r0 + j : own_row;
-            trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
-          }
-        } else {
-          for (int j = 0; j < nt; ++j) {
-            const int64_t r = r0 + j;
-            trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
-          }
-        }
-      }
-      nv = tot;
-      __syncthreads();
     }
-    const bool own_here = rl.e_own >= cb && rl.e_own < cb + nloc;
-    // tokens to attend: whole blocks, the own block's tail last
-    const int ntok = own_here ? ((nv - 1) << bs) + tail : (nv << bs);
-    for (int p = ntok + (int)threadIdx.x; p < ((ntok + 15) & ~15); p += NT) trow[tslot(p)] = own_t;
-    __syncthreads();
-    const int n_tiles = (ntok + 15) / 16;
-    const int last = n_tiles - 1;
-    // A tile is 16 tokens, tile row 4i + j = entry i, token j.  The K and
-    // V rows of the wave's next tile are loaded while the current one is
-    // computed, both the same way: load i reads entry i, lane group g its
-    // token g, lane c16 its 16-byte chunk, so that 16 lanes read a whole
-    // row (whole cache lines; the MFMA operand order, 64 bytes of 16 rows
-    // per load, costs the vector cache about twice as much).  Every load
-    // reads a row present in the cache (masked tokens read the own block's
-    // first token).
-    auto load_tile = [&](int tile, u32x4_t (&kf)[4], u32x4_t (&vf)[4]) {
-      const u32x4_t tv = *reinterpret_cast<const u32x4_t*>(trow + tile * 16 + 4 * g);
+  };
+  // one tile: S^T, online softmax, O^T update.  Only the last tile of
+  // the chunk can hold tokens not to attend (the own block's tail, the
+  // padding), so only it masks.
+  auto compute = [&](auto masked, int tile, const u32x4_t (&kf)[4], const u32x4_t (&vf)[4]) {
+    constexpr bool MASK = decltype(masked)::value;
+    // K and V rows to LDS (row 4i + g)
+    if (c16 < D / 8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (WIDE) {
-          const int64_t o = (int64_t)tv[i] * rowbytes + lane_c;
-          kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
-          vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
-        } else {
-          const uint32_t o = tv[i] + lane_c;
-          kf[i] = *reinterpret_cast<const u32x4_t*>(kbase + o);
-          vf[i] = *reinterpret_cast<const u32x4_t*>(vbase + o);
-        }
+        const int r = 4 * i + g;
+        *reinterpret_cast<u32x4_t*>(ks + r * KP + 16 * (cv ^ (r % NCH))) = kf[i];
+        *reinterpret_cast<u32x4_t*>(vs + (4 * i + g) * VP + 16 * c16) = vf[i];
       }
-    };
-    // one tile: S^T, online softmax, O^T update.  Only the last tile of
-    // the chunk can hold tokens not to attend (the own block's tail, the
-    // padding), so only it masks.
-    auto compute = [&](auto masked, int tile, const u32x4_t (&kf)[4], const u32x4_t (&vf)[4]) {
-      constexpr bool MASK = decltype(masked)::value;
-      // K and V rows to LDS (row 4i + g)
-      if (c16 < D / 8) {
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // S^T: lane holds tile tokens 4g + r (entry g, token r) for head c16
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * i + g;
-          *reinterpret_cast<u32x4_t*>(ks + r * KP + 16 * (cv ^ (r % NCH))) = kf[i];
-          *reinterpret_cast<u32x4_t*>(vs + (4 * i + g) * VP + 16 * c16) = vf[i];
-        }
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const u32x4_t kfr = *reinterpret_cast<const u32x4_t*>(
+          ks + kr_off + 16 * ((4 * s2 + g) ^ (c16 % NCH)));
+      sc = mfma16(kfr, qf[s2], sc);
+    }
+    float x[4];
+    if constexpr (PAIR) {
+      // the column's row sees token 4g + r of the tile
+      const uint32_t mk = *reinterpret_cast<const uint32_t*>(tmask + tile * 16 + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = ((mk >> (8 * r)) & colbit) ? sc[r] : -INFINITY;
+    } else if constexpr (MASK) {
+      const int p0 = tile * 16 + 4 * g;  // list token of row r: p0 + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = p0 + r < ntok ? sc[r] : -INFINITY;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = sc[r];
+    }
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__ballot(mx > mlim) != 0ull) {
+      // the column's maximum over the four lane groups (rows 16 apart,
+      // then 32 apart)
+      float cm = mx;
+      {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm),
+                                                        false, false);
+        cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      // S^T: lane holds tile tokens 4g + r (entry g, token r) for head c16
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        const u32x4_t kfr = *reinterpret_cast<const u32x4_t*>(
-            ks + kr_off + 16 * ((4 * s2 + g) ^ (c16 % NCH)));
-        sc = mfma16(kfr, qf[s2], sc);
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm),
+                                                        false, false);
+        cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
       }
-      float x[4];
-      if constexpr (MASK) {
-        const int p0 = tile * 16 + 4 * g;  // list token of row r: p0 + r
+      if (cm > mlim) {
+        const float msl2_new = cm * sl2;
+        const float corr = __builtin_amdgcn_exp2f(msl2 - msl2_new);  // 0 while msl2 = -inf
+        lacc = lacc * corr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = p0 + r < ntok ? sc[r] : -INFINITY;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = sc[r];
+        for (int n = 0; n < NDT; ++n) acc[n] = acc[n] * corr;
+        m_raw = cm;
+        msl2 = msl2_new;
+        mlim = m_raw + slack_raw;
       }
-      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__ballot(mx > mlim) != 0ull) {
-        // the column's maximum over the four lane groups (rows 16 apart,
-        // then 32 apart)
-        float cm = mx;
-        {
-          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm),
-                                                          false, false);
-          cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        }
-        {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm),
-                                                          false, false);
-          cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        }
-        if (cm > mlim) {
-          const float msl2_new = cm * sl2;
-          const float corr = __builtin_amdgcn_exp2f(msl2 - msl2_new);  // 0 while msl2 = -inf
-          lacc = lacc * corr;
+    }
+    // (PAIR: a column whose row has seen no token yet has msl2 = -inf and
+    // only masked scores; 0 in place of -msl2 keeps their numerators 0)
+    const float nm = (PAIR && msl2 == -INFINITY) ? 0.0f : -msl2;
+    float p[4];
 #pragma unroll
-          for (int n = 0; n < NDT; ++n) acc[n] = acc[n] * corr;
-          m_raw = cm;
-          msl2 = msl2_new;
-          mlim = m_raw + slack_raw;
-        }
-      }
-      float p[4];
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(x[r], sl2, nm));
+    const u32x2_t pb = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // O^T += V^T . P^T.  A lane's k-slots j are tile tokens 4g + j
+    // (where S^T left them); the transposing LDS read gives lane (g, c16)
+    // V[4g + j][16n + c16], j = 0..3.
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(x[r], sl2, -msl2));
-      const u32x2_t pb = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      // O^T += V^T . P^T.  A lane's k-slots j are tile tokens 4g + j
-      // (where S^T left them); the transposing LDS read gives lane (g, c16)
-      // V[4g + j][16n + c16], j = 0..3.
-#pragma unroll
-      for (int n = 0; n < NDT; ++n) {
-        const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vs + tr_off + 32 * n));
-        acc[n] = mfma16k16(__builtin_bit_cast(u32x2_t, v4), pb, acc[n]);
-      }
-      lacc = mfma16k16(ones, pb, lacc);
-      __builtin_amdgcn_wave_barrier();
-    };
+    for (int n = 0; n < NDT; ++n) {
+      const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vs + tr_off + 32 * n));
+      acc[n] = mfma16k16(__builtin_bit_cast(u32x2_t, v4), pb, acc[n]);
+    }
+    lacc = mfma16k16(ones, pb, lacc);
+    __builtin_amdgcn_wave_barrier();
+  };
+  // the current pass's tiles, split among the waves of the KV head
+  auto run_tiles = [&]() {
+    const int n_tiles = (ntok + 15) / 16;
+    const int last = n_tiles - 1;
     // The wave's tiles are wsub + q * wph, q < nmine; the last tile of the
     // chunk (masked) is its owner's last.  Two register sets alternate: the
     // loads of the next tile go to the set not being computed (past the end
@@ -468,12 +442,166 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
         compute(std::true_type{}, T(q), kA, vA);
       }
     }
+  };
+  if constexpr (!PAIR) {
+    for (int cb = e_beg; cb < e_end; cb += epp) {
+      const int nloc = min(e_end, cb + epp) - cb;
+      __syncthreads();
+      // Stage the valid entries of [cb, cb + nloc) at the front, in list
+      // order (a block-wide prefix count of the valid flags), so that every
+      // tile but the last holds only tokens to attend.  The own block is the
+      // last entry of the list, hence the last valid entry of its chunk.
+      int nv = 0;
+      for (int i0 = 0; i0 < nloc; i0 += NT) {
+        const int i = i0 + (int)threadIdx.x;
+        const int E = cb + i;
+        const bool own = (E == rl.e_own);
+        bool ok = i < nloc;
+        int b = b_own;
+        if (ok && !own) {
+          if (!DENSE && rl.own_sel && cb == e_beg && i0 == 0 && E < rl.n_list) {
+            b = pre;
+            ok = b >= 0 && b < rl.b_sel;
+            if (!ok) debug_flag(QSA_DEBUG_BAD_SEL);
+          } else {
+            b = rl.block(E, DENSE, ok);
+          }
+        }
+        const uint64_t bal = __ballot(ok);
+        if (l == 0) wcnt[w] = __popcll(bal);
+        __syncthreads();
+        int pos = nv + (int)lanes_below(bal), tot = nv;
+  #pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          const int c = wcnt[j];
+          pos += j < w ? c : 0;
+          tot += c;
+        }
+        if (ok) {
+          const int64_t r0 = a.pm.token_slot(seq, b << bs);
+          const int nt = own ? tail : nb;
+          const int p0 = pos << bs;
+          if (nb == 4) {  // QSA blocks: four stores, no loop
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t r = j < nt ? r0 + j : own_row;
+              trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+            }
+          } else {
+            for (int j = 0; j < nt; ++j) {
+              const int64_t r = r0 + j;
+              trow[tslot(p0 + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+            }
+          }
+        }
+        nv = tot;
+        __syncthreads();
+      }
+      const bool own_here = rl.e_own >= cb && rl.e_own < cb + nloc;
+      // tokens to attend: whole blocks, the own block's tail last
+      ntok = own_here ? ((nv - 1) << bs) + tail : (nv << bs);
+      for (int p = ntok + (int)threadIdx.x; p < ((ntok + 15) & ~15); p += NT) trow[tslot(p)] = own_t;
+      __syncthreads();
+      run_tiles();
+    }
+  } else {
+    // Both rows' entry lists (selected blocks, then the own block; invalid
+    // ids as -1) go to la and lb in the K/V staging area, which no tile
+    // uses yet.
+    int32_t* la = reinterpret_cast<int32_t*>(lds);
+    int32_t* lb = la + kPairHalf;
+    const RowList rlB(a, hasB ? rowB : row, hasB ? tB : t, false, hasB ? nselB_raw : 0);
+    const int nA = rl.n_list + 1;
+    const int nB = hasB ? rlB.n_list + 1 : 0;
+    bool ok = true;  // this thread's entries are valid and ascending
+    for (int e = (int)threadIdx.x; e < nA; e += NT) {
+      bool v = true;
+      const int b = e < rl.n_list ? rl.block(e, false, v) : b_own;
+      la[e] = v ? b : -1;
+      ok = ok && v;
+    }
+    for (int e = (int)threadIdx.x; e < nB; e += NT) {
+      bool v = true;
+      const int b = e < rlB.n_list ? rlB.block(e, false, v) : rlB.b_own;
+      lb[e] = v ? b : -1;
+      ok = ok && v;
+    }
+    __syncthreads();
+    for (int e = (int)threadIdx.x + 1; e < nA; e += NT) ok = ok && la[e - 1] < la[e];
+    for (int e = (int)threadIdx.x + 1; e < nB; e += NT) ok = ok && lb[e - 1] < lb[e];
+    // one sequence, both lists valid and strictly ascending: a block both
+    // rows list is staged once (else the lists are staged one after the
+    // other, each block for its own row)
+    const bool share = (__syncthreads_and(ok ? 1 : 0) != 0) && hasB && seqB == seq;
+    auto listed = [](const int32_t* v, int n, int x) {  // x in ascending v[0, n)
+      int lo = 0, hi = n;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (v[mid] < x) lo = mid + 1; else hi = mid;
+      }
+      return lo < n && v[lo] == x;
+    };
+    // the union: row A's entries, then those of row B's that A does not list
+    for (int e = (int)threadIdx.x; e < nA; e += NT) {
+      const int b = la[e];
+      ublk[e] = b;
+      umem[e] = b < 0 ? 0 : (uint8_t)(1u | ((share && listed(lb, nB, b)) ? 2u : 0u));
+    }
+    int nU = nA;
+    for (int i0 = 0; i0 < nB; i0 += NT) {
+      const int e = i0 + (int)threadIdx.x;
+      const bool keep = e < nB && !(share && listed(la, nA, lb[e]));
+      const uint64_t bal = __ballot(keep);
+      if (l == 0) wcnt[w] = __popcll(bal);
+      __syncthreads();
+      int pos = nU + (int)lanes_below(bal), tot = nU;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const int c = wcnt[j];
+        pos += j < w ? c : 0;
+        tot += c;
+      }
+      if (keep) {
+        ublk[pos] = lb[e];
+        umem[pos] = lb[e] < 0 ? 0 : 2;
+      }
+      nU = tot;
+      __syncthreads();
+    }
+    // Passes of epp union entries: every token of an entry is staged with
+    // its visibility (the row lists the block and the token is at or before
+    // the row's position: the own blocks' tails); invisible tokens read
+    // row A's own first token.  All tiles mask by column.
+    for (int cb = 0; cb < nU; cb += epp) {
+      const int nloc = min(nU, cb + epp) - cb;
+      __syncthreads();  // the previous pass's tiles (or the union's reads) are done
+      for (int i = (int)threadIdx.x; i < nloc; i += NT) {
+        const int b = ublk[cb + i];
+        const uint32_t m = umem[cb + i];
+        const int64_t r0 = m ? a.pm.token_slot((m & 1u) ? seq : seqB, b << bs) : own_row;
+        for (int j = 0; j < nb; ++j) {
+          const int pt = (b << bs) + j;
+          const uint32_t vis =
+              (((m & 1u) && pt <= t) ? 1u : 0u) | (((m & 2u) && pt <= tB) ? 2u : 0u);
+          const int64_t r = vis ? r0 + j : own_row;
+          trow[tslot((i << bs) + j)] = WIDE ? (uint32_t)r : (uint32_t)(r * rowbytes);
+          tmask[(i << bs) + j] = (uint8_t)vis;
+        }
+      }
+      ntok = nloc << bs;
+      for (int p = ntok + (int)threadIdx.x; p < ((ntok + 15) & ~15); p += NT) {
+        trow[tslot(p)] = own_t;
+        tmask[p] = 0;
+      }
+      __syncthreads();
+      run_tiles();
+    }
   }
   const float lsum = lacc[0];  // every row of the ones product is the column sum
   __syncthreads();
   // per-wave results to LDS: [wave][head][D + 2] (acc, then m, l)
   float* mrg = reinterpret_cast<float*>(lds);
-  if (c16 < G) {
+  if (c16 < (PAIR ? 2 * G : G)) {
     float* o = mrg + (w * 16 + c16) * (D + 2);
 #pragma unroll
     for (int n = 0; n < NDT; ++n)
@@ -488,7 +616,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   bf16_t* orow = static_cast<bf16_t*>(a.out) + (int64_t)row * hq * D;
   // combine the waves of each KV head: thread = (head, its dims); lane.h is
   // the query head (SPLIT) or the head within this workgroup's group
-  const MergeLane<D, NT> lane(SPLIT ? hq : G);
+  const MergeLane<D, NT> lane(SPLIT ? hq : (PAIR ? 2 * G : G));
   constexpr int ND = MergeLane<D, NT>::ND;
   if (lane.on) {
     const int hk_ = SPLIT ? lane.h / G : 0, hh = SPLIT ? lane.h % G : lane.h;
@@ -507,9 +635,13 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     }
     if constexpr (!SPLIT) {
       const float inv = 1.0f / L;
-      bf16_t* oh = orow + (hk * G + lane.h) * D + lane.d0;
+      const bool isB = PAIR && lane.h >= G;  // a column of row B
+      if (!isB || hasB) {
+        bf16_t* oh = (isB ? orow + hq * D : orow) + (hk * G + (isB ? lane.h - G : lane.h)) * D +
+                     lane.d0;
 #pragma unroll
-      for (int i = 0; i < ND; ++i) oh[i] = f32_to_bf16(O[i] * inv);
+        for (int i = 0; i < ND; ++i) oh[i] = f32_to_bf16(O[i] * inv);
+      }
     } else {
       // partials are read by another workgroup: agent-scope stores, 8 bytes
       // at a time
@@ -533,28 +665,40 @@ bool attn_mfma_supported(int dtype, int hq, int hkv, int d) {
 
 void run_attention_mfma(const AttnArgs& a, int d, bool dense, int n_rows, hipStream_t st) {
   const bool split = a.n_splits > 1;
-  // SPLIT: (split, row); per row: one workgroup per (row, KV head)
+  // rows in pairs: a selection of at most kPairHalf - 1 blocks each, the
+  // query heads of both rows in the 16 product columns
+  const bool pair = !dense && !split && a.sel_of == nullptr && 2 * (a.hq / a.hkv) <= 16 &&
+                    a.top_k + 1 <= kPairHalf && n_rows >= 2;
+  // SPLIT: (split, row); per row (pair): one workgroup per (row or pair, KV head)
   const dim3 grid = split ? dim3((unsigned)a.n_splits, (unsigned)n_rows)
-                          : dim3((unsigned)n_rows * (unsigned)a.hkv);
+                          : dim3((unsigned)(pair ? (n_rows + 1) / 2 : n_rows) * (unsigned)a.hkv);
   const bool wide = a.n_slots * a.hkv * d * 2 > kNarrowCacheBytes;
-#define QSA_ATTN_LAUNCH(DD, DN, SP, WD) \
-  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD>), grid, dim3(attn_waves<SP>() * 64), 0, \
+#define QSA_ATTN_LAUNCH(DD, DN, SP, WD, PR) \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, DN, SP, WD, PR>), grid, dim3(attn_waves<SP>() * 64), 0, \
                      st, a)
 #define QSA_ATTN_LAUNCH_W(DD, DN, SP) \
-  if (wide) QSA_ATTN_LAUNCH(DD, DN, SP, true); else QSA_ATTN_LAUNCH(DD, DN, SP, false)
+  if (wide) QSA_ATTN_LAUNCH(DD, DN, SP, true, false); else QSA_ATTN_LAUNCH(DD, DN, SP, false, false)
+#define QSA_ATTN_LAUNCH_P(DD) \
+  if (wide) QSA_ATTN_LAUNCH(DD, false, false, true, true); \
+  else QSA_ATTN_LAUNCH(DD, false, false, false, true)
   if (d == 128) {
     if (dense) {
       if (split) { QSA_ATTN_LAUNCH_W(128, true, true); } else { QSA_ATTN_LAUNCH_W(128, true, false); }
     } else {
-      if (split) { QSA_ATTN_LAUNCH_W(128, false, true); } else { QSA_ATTN_LAUNCH_W(128, false, false); }
+      if (split) { QSA_ATTN_LAUNCH_W(128, false, true); }
+      else if (pair) { QSA_ATTN_LAUNCH_P(128); }
+      else { QSA_ATTN_LAUNCH_W(128, false, false); }
     }
   } else {
     if (dense) {
       if (split) { QSA_ATTN_LAUNCH_W(64, true, true); } else { QSA_ATTN_LAUNCH_W(64, true, false); }
     } else {
-      if (split) { QSA_ATTN_LAUNCH_W(64, false, true); } else { QSA_ATTN_LAUNCH_W(64, false, false); }
+      if (split) { QSA_ATTN_LAUNCH_W(64, false, true); }
+      else if (pair) { QSA_ATTN_LAUNCH_P(64); }
+      else { QSA_ATTN_LAUNCH_W(64, false, false); }
     }
   }
+#undef QSA_ATTN_LAUNCH_P
 #undef QSA_ATTN_LAUNCH_W
 #undef QSA_ATTN_LAUNCH
 }

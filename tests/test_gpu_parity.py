@@ -351,6 +351,40 @@ def test_attention_skips_invalid_entries(gpu, mode):
         assert err <= TOL[wl.dtype], f"row {i} t={pb.pos_list[i]} err={err}"
 
 
+def test_attention_prefill_pairs(gpu):
+    """Many-row attention serves rows in pairs: an odd row count (the last
+    row alone), pairs of one sequence with ascending selections (blocks both
+    rows list staged once; own blocks equal or adjacent), pairs of two
+    sequences, and rows whose selections are shuffled (each row's blocks
+    staged for it alone).  Every row matches the oracle on its own
+    selection."""
+    _say("attention prefill pairs")
+    wl = MIXED.replace(name="pairs", n_ctx=22000, n_seqs=2, n_needles=4, permute_pages=True,
+                       seed=93)
+    # pairs (0, 1), (8, 9), (10, 11) share (own blocks adjacent, equal,
+    # equal); (2, 3), (4, 5), (12, 13) hold a shuffled row; (6, 7) two
+    # sequences; row 14 is alone
+    pos = [7, 8, 2047, 2048, 4000, 4001, 9003, 9004, 15000, 15003, 21998, 21999, 300, 301, 5555]
+    seq_id = [0, 0, 0, 0, 1, 1, 0, 1, 1, 1, 0, 0, 1, 1, 0]
+    pb = Problem(wl, gpu, seq_id, pos)
+    pb.pool_all()
+    T = len(pos)
+    rng = np.random.default_rng(11)
+    sel = torch.full((T, wl.top_k), -1, dtype=torch.int32)
+    n_sel = torch.zeros(T, dtype=torch.int32)
+    sels = []
+    for i in range(T):
+        s = pb.oracle_select(i).astype(np.int64)
+        sels.append(s)
+        lst = rng.permutation(s) if i in (2, 5, 13) else s
+        sel[i, : len(lst)] = torch.from_numpy(lst.astype(np.int32))
+        n_sel[i] = len(lst)
+    got = _run_attention(pb, pb.cv, sel, n_sel, "prefill")
+    for i in range(T):
+        err = np.abs(got[i] - pb.oracle_attend(i, sels[i])).max()
+        assert err <= TOL[wl.dtype], f"row {i} seq={seq_id[i]} t={pos[i]} err={err}"
+
+
 # draft groups (selection position, lags of the rows reusing it); lag 0 is
 # the row the selection was made for
 SHARED_GROUPS = {
