@@ -330,7 +330,8 @@ def run_prefill(wl, steps: int, warmup: int, dev, dense: bool = True,
         "topk": {"flops": 2 * wl.hi * wl.di * cand,
                  "bytes": sum((c[3][-1] // bk) * wl.di * esz for c in chunks),
                  "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_wave_kernel+pidx_select_kernel",
-                 "files": ("index_mfma.hip", "index.hpp", "select.hpp", "common.hpp")},
+                 "files": ("index_mfma.hip", "index_device.hpp", "index.hpp", "select.hpp",
+                           "common.hpp")},
         "pool": {"bytes": (wl.n_new // bk) * (bk + 1) * wl.di * esz,
                  "kernel": "pool_kernel", "files": ("index.hip", "index_device.hpp", "index.hpp",
                                                     "common.hpp")},
@@ -547,15 +548,18 @@ def _oracle_rows(O, arrs, job):
 
 def _stratified_prefill_rows(wl, ctx):
     """Rows of the 1M prefill for the sampled CPU baseline: the first and
-    last four rows of every chunk (every t mod 4 at both chunk edges), rows
-    t <= 2,051 (selection covers the whole context), and the first row
-    after each needle (the first that can select it)."""
+    last four rows of every chunk (every t mod 4 at both chunk edges), 14
+    evenly spaced rows inside every chunk, rows t <= 2,051 (selection covers
+    the whole context), and the first row after each needle (the first that
+    can select it): about 750 rows, some 16 s of oracle work."""
     chunks = ctx["chunks"]
     picks = set()
     for ci, c in enumerate(chunks):
         pos = c[3]
         for i in list(range(4)) + list(range(len(pos) - 4, len(pos))):
             picks.add((ci, i))
+        for j in range(1, 15):
+            picks.add((ci, j * len(pos) // 15))
     first, clen = chunks[0][3][0], len(chunks[0][3])
 
     def add(t):  # the row at position t, if the prefill has one
@@ -700,7 +704,8 @@ def cpu_baseline(wl, ctx, budget_s=12.0):
     return {"value": round(float(ctx["rows"] / job_s), 3), "unit": "query-tokens/s",
             "cores": nw, "kind": "oracle",
             "sample": f"stratified sample of {len(ys)} rows of {wl.name} (first and last 4 rows "
-                      "of each of its chunks, rows t <= 2,051, the first row after each needle) "
+                      "and 14 evenly spaced rows of each of its chunks, rows t <= 2,051, the "
+                      "first row after each needle) "
                       f"over {nw} worker processes, one BLAS thread each ({wall:.1f} s); whole "
                       f"job extrapolated: pooling {pool_s:.1f} s + row time fitted as "
                       f"{a * 1e3:.2f} ms + {b * 1e9:.1f} ns x t summed over every row, "

@@ -73,8 +73,10 @@ def test_cpu_baseline_leg_on_small_workloads():
     ctx = _prefill_ctx(W, wl)
     picks = bench._stratified_prefill_rows(wl, ctx)
     ts = {ctx["chunks"][ci][3][i] for ci, i in picks}
-    for c in ctx["chunks"]:
+    for ci, c in enumerate(ctx["chunks"]):
         assert set(c[3][:4]) <= ts and set(c[3][-4:]) <= ts
+        inner = {c[3][j * len(c[3]) // 15] for j in range(1, 15)}
+        assert inner <= ts and len(inner) == 14
     assert {0, 1, 2, 3, 2048, 2051} <= ts
     assert all(4 * (b + 1) in ts for b in ctx["cache"].needles[0])
     r = bench.cpu_baseline(wl, ctx, budget_s=1.0)
