@@ -22,7 +22,11 @@
 // instances (many rows) run 4 waves per (row, KV head): workgroup
 // row * Hkv + head, so that with the round-robin placement of workgroups on
 // the 8 XCDs (Hkv dividing 8) every XCD serves one KV head only, and its L2
-// holds twice as many blocks of that head as it would of both.
+// holds twice as many blocks of that head as it would of both.  The PAIR
+// instances serve two neighbouring rows per workgroup (pair * Hkv + head):
+// the query heads of both rows fill the 16 product columns, a block both
+// rows list is staged once, and each staged token carries a visibility bit
+// per row, so every tile masks by column.
 #include <type_traits>
 
 #include "attention.hpp"
