@@ -126,6 +126,25 @@ def test_topk_bit_exact(gpu, case, fused):
     _check_topk(pb, st)
 
 
+def test_topk_arrival_groups(gpu):
+    """Rows of one top-k launch whose chunk counts W (1,024 candidates each)
+    are 33, 40 and 109 (arrival counted in groups of 32 chunks with a short
+    last group, then a top counter) beside one of 20 (a single counter):
+    selections bit for bit, twice in a row (every counter is reset by its
+    last arrival)."""
+    _say("topk arrival groups")
+    wl = MIXED.replace(name="groups", n_ctx=450004, n_needles=8, permute_pages=True, seed=97)
+    pos = [33 * 4096 - 100, 40 * 4096 - 5, 109 * 4096 - 2, 20 * 4096 + 3]
+    pb = Problem(wl, gpu, [0] * len(pos), pos)
+    pb.pool_all()
+    for rep in range(2):
+        st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, wl.top_k, wl.scale)
+        st.sel.fill_(-7)
+        st.select()
+        torch.cuda.synchronize()
+        _check_topk(pb, st)
+
+
 @pytest.mark.parametrize("rows", [4, 64], ids=["4rows", "64rows"])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "scores"])
 @pytest.mark.parametrize("n_tied,first", [(690, 10), (1024, 0), (300, 8190), (2000, 5000),
