@@ -329,7 +329,7 @@ def run_prefill(wl, steps: int, warmup: int, dev, dense: bool = True,
         # the pooled keys of a chunk are read once per launch
         "topk": {"flops": 2 * wl.hi * wl.di * cand,
                  "bytes": sum((c[3][-1] // bk) * wl.di * esz for c in chunks),
-                 "kernel": "pidx_kernel+pidx_tau_kernel+pidx_select_wave_kernel+pidx_select_kernel",
+                 "kernel": "pidx_kernel+pidx_tau_wave_kernel+pidx_select_wave_kernel+pidx_select_kernel",
                  "files": ("index_mfma.hip", "index_device.hpp", "index.hpp", "select.hpp",
                            "common.hpp")},
         "pool": {"bytes": (wl.n_new // bk) * (bk + 1) * wl.di * esz,

@@ -331,9 +331,32 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
 // again, so about 1.5 k keys survive.  For s = 1 this is a guaranteed lower
 // bound of the k-th key; otherwise P4 checks that at least k keys survived
 // and falls back to an exact select when they did not.
-__global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
-  __shared__ SelShared sh;
-  const int rl = blockIdx.x, row = a.row0 + rl;
+//
+// One wave per row (four rows per workgroup): the k'-th largest of the
+// row's un union entries, empty entries (key 0) included, found bit by bit
+// over the wave without barriers; lane l holds entries l, l + 64, ...
+template <int EPW>
+__device__ __forceinline__ uint32_t union_kth_wave(const PIdxArgs& a, int rl, int un, int kq) {
+  const int l = lane_id();
+  const uint32_t* src = a.uni + (int64_t)rl * kPUnion;
+  uint32_t key[EPW];
+  uint32_t nz = 0;
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) {
+    const int jj = i * kWave + l;
+    key[i] = jj < un ? src[jj] : 0u;
+    nz += key[i] != 0u ? 1u : 0u;
+  }
+  // fewer than kq nonzero entries: the kq-th largest entry is an empty one
+  if (wave_sum_u32(nz) < (uint32_t)kq) return 0u;
+  uint32_t kk;
+  return wave_kth<EPW>(key, kq, kk);
+}
+
+__global__ void __launch_bounds__(256) pidx_tau_wave_kernel(PIdxArgs a) {
+  const int rl = blockIdx.x * (256 / kWave) + (int)threadIdx.x / kWave;
+  if (rl >= a.rows) return;  // whole waves
+  const int row = a.row0 + rl;
   const int n = a.idx.pos_of(row) >> a.idx.pm.blk_shift;
   if (n <= a.top_k) return;
   const int s = a.row_stride[rl];
@@ -342,22 +365,11 @@ __global__ void __launch_bounds__(256) pidx_tau_kernel(PIdxArgs a) {
   const int kq = s == 1 ? a.top_k : max(1, min(a.top_k, (3 * a.top_k + 2 * s - 1) / (2 * s)));
   uint32_t tau = 0u;
   if (un >= kq) {
-    // thread t holds union entries [EPT t, EPT t + EPT), loaded at once
-    constexpr int EPT = kPUnion / 256;
-    const u32x4_t* src =
-        reinterpret_cast<const u32x4_t*>(a.uni + (int64_t)rl * kPUnion) + threadIdx.x * (EPT / 4);
-    uint32_t key[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT / 4; ++j) {
-      const u32x4_t v = src[j];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * j + c] = v[c];
-    }
-    int r;
-    bool resolved;
-    radix_kth_regs<EPT>(key, un, kq, sh, tau, r, resolved);
+    if (un <= 16 * kWave) tau = union_kth_wave<16>(a, rl, un, kq);
+    else if (un <= 32 * kWave) tau = union_kth_wave<32>(a, rl, un, kq);
+    else tau = union_kth_wave<kPUnion / kWave>(a, rl, un, kq);
   }
-  if (threadIdx.x == 0) a.tau[rl] = tau;
+  if (lane_id() == 0) a.tau[rl] = tau;
 }
 
 // Key of candidate e recomputed by this lane alone (P4's rare fallback).
@@ -656,14 +668,14 @@ void run_pidx(const PIdxArgs& a, int di, hipStream_t st) {
   hipLaunchKernelGGL(pidx_stride_kernel, dim3(tiles), dim3(256), 0, st, a);
   if (di == 64) {
     hipLaunchKernelGGL((pidx_kernel<64, false>), grid, dim3(kPThreads), 0, st, a);
-    hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(pidx_tau_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_kernel<64, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<64>), dim3(a.rows), dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_fallback_kernel<64>), dim3(kPFallbackWgs), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((pidx_kernel<128, false>), grid, dim3(kPThreads), 0, st, a);
-    hipLaunchKernelGGL(pidx_tau_kernel, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(pidx_tau_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_kernel<128, true>), grid, dim3(kPThreads), 0, st, a);
     hipLaunchKernelGGL(pidx_select_wave_kernel, wave_grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((pidx_select_kernel<128>), dim3(a.rows), dim3(256), 0, st, a);

@@ -71,10 +71,11 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 // (a count over the wave per bit, no barriers); then the keys above T and
 // the first of the keys equal to T, in element order, are written to out in
 // element order (k ids; at least k elements must be present).
+// The k-th largest key T of the nonzero keys a wave holds (at least k of
+// them), found bit by bit (a count over the wave per bit, no barriers);
+// kk receives how many keys equal to T belong to the k largest.
 template <int EPW>
-__device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
-                                                  const int32_t (&id)[EPW], int k,
-                                                  int32_t* out) {
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[EPW], int k, uint32_t& kk) {
   uint32_t mx = 0u, nmn = 0u;
 #pragma unroll
   for (int i = 0; i < EPW; ++i) {
@@ -85,7 +86,8 @@ __device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
   }
   mx = wave_max_u32(mx);
   const uint32_t mn = ~wave_max_u32(nmn);
-  uint32_t T = mx, kk = (uint32_t)k;
+  uint32_t T = mx;
+  kk = (uint32_t)k;
   if (mx != mn) {
     const int hi = 31 - __clz(mx ^ mn);  // highest bit where the keys differ
     T = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
@@ -99,6 +101,15 @@ __device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
       if (cnt >= kk) T = cand; else kk -= cnt;
     }
   }
+  return T;
+}
+
+template <int EPW>
+__device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
+                                                  const int32_t (&id)[EPW], int k,
+                                                  int32_t* out) {
+  uint32_t kk;
+  const uint32_t T = wave_kth<EPW>(key, k, kk);
   // in element order: keys above T, and the first kk keys equal to T
   uint32_t eq_before = 0, taken = 0;
 #pragma unroll
