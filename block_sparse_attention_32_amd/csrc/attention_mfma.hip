@@ -333,8 +333,8 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
   // one tile: S^T, online softmax, O^T update.  Only the last tile of
   // the chunk can hold tokens not to attend (the own block's tail, the
   // padding), so only it masks.
-  auto compute = [&](auto masked, int tile, const u32x4_t (&kf)[4], const u32x4_t (&vf)[4]) {
-    constexpr bool MASK = decltype(masked)::value;
+  // (masked: wave-uniform, true for the last tile of a pass only)
+  auto compute = [&](bool masked, int tile, const u32x4_t (&kf)[4], const u32x4_t (&vf)[4]) {
     // K and V rows to LDS (row 4i + g)
     if (c16 < D / 8) {
 #pragma unroll
@@ -360,7 +360,7 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
       const uint32_t mk = *reinterpret_cast<const uint32_t*>(tmask + tile * 16 + 4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = ((mk >> (8 * r)) & colbit) ? sc[r] : -INFINITY;
-    } else if constexpr (MASK) {
+    } else if (masked) {
       const int p0 = tile * 16 + 4 * g;  // list token of row r: p0 + r
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = p0 + r < ntok ? sc[r] : -INFINITY;
@@ -420,30 +420,24 @@ __global__ void __launch_bounds__(attn_waves<SPLIT>() * 64, SPLIT ? 2 : 3)
     const int n_tiles = (ntok + 15) / 16;
     const int last = n_tiles - 1;
     // The wave's tiles are wsub + q * wph, q < nmine; the last tile of the
-    // chunk (masked) is its owner's last.  Two register sets alternate: the
+    // pass (masked) is its owner's last.  Two register sets alternate: the
     // loads of the next tile go to the set not being computed (past the end
     // a wave reloads its last tile, so every step issues the same loads and
-    // the wait before a product covers only the current tile's).
+    // the wait before a product covers only the current tile's).  One loop
+    // shape for every tile, the last included, keeps both sets in registers.
     const int nmine = wsub < n_tiles ? (last - wsub) / wph + 1 : 0;
     const bool has_last = nmine > 0 && wsub + (nmine - 1) * wph == last;
-    const int nclean = nmine - (has_last ? 1 : 0);
     auto T = [&](int q) { return wsub + min(q, nmine - 1) * wph; };
     u32x4_t kA[4], vA[4], kB[4], vB[4];
     if (nmine > 0) {
       load_tile(T(0), kA, vA);
-      int q = 0;
-      for (; q + 2 <= nclean; q += 2) {
+      for (int q = 0; q < nmine; q += 2) {
         load_tile(T(q + 1), kB, vB);
-        compute(std::false_type{}, T(q), kA, vA);
-        load_tile(T(q + 2), kA, vA);
-        compute(std::false_type{}, T(q + 1), kB, vB);
-      }
-      if (q < nclean) {  // one clean tile left (in A), then perhaps the last (B)
-        load_tile(T(q + 1), kB, vB);
-        compute(std::false_type{}, T(q), kA, vA);
-        if (has_last) compute(std::true_type{}, T(q + 1), kB, vB);
-      } else if (has_last) {
-        compute(std::true_type{}, T(q), kA, vA);
+        compute(has_last && q == nmine - 1, T(q), kA, vA);
+        if (q + 1 < nmine) {
+          load_tile(T(q + 2), kA, vA);
+          compute(has_last && q + 1 == nmine - 1, T(q + 1), kB, vB);
+        }
       }
     }
   };
