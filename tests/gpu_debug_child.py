@@ -86,6 +86,12 @@ def run_cases(debug, out_path):
     dec.attend()
     torch.cuda.synchronize()
     flags["bad_sel"] = take(True)
+    # the same in the many-row (paired) prefill attention: a selected id past
+    # the row's blocks in row 3, which shares a workgroup with row 2
+    pre.sel[3, 5] = ppos[3] // 4 + 7
+    pre.attend()
+    torch.cuda.synchronize()
+    flags["bad_sel_prefill"] = take(True)
     return flags
 
 

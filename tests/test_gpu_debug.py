@@ -45,3 +45,4 @@ def test_debug_build_checks_device_data(gpu, tmp_path):
     assert flags["bad_page"] & B.QSA_DEBUG_BAD_PAGE, flags
     assert flags["bad_row"] & B.QSA_DEBUG_BAD_ROW, flags
     assert flags["bad_sel"] & B.QSA_DEBUG_BAD_SEL, flags
+    assert flags["bad_sel_prefill"] & B.QSA_DEBUG_BAD_SEL, flags
