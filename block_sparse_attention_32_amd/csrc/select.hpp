@@ -22,10 +22,44 @@ struct IdArray {
 };
 
 struct SelShared {
-  uint32_t hist[256];
+  alignas(16) uint32_t hist[3][256];  // radix_kth: hist[0]; radix_kth_regs rotates all three
   uint32_t wcnt[2][kSelWaves];
   uint32_t bc[4];
 };
+
+// Thread-contiguous data read from memory in coalesced order.  The
+// selection routines want thread t to hold 128 contiguous bytes (16-byte
+// chunks 8t .. 8t + 7); read that way, every wave load touches 64 cache
+// lines.  stage_chunks reads chunk 256 j + t in step j instead (a wave's
+// load covers 1 KB contiguous), and transposes through a 32 KB LDS area in
+// which chunk c sits at stage_pos(c): the chunks of each thread permuted
+// among themselves so that the coalesced writes (consecutive chunks across
+// lanes) and the thread-contiguous reads (lanes 128 bytes apart) both fall
+// on distinct banks.
+constexpr int kStageChunks = 8;  // 16-byte chunks per thread (32 KB per workgroup)
+
+__device__ __forceinline__ int stage_pos(int c) {
+  const int t = c >> 3;
+  return c ^ ((t & 7) ^ ((t >> 3) & 1));
+}
+
+// out[i] = chunk kStageChunks * t + i for thread t, where load(c) returns
+// chunk c.  Contains one workgroup barrier; the caller keeps the staging
+// area untouched until every thread is past a later barrier.
+template <class Load>
+__device__ __forceinline__ void stage_chunks(const Load& load, uint4* stage,
+                                             uint4 (&out)[kStageChunks]) {
+  uint4 v[kStageChunks];
+#pragma unroll
+  for (int j = 0; j < kStageChunks; ++j) v[j] = load(j * kSelThreads + (int)threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < kStageChunks; ++j)
+    stage[stage_pos(j * kSelThreads + (int)threadIdx.x)] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kStageChunks; ++i)
+    out[i] = stage[stage_pos(kStageChunks * (int)threadIdx.x + i)];
+}
 
 // Exclusive prefix sum of one value per thread over the workgroup.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared& sh,
@@ -208,17 +242,17 @@ __device__ void radix_kth(const Get& get, int n, int k, SelShared& sh,
   for (int pass = 0; pass < max_passes; ++pass) {
     const int shift = hi >= 7 ? hi - 7 : 0;
     const uint32_t dmask = (1u << (hi - shift + 1)) - 1u;
-    sh.hist[tid] = 0u;
+    sh.hist[0][tid] = 0u;
     __syncthreads();
 #pragma unroll 4
     for (int e = tid; e < n; e += kSelThreads) {
       const uint32_t key = get(e);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[0][(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     // thread t looks at digit 255 - t: counts from the top down
     const uint32_t d = 255u - (uint32_t)tid;
-    const uint32_t h = sh.hist[d];
+    const uint32_t h = sh.hist[0][d];
     uint32_t tot;
     const uint32_t incl = block_incl_scan(h, sh, tot);
     if (incl - h < kk && kk <= incl) {
@@ -293,10 +327,18 @@ __device__ void emit_topk(const Get& get, const Id& id, int n, uint32_t T,
 // key with any unresolved low bits cleared (a lower bound of it) and r the
 // number of keys equal to T among the k largest (meaningful only when
 // resolved is set).
+//
+// One workgroup barrier per pass: three histograms rotate (pass p counts
+// into histogram p % 3 and clears the one pass p + 1 uses, whose last
+// readers finished before pass p - 1's barrier), and every wave scans the
+// whole histogram itself, so that no second exchange is needed to share the
+// digit found.  The waves may still read the last pass's histogram on
+// return; the next writer of a histogram clears it after a barrier.
 template <int EPT>
 __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShared& sh,
                                uint32_t& T, int& r, bool& resolved, int max_passes = 4) {
   const int base_e = threadIdx.x * EPT;
+  const int lane = lane_id();
   uint32_t mx = 0u, nmn = 0u;  // max and (~min)
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
@@ -305,8 +347,28 @@ __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShar
       nmn = max(nmn, ~key[i]);
     }
   }
-  sh.hist[threadIdx.x] = 0u;  // the first pass's histogram, cleared under the exchange below
-  block_max2_u32(mx, nmn, sh);
+  {
+    // the maximum and (~minimum) over the workgroup; between the two
+    // barriers every wave is past any earlier use of the histograms, and the
+    // first pass's is cleared
+    const int wave = threadIdx.x / kWave;
+    mx = wave_max_u32(mx);
+    nmn = wave_max_u32(nmn);
+    if (lane == 0) {
+      sh.wcnt[0][wave] = mx;
+      sh.wcnt[1][wave] = nmn;
+    }
+    __syncthreads();
+    sh.hist[0][threadIdx.x] = 0u;
+    mx = 0u;
+    nmn = 0u;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      mx = max(mx, sh.wcnt[0][w]);
+      nmn = max(nmn, sh.wcnt[1][w]);
+    }
+    __syncthreads();
+  }
   const uint32_t mn = ~nmn;
   if (mx == mn) {
     T = mx;
@@ -322,30 +384,40 @@ __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShar
   for (int pass = 0; pass < max_passes; ++pass) {
     const int shift = hi >= 7 ? hi - 7 : 0;
     const uint32_t dmask = (1u << (hi - shift + 1)) - 1u;
-    if (pass > 0) {
-      sh.hist[threadIdx.x] = 0u;
-      __syncthreads();
-    }
+    const uint32_t* hist = sh.hist[pass % 3];
+    sh.hist[(pass + 1) % 3][threadIdx.x] = 0u;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       if (base_e + i < n && (key[i] & mask) == prefix)
-        atomicAdd(&sh.hist[(key[i] >> shift) & dmask], 1u);
+        atomicAdd(&sh.hist[pass % 3][(key[i] >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // thread t looks at digit 255 - t: counts from the top down
-    const uint32_t d = 255u - threadIdx.x;
-    const uint32_t h = sh.hist[d];
-    uint32_t tot;
-    const uint32_t incl = block_incl_scan(h, sh, tot);
-    if (incl - h < kk && kk <= incl) {
-      sh.bc[0] = d;
-      sh.bc[1] = kk - (incl - h);
+    // lane l: digits 255 - 4l .. 252 - 4l, counted from the top down
+    const uint4 h = reinterpret_cast<const uint4*>(hist)[kWave - 1 - lane];
+    const uint32_t cnt = h.x + h.y + h.z + h.w;
+    const uint32_t incl = wave_incl_scan_dpp(cnt);
+    // the lane in whose digits the count from the top first reaches kk (the
+    // counts total at least kk: every key matches in the first pass, and
+    // the digit chosen by a pass holds at least the kk keys the next needs)
+    const uint64_t at = ballot(incl - cnt < kk && kk <= incl);
+    const int src = __ffsll((unsigned long long)at) - 1;
+    uint32_t c = incl - cnt;
+    uint32_t d = 252u - 4u * (uint32_t)lane, left = kk - c;
+    if (c + h.w >= kk) {
+      d += 3u;
+    } else if ((c += h.w) + h.z >= kk) {
+      d += 2u;
+      left = kk - c;
+    } else if ((c += h.z) + h.y >= kk) {
+      d += 1u;
+      left = kk - c;
+    } else {
+      left = kk - (c + h.y);
     }
-    __syncthreads();
-    prefix |= sh.bc[0] << shift;
+    d = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+    kk = (uint32_t)__builtin_amdgcn_readlane((int)left, src);
+    prefix |= d << shift;
     mask |= dmask << shift;
-    kk = sh.bc[1];
-    __syncthreads();
     if (shift == 0) {
       resolved = true;
       break;
@@ -364,26 +436,29 @@ __device__ void radix_kth_regs(const uint32_t (&key)[EPT], int n, int k, SelShar
 template <int EPT>
 __device__ void emit_regs(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int n,
                           uint32_t T, int r, int32_t* out, int out_cap, SelShared& sh) {
+  static_assert(EPT * kSelThreads < 65536, "counts fit 16 bits");
   const int base_e = threadIdx.x * EPT;
-  uint32_t ties = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) ties += (base_e + i < n && key[i] == T) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t tie_before = block_incl_scan(ties, sh, tot) - ties;
-  uint32_t take_n = 0;
-  bool take[EPT];
+  // the selected elements before thread t: every key above T, and the first
+  // r keys equal to T -- one scan of both counts, packed (equal << 16 | above)
+  uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const bool valid = base_e + i < n;
-    const bool eq = valid && key[i] == T;
-    take[i] = valid && (key[i] > T || (eq && tie_before < (uint32_t)r));
-    tie_before += eq ? 1u : 0u;
-    take_n += take[i] ? 1u : 0u;
+    gt += (valid && key[i] > T) ? 1u : 0u;
+    eq += (valid && key[i] == T) ? 1u : 0u;
   }
-  uint32_t at = block_incl_scan(take_n, sh, tot) - take_n;
+  uint32_t tot;
+  const uint32_t packed = (eq << 16) | gt;
+  const uint32_t before = block_incl_scan(packed, sh, tot) - packed;
+  uint32_t tie_before = before >> 16;
+  uint32_t at = (before & 0xffffu) + min(tie_before, (uint32_t)r);
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    if (take[i]) {
+    const bool valid = base_e + i < n;
+    const bool is_eq = valid && key[i] == T;
+    const bool take = valid && (key[i] > T || (is_eq && tie_before < (uint32_t)r));
+    tie_before += is_eq ? 1u : 0u;
+    if (take) {
       if (at < (uint32_t)out_cap) out[at] = id[i];
       ++at;
     }

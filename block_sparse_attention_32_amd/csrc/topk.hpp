@@ -134,12 +134,44 @@ constexpr int kWaveSel = 16;  // survivors per lane of the one-wave final select
 
 // LDS of the tail of a long row.
 struct LongShared {
-  uint32_t skey[kSelCap];  // survivors, in ascending id order
+  alignas(16) uint32_t skey[kSelCap];  // survivors, in ascending id order
   int32_t sid[kSelCap];
   int32_t sat_w[kMaxSat];  // saturated runs
   uint32_t sat_cnt[kMaxSat], sat_off[kMaxSat];
   uint32_t n_sat;
+  // skey and sid back to back: the staging area of the coalesced reads
+  // (stage_chunks) before any survivor is placed
+  __device__ __forceinline__ uint4* stage() { return reinterpret_cast<uint4*>(skey); }
 };
+static_assert(offsetof(LongShared, sid) == sizeof(uint32_t) * kSelCap &&
+                  2 * sizeof(uint32_t) * kSelCap == 16 * kStageChunks * kSelThreads,
+              "skey and sid together are one 32 KB staging area");
+
+// Keys of elements 4c .. 4c + 3 of a row of n >= 1 (0 past n), read with
+// no branch, so that a thread's loads are all in flight together: every
+// read is clamped into the row and the elements past n are then zeroed.
+__device__ __forceinline__ uint4 mask_chunk(uint4 v, int c, int n) {
+  const int e = 4 * c;
+  return uint4{e < n ? v.x : 0u, e + 1 < n ? v.y : 0u, e + 2 < n ? v.z : 0u,
+               e + 3 < n ? v.w : 0u};
+}
+template <class Get>
+__device__ __forceinline__ uint4 key_chunk(const Get& get, int c, int n) {
+  const int e = 4 * c;
+  return mask_chunk(uint4{get(min(e, n - 1)), get(min(e + 1, n - 1)), get(min(e + 2, n - 1)),
+                          get(min(e + 3, n - 1))},
+                    c, n);
+}
+// Stored keys: the workspace row is 16-byte aligned and holds a multiple of
+// four keys, at least n, so the chunk holding element n - 1 is whole.
+struct StoredKeys {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int e) const { return k[e]; }
+};
+__device__ __forceinline__ uint4 key_chunk(const StoredKeys& get, int c, int n) {
+  const uint4 v = *reinterpret_cast<const uint4*>(get.k + 4 * min(c, (n - 1) >> 2));
+  return mask_chunk(v, c, n);
+}
 
 // Tail of a long row (the last chunk to finish), JW keys per published run.
 // Thread t holds union entries [E t, E t + E) -- whole runs, E = union cap /
@@ -167,7 +199,40 @@ __device__ __forceinline__ void long_tail(const Src& src, const Run& run_keys, u
   uint32_t k[E];
   int32_t id[E];
   uint32_t nx[R];  // largest unpublished key of each of this thread's runs
-  {
+  if constexpr (E == 2 * kStageChunks) {
+    // the 4,096-pair union: read coalesced, through LDS, every chunk of the
+    // row's 4,096 entries with no branch (pairs past un are then zeroed)
+    uint4 ch[kStageChunks];
+    stage_chunks(
+        [&](int c) -> uint4 {
+          const uint4 v = *reinterpret_cast<const uint4*>(tops + 2 * c);
+          const bool lo = 2 * c < un, hi = 2 * c + 1 < un;
+          return uint4{lo ? v.x : 0u, lo ? v.y : 0u, hi ? v.z : 0u, hi ? v.w : 0u};
+        },
+        ls.stage(), ch);
+#pragma unroll
+    for (int i = 0; i < kStageChunks; ++i) {
+      k[2 * i] = ch[i].x;
+      id[2 * i] = (int32_t)ch[i].y;
+      k[2 * i + 1] = ch[i].z;
+      id[2 * i + 1] = (int32_t)ch[i].w;
+    }
+    bool nx_done = false;
+    if constexpr (R == 4) {
+      if (e0 + E <= un) {  // the thread's 4 words, 16-byte aligned
+        const uint4 n4 = *reinterpret_cast<const uint4*>(nxt + e0 / JW);
+        nx[0] = n4.x;
+        nx[1] = n4.y;
+        nx[2] = n4.z;
+        nx[3] = n4.w;
+        nx_done = true;
+      }
+    }
+    if (!nx_done) {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) nx[rr] = e0 + rr * JW < un ? nxt[e0 / JW + rr] : 0u;
+    }
+  } else {
     uint64_t v[E];
     if (e0 + E <= un) {
       // whole runs in range (every thread of a full union): 16-byte loads,
@@ -333,21 +398,49 @@ __device__ __forceinline__ void long_tail(const Src& src, const Run& run_keys, u
 }
 
 // Exact top-k of a row of n <= kDirectCap candidates whose keys get(e)
-// returns: thread t holds keys t * EPT .. t * EPT + EPT - 1 in registers
-// (all of its loads in flight at once), then a register radix select and
-// ordered emission.  Kept out of line: it runs once per row.
+// returns: up to 1,024 candidates go to one wave's bit-by-bit select;
+// otherwise thread t holds keys t * EPT .. t * EPT + EPT - 1 in registers
+// (read coalesced through the 32 KB LDS area stage), then a register radix
+// select and ordered emission.  Kept out of line: it runs once per row.
 template <class Get>
 __device__ __noinline__ void select_direct(Get get, int n, int top_k, int32_t* sel_row,
-                                           int32_t* n_sel, int row, SelShared& sh) {
+                                           int32_t* n_sel, int row, uint4* stage, SelShared& sh) {
+  if (n <= kWave * kWaveSel) {
+    // few candidates: one wave selects them, bit by bit without barriers
+    // (element jj at lane jj % 64, in id order)
+    if (threadIdx.x < kWave) {
+      const int lane = lane_id();
+      uint32_t key[kWaveSel];
+      int32_t id[kWaveSel];
+#pragma unroll
+      for (int i = 0; i < kWaveSel; ++i) {
+        const int jj = i * kWave + lane;
+        key[i] = jj < n ? get(jj) : 0u;
+        id[i] = jj;
+      }
+      wave_topk_ordered<kWaveSel>(key, id, top_k, sel_row);
+      if (lane == 0) n_sel[row] = top_k;
+    }
+    return;
+  }
   constexpr int EPT = kDirectCap / kSelThreads;
+  static_assert(EPT == 4 * kStageChunks, "a thread's keys are its staged chunks");
   const int base = (int)threadIdx.x * EPT;
   uint32_t key[EPT];
   int32_t id[EPT];
+  {
+    uint4 ch[kStageChunks];
+    stage_chunks([&](int c) { return key_chunk(get, c, n); }, stage, ch);
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    key[i] = get(min(base + i, n - 1));
-    id[i] = base + i;
+    for (int i = 0; i < kStageChunks; ++i) {
+      key[4 * i] = ch[i].x;
+      key[4 * i + 1] = ch[i].y;
+      key[4 * i + 2] = ch[i].z;
+      key[4 * i + 3] = ch[i].w;
+    }
   }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) id[i] = base + i;
   uint32_t thr;
   int r;
   bool resolved;
@@ -390,7 +483,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   const float* given = t.scores ? t.scores + (int64_t)row * t.ld : nullptr;
   if (direct && given) {  // every score is stored already: one workgroup
     if (c != 0) return;
-    select_direct(ScoreKeys{given}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(ScoreKeys{given}, p.n, t.top_k, sel_row, t.n_sel, row, ls.stage(), sh);
     return;
   }
   if (c >= p.W) return;
@@ -446,7 +539,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
                                       (uint32_t)c, (uint32_t)p.W, &flag))
     return;
   if (direct) {
-    select_direct(KeyArray{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, sh);
+    select_direct(StoredKeys{ws_row}, p.n, t.top_k, sel_row, t.n_sel, row, ls.stage(), sh);
     return;
   }
 
