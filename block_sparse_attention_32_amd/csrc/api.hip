@@ -435,7 +435,13 @@ static qsa_status topk_common(const qsa_cache* c, const qsa_queries* qm, const f
       run_pidx(a, c->idx_dim, as_stream(stream));
       if ((st = launched()) != QSA_OK) return st;
     }
-    return QSA_OK;
+    // the chunked top-k's arrival counters (the first p.off_tops bytes of
+    // its layout) lie under the indexer's data: zero them, so that a later
+    // call of the same shape on the chunked path finds them at zero
+    const int words = (int)(p.off_tops / 4);
+    hipLaunchKernelGGL(clear_words, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                       as_stream(stream), reinterpret_cast<uint32_t*>(base), words);
+    return launched();
   }
   TopkArgs t;
   memset(&t, 0, sizeof(t));

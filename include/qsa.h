@@ -162,7 +162,13 @@ qsa_status qsa_index_scores(const qsa_cache *c, const qsa_queries *qm,
  * n_idx_heads must be given.  1 <= top_k <= QSA_MAX_TOPK (the pages'
  * budget is 2048 / B).  Selections of more than 512 blocks of rows with
  * fewer than about 64 K candidates take an exact but slower path.
- * ws: workspace of qsa_workspace_size(QSA_OP_TOPK, ...) bytes. */
+ * ws: workspace of qsa_workspace_size(QSA_OP_TOPK, ...) bytes, zero-filled
+ * before the first call; every call leaves it ready for the next call of
+ * the same shape.  Fused calls of 64 rows or more on bfloat16 keys of
+ * Di 64 or 128 run the matrix-core indexer, whose data lies over the
+ * chunked path's counters; such a call zeroes those counters for its own
+ * row count and length, so a workspace that then serves a chunked call of
+ * other shapes must be zero-filled again first. */
 qsa_status qsa_topk_blocks(const qsa_cache *c, const qsa_queries *qm,
                            const float *scores, int64_t ld,
                            const void *q_idx, const float *w,

@@ -126,6 +126,30 @@ def test_topk_bit_exact(gpu, case, fused):
     _check_topk(pb, st)
 
 
+def test_topk_workspace_shared_across_paths(gpu):
+    """One top-k workspace serves the matrix-core indexer (80 rows, fused)
+    and then the chunked top-k over the same rows (caller scores), twice in
+    turn: the indexer's data lies over the chunked path's arrival counters,
+    which the indexer call returns to zero; every selection bit for bit."""
+    _say("topk workspace shared by both paths")
+    pb = Problem(MIXED, gpu, [0] * len(MIXED80_POS), MIXED80_POS)
+    pb.pool_all()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, pb.wl.top_k, pb.wl.scale)
+    max_n = max(max(pb.pos_list) // 4, 1)
+    scores = torch.empty((len(pb.pos_list), max_n), device=gpu)
+    B.qsa_index_scores(pb.cv, pb.rows, pb.qs.q_idx, pb.qs.w, scores)
+    for _ in range(2):
+        for fused in (True, False):
+            st.sel.fill_(-7)
+            st.n_sel.fill_(-7)
+            if fused:
+                st.select()
+            else:
+                st.select(scores=scores)
+            torch.cuda.synchronize()
+            _check_topk(pb, st)
+
+
 def test_topk_arrival_groups(gpu):
     """Rows of one top-k launch whose chunk counts W (1,024 candidates each)
     are 33, 40 and 109 (arrival counted in groups of 32 chunks with a short
