@@ -53,8 +53,13 @@ template <int DI>
 struct PGeom {
   static constexpr int KS = DI / 32;              // MFMA k steps
   static constexpr int ROWB = DI * 2;             // bytes per pooled key
-  static constexpr int PITCH = ROWB + 16;         // LDS row pitch (bank spread)
   static constexpr int VPR = ROWB / 16;           // 16-byte vectors per row
+  static constexpr int BUF = kPGrp * ROWB;        // LDS bytes of one staged group
+  // LDS rows are unpadded; 16-byte chunk c of row r sits at position
+  // c ^ swz(r), so that the 16 rows one operand read touches (the same
+  // chunk of each) fall on 16 distinct groups of four banks (64 banks of
+  // 4 bytes: two rows of Di 64, or one of Di 128, per 256 bytes)
+  __device__ static constexpr int swz(int r) { return (r / (256 / ROWB)) % VPR; }
 };
 
 struct TileMeta {
@@ -149,7 +154,9 @@ template <int DI, bool FILTER>
 __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxArgs a) {
   using Gm = PGeom<DI>;
   constexpr int AT = kPQT / (kPThreads / kWave) / 4;  // MFMA tiles per wave
-  __shared__ __align__(16) unsigned char kst[kPGrp * Gm::PITCH];
+  // two staged groups of pooled keys: the next group is loaded (straight
+  // into LDS) while the current one is scored
+  __shared__ __align__(16) unsigned char kst[2 * Gm::BUF];
   __shared__ TileMeta tm;
   const int split = blockIdx.x, tile = blockIdx.y;
   const int w = threadIdx.x / kWave, l = lane_id(), g = l / 16, c16 = l % 16;
@@ -201,45 +208,70 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
     // blocks at or past a row's candidate count only occur in tiles that
     // reach past the pass's smallest count
     const int n_lo_pass = __builtin_amdgcn_readfirstlane(tm.n_lo);
+    // A group is staged by VPT wave loads per wave, each 64 lanes x 16 bytes
+    // written straight to 1 KB of LDS (global_load_lds_dwordx4): lane l of
+    // wave load j fills LDS vector (w VPT + j) 64 + l of the group, i.e.
+    // row vi / VPR at position vi % VPR, with the chunk that the row's
+    // swizzle puts there.  Rows past the pass's largest candidate count read
+    // the last candidate's key (finite; never a candidate of any row).
     constexpr int VPT = kPGrp * Gm::VPR / kPThreads;
     const int64_t tbase = (int64_t)seq * a.idx.pm.max_pages;
+    const int bmask = (1 << bpp_sh) - 1;
     auto first_group = [&](int G) {
       while (G < g1 && !FILTER && (G % s) != 0) ++G;
       return G;
     };
-    for (int G = first_group(g0); G < g1; G = first_group(G + 1)) {
-      const int b0 = G * kPGrp;
-      __syncthreads();  // the previous group's LDS reads are done
-      {
-        // pooled keys of the group -> LDS (other workgroups on the CU
-        // compute meanwhile)
-        u32x4_t v[VPT];
+    int32_t pgn[VPT];  // page ids of the rows this lane loads for the next group
+    auto load_pages = [&](int G) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-          const int vi = threadIdx.x + kPThreads * j;
-          const int b = b0 + vi / Gm::VPR, part = vi % Gm::VPR;
-          v[j] = u32x4_t{0u, 0u, 0u, 0u};
-          if (b < n_hi) {
-            const int32_t pg = checked_page(a.idx.pm.table[tbase + (b >> bpp_sh)], a.idx.pm.n_pages);
-            const int64_t slot = ((int64_t)pg << bpp_sh) + (b & ((1 << bpp_sh) - 1));
-            v[j] = *reinterpret_cast<const u32x4_t*>(kbar + slot * DI + part * 8);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-          const int vi = threadIdx.x + kPThreads * j;
-          *reinterpret_cast<u32x4_t*>(kst + (vi / Gm::VPR) * Gm::PITCH + (vi % Gm::VPR) * 16) =
-              v[j];
-        }
+      for (int j = 0; j < VPT; ++j) {
+        const int vi = (w * VPT + j) * kWave + l;
+        const int b = min(G * kPGrp + vi / Gm::VPR, n_hi - 1);
+        pgn[j] = a.idx.pm.table[tbase + (b >> bpp_sh)];
       }
+    };
+    auto stage = [&](int G, int buf) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int vi = (w * VPT + j) * kWave + l;
+        const int r = vi / Gm::VPR, c = (vi % Gm::VPR) ^ Gm::swz(r);
+        const int b = min(G * kPGrp + r, n_hi - 1);
+        const int64_t slot =
+            ((int64_t)checked_page(pgn[j], a.idx.pm.n_pages) << bpp_sh) + (b & bmask);
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(kbar + slot * DI + c * 8),
+            (__attribute__((address_space(3))) void*)(kst + buf * Gm::BUF +
+                                                      (w * VPT + j) * kWave * 16),
+            16, 0, 0);
+      }
+    };
+    int G = first_group(g0);
+    if (G < g1) {
+      load_pages(G);
+      stage(G, 0);
+    }
+    int Gn = G < g1 ? first_group(G + 1) : g1;
+    if (Gn < g1) load_pages(Gn);
+    for (int buf = 0; G < g1; buf ^= 1) {
+      const int b0 = G * kPGrp;
+      // this wave's loads of group G have landed; after the barrier every
+      // wave's have, and every wave is done reading the other buffer
+      wait_own_stores();
       __syncthreads();
+      const int Gnn = Gn < g1 ? first_group(Gn + 1) : g1;
+      if (Gn < g1) {
+        stage(Gn, buf ^ 1);
+        if (Gnn < g1) load_pages(Gnn);
+      }
+      const unsigned char* kcur = kst + buf * Gm::BUF;
 #pragma unroll 1
       for (int t16 = 0; t16 < kPGrp / 16; ++t16) {
         u32x4_t bf[Gm::KS];
-        const unsigned char* rowp = kst + (t16 * 16 + c16) * Gm::PITCH;
+        const int kr = t16 * 16 + c16;
+        const unsigned char* rowp = kcur + kr * Gm::ROWB;
 #pragma unroll
         for (int ks = 0; ks < Gm::KS; ++ks)
-          bf[ks] = *reinterpret_cast<const u32x4_t*>(rowp + 64 * ks + 16 * g);
+          bf[ks] = *reinterpret_cast<const u32x4_t*>(rowp + 16 * ((4 * ks + g) ^ Gm::swz(kr)));
         const int b = b0 + t16 * 16 + c16;
         f32x4_t c[AT];
 #pragma unroll
@@ -298,6 +330,8 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
           lmax[at] = kNegInf;
         }
       }
+      G = Gn;
+      Gn = Gnn;
     }
     if (FILTER && c16 == 0) {
 #pragma unroll
