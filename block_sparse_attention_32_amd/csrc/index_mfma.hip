@@ -368,7 +368,12 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
 //
 // One wave per row (four rows per workgroup): the k'-th largest of the
 // row's un union entries, empty entries (key 0) included, found bit by bit
-// over the wave without barriers; lane l holds entries l, l + 64, ...
+// over the wave without barriers (lane l holds entries l, l + 64, ...), to
+// kTauBits bits below the highest bit where the union's keys differ, the
+// lower bits cleared: still a lower bound of the k'-th key (the keys it
+// admits beyond it lie within 1/4096 of the union's key range), in about
+// half the passes.
+constexpr int kTauBits = 12;
 template <int EPW>
 __device__ __forceinline__ uint32_t union_kth_wave(const PIdxArgs& a, int rl, int un, int kq) {
   const int l = lane_id();
@@ -383,8 +388,7 @@ __device__ __forceinline__ uint32_t union_kth_wave(const PIdxArgs& a, int rl, in
   }
   // fewer than kq nonzero entries: the kq-th largest entry is an empty one
   if (wave_sum_u32(nz) < (uint32_t)kq) return 0u;
-  uint32_t kk;
-  return wave_kth<EPW>(key, kq, kk);
+  return wave_kth_floor<EPW>(key, kq, kTauBits);
 }
 
 __global__ void __launch_bounds__(256) pidx_tau_wave_kernel(PIdxArgs a) {

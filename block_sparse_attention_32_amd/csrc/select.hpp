@@ -138,6 +138,40 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&key)[EPW], int k, 
   return T;
 }
 
+// A lower bound of the k-th largest nonzero key a wave holds (at least k
+// of them): the bits of the k-th key from the highest bit where the wave's
+// keys differ down to `bits` bits below it, the lower bits cleared.  At
+// least k keys are >= the result, and it is within 2^-bits of the wave's
+// key range below the k-th key.
+template <int EPW>
+__device__ __forceinline__ uint32_t wave_kth_floor(const uint32_t (&key)[EPW], int k, int bits) {
+  uint32_t mx = 0u, nmn = 0u;
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) {
+    if (key[i] != 0u) {
+      mx = max(mx, key[i]);
+      nmn = max(nmn, ~key[i]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  const uint32_t mn = ~wave_max_u32(nmn);
+  if (mx == mn) return mx;
+  const int hi = 31 - __clz(mx ^ mn);
+  const int lo = hi - bits + 1 > 0 ? hi - bits + 1 : 0;
+  uint32_t T = hi == 31 ? 0u : (mx & ~((2u << hi) - 1u));
+  uint32_t kk = (uint32_t)k;
+  for (int bit = hi; bit >= lo; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    const uint32_t msk = ~((1u << bit) - 1u);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) cnt += (key[i] & msk) == cand ? 1u : 0u;
+    cnt = wave_sum_u32(cnt);
+    if (cnt >= kk) T = cand; else kk -= cnt;
+  }
+  return T;
+}
+
 template <int EPW>
 __device__ __forceinline__ void wave_topk_ordered(const uint32_t (&key)[EPW],
                                                   const int32_t (&id)[EPW], int k,
