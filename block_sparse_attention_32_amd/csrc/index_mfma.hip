@@ -20,9 +20,9 @@
 // Exact top-k in four launches per batch of rows:
 //   P1  sampled groups only (every s-th): for each (query, lane) the largest
 //       key of the group -> the row's "union" of group maxima;
-//   P2  per row: tau = the k'-th largest union key, k' = ceil(1.5 k / s)
-//       (k' = k without sampling: then tau is a lower bound of the k-th
-//       key; with sampling about 1.5 k keys reach it);
+//   P2  per row: tau = the k'-th largest union key, k' = ceil(1.5 k / s),
+//       its low bits cleared (k' = k without sampling: then tau is a lower
+//       bound of the k-th key; with sampling about 1.5 k keys reach it);
 //   P3  all groups: keys >= tau (the survivors; stored as block id and
 //       score bits) appended per (row, split) in block order;
 //   P4  per row: survivors gathered in block order -> exact radix select and
@@ -360,8 +360,8 @@ __global__ void __launch_bounds__(256) pidx_stride_kernel(PIdxArgs a) {
 
 // P2: tau per row from its union of group maxima: the k'-th largest union
 // key, k' = ceil(1.5 k / s) for sampling stride s (k' = k when every group
-// was sampled).  Each union key is a distinct key of the row, so at least
-// k' keys are >= tau; the unsampled groups hold about (s - 1) times as many
+// was sampled), its low bits cleared (see below).  Each union key is a
+// distinct key of the row, so at least k' keys are >= tau; the unsampled groups hold about (s - 1) times as many
 // again, so about 1.5 k keys survive.  For s = 1 this is a guaranteed lower
 // bound of the k-th key; otherwise P4 checks that at least k keys survived
 // and falls back to an exact select when they did not.
