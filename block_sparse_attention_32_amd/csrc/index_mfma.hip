@@ -264,7 +264,9 @@ __global__ void __launch_bounds__(kPThreads, DI == 64 ? 4 : 2) pidx_kernel(PIdxA
         if (Gnn < g1) load_pages(Gnn);
       }
       const unsigned char* kcur = kst + buf * Gm::BUF;
-#pragma unroll 1
+      // four steps of 16 keys per loop iteration: the compiler interleaves
+      // one step's products with the previous step's epilogue
+#pragma unroll 4
       for (int t16 = 0; t16 < kPGrp / 16; ++t16) {
         u32x4_t bf[Gm::KS];
         const int kr = t16 * 16 + c16;
