@@ -126,6 +126,29 @@ def test_topk_bit_exact(gpu, case, fused):
     _check_topk(pb, st)
 
 
+@pytest.mark.parametrize("n_rows", [80, 4], ids=["matrix-core", "chunked"])
+def test_topk_negative_head_weights(gpu, n_rows):
+    """Head weights of both signs (a learned indexer's weights need not be
+    positive): scores of both signs, so the union keys span the sign bit
+    and the sampled threshold starts from the top bit.  Weights stay on the
+    grid (multiples of 1/16), so the selection is exact: bit for bit
+    against the oracle on the matrix-core path (80 rows) and the chunked
+    path (4 rows)."""
+    _say(f"topk negative weights rows={n_rows}")
+    pos = MIXED80_POS if n_rows == 80 else [2051, 32771, 59999, 60000]
+    pb = Problem(MIXED, gpu, [0] * len(pos), pos)
+    pb.pool_all()
+    g = torch.Generator().manual_seed(31)
+    flip = torch.randint(0, 2, tuple(pb.qs.w.shape), generator=g).to(gpu) * 2 - 1
+    pb.qs.w.mul_(flip.to(pb.qs.w.dtype))
+    assert (pb.qs.w < 0).any() and (pb.qs.w > 0).any()
+    st = P.QsaStep(pb.cv, pb.rows, pb.qs.q, pb.qs.q_idx, pb.qs.w, pb.wl.top_k, pb.wl.scale)
+    st.sel.fill_(-7)
+    st.select()
+    torch.cuda.synchronize()
+    _check_topk(pb, st)
+
+
 def test_topk_workspace_shared_across_paths(gpu):
     """One top-k workspace serves the matrix-core indexer (80 rows, fused)
     and then the chunked top-k over the same rows (caller scores), twice in
