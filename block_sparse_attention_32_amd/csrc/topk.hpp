@@ -498,6 +498,13 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs t) {
   } else {
     load_row_query<T, DI, HI>(iq, t.idx, row);
     chunk_scores<T, DI, HI>(t.idx, p.seq, p.n, c0, iq, pages, keys);
+    if (p.W == 1) {
+      // the row's only chunk: every key is in this workgroup's LDS
+      // (chunk_scores ends with a barrier), so it selects at once, with no
+      // hand-off through memory and no arrival
+      select_direct(KeyArray{keys}, p.n, t.top_k, sel_row, t.n_sel, row, ls.stage(), sh);
+      return;
+    }
     if (keep) {
       for (int i = threadIdx.x; i < kChunk && c0 + i < p.n; i += blockDim.x)
         st_agent(ws_row + c0 + i, keys[i]);
